@@ -1,0 +1,230 @@
+// C ABI of the PISA hot path: argument validation, pyramid geometry,
+// workspace layout and kernel launches.  See include/pisa.h for the contract.
+#include <math.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pisa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pisa_status fail(pisa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pisa_status ok() {
+  g_last_error.clear();
+  return PISA_OK;
+}
+
+pisa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool supported_group(int32_t G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+pisa::PyrGeom make_geom(int64_t cap, int32_t C) {
+  pisa::PyrGeom g{};
+  g.levels_cap = pisa::num_levels(cap, C);
+  int64_t off = 0;
+  for (int32_t l = 1; l <= g.levels_cap; ++l) {
+    g.level_off[l] = off;
+    off += pisa::level_rows(cap, C, l);
+  }
+  g.rows = off;
+  return g;
+}
+
+// Validates a problem and fills the internal form.
+pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
+  if (p == nullptr) return fail(PISA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B < 1 || p->N < 1 || p->Hq < 1 || p->Hkv < 1 || p->D < 1)
+    return fail(PISA_ERR_INVALID_ARG, "B, N, Hq, Hkv, D must be >= 1 (got %d %d %d %d %d)", p->B, p->N, p->Hq,
+                p->Hkv, p->D);
+  if (p->Hq % p->Hkv != 0) return fail(PISA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->C < 1) return fail(PISA_ERR_INVALID_ARG, "C must be >= 1 (got %d)", p->C);
+  if (p->K < 1) return fail(PISA_ERR_INVALID_ARG, "K must be >= 1 (got %d)", p->K);
+  if (p->causal != 0 && p->causal != 1) return fail(PISA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->dtype != PISA_F32 && p->dtype != PISA_BF16) return fail(PISA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (!(p->scale >= 0.f) || !isfinite(p->scale)) return fail(PISA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (p->cap != 0 && p->cap < p->N) return fail(PISA_ERR_INVALID_ARG, "cap (%d) must be 0 or >= N (%d)", p->cap, p->N);
+  if (p->select_algo < 0 || p->select_algo > 2) return fail(PISA_ERR_INVALID_ARG, "unknown select_algo %d", p->select_algo);
+  if (p->q_tile < 0) return fail(PISA_ERR_INVALID_ARG, "q_tile must be >= 0");
+  const int32_t G = p->Hq / p->Hkv;
+  if (p->g != 2) return fail(PISA_ERR_UNSUPPORTED, "merge factor g must be 2 (got %d)", p->g);
+  if (p->D != 64 && p->D != 128) return fail(PISA_ERR_UNSUPPORTED, "head dim D must be 64 or 128 (got %d)", p->D);
+  if (!supported_group(G)) return fail(PISA_ERR_UNSUPPORTED, "G_Q = Hq/Hkv must be 1, 2, 4, 8 or 16 (got %d)", G);
+  if (p->K > 32) return fail(PISA_ERR_UNSUPPORTED, "K must be <= 32 (got %d)", p->K);
+  if (p->C > 128) return fail(PISA_ERR_UNSUPPORTED, "C must be <= 128 (got %d)", p->C);
+  if (p->q_tile != 0 && p->q_tile != 16 / G)
+    return fail(PISA_ERR_UNSUPPORTED, "q_tile must be 0 or 16/G_Q = %d (got %d)", 16 / G, p->q_tile);
+  const int64_t cap = p->cap ? p->cap : p->N;
+  if ((int64_t)p->B * p->Hkv * p->N * p->K > INT32_MAX || (int64_t)p->N * p->K > INT32_MAX)
+    return fail(PISA_ERR_UNSUPPORTED, "B*Hkv*N*K exceeds 2^31-1");
+  out->B = p->B;
+  out->N = p->N;
+  out->Hq = p->Hq;
+  out->Hkv = p->Hkv;
+  out->G = G;
+  out->D = p->D;
+  out->C = p->C;
+  out->K = p->K;
+  out->causal = p->causal != 0;
+  out->dtype = p->dtype;
+  out->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
+  out->cap = cap;
+  out->L = pisa::num_levels(p->N, p->C);
+  out->q_tile = 16 / G;
+  out->geo = make_geom(cap, p->C);
+  return ok();
+}
+
+size_t blk2_bytes(const pisa::Problem& q) { return align256(sizeof(int32_t) * (size_t)q.B * q.Hkv * q.N * q.K); }
+
+}  // namespace
+
+extern "C" {
+
+const char* pisa_last_error(void) { return g_last_error.c_str(); }
+
+const char* pisa_version(void) { return "pisa-mi355x 0.1 (gfx950)"; }
+
+int32_t pisa_levels(int64_t n, int32_t C) { return (n < 1 || C < 1) ? 0 : pisa::num_levels(n, C); }
+
+int64_t pisa_level_rows(int64_t n, int32_t C, int32_t l) {
+  return (n < 1 || C < 1 || l < 1 || l > 62) ? 0 : pisa::level_rows(n, C, l);
+}
+
+int64_t pisa_level_offset(int64_t cap, int32_t C, int32_t l) {
+  if (cap < 1 || C < 1 || l < 1 || l > pisa::num_levels(cap, C)) return -1;
+  int64_t off = 0;
+  for (int32_t i = 1; i < l; ++i) off += pisa::level_rows(cap, C, i);
+  return off;
+}
+
+size_t pisa_pyramid_bytes(const pisa_problem* p) {
+  pisa::Problem q;
+  if (validate(p, &q) != PISA_OK) return 0;
+  return sizeof(float) * (size_t)q.B * q.Hkv * q.geo.rows * q.D;
+}
+
+pisa_status pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyr, hipStream_t stream) {
+  pisa::Problem q;
+  pisa_status s = validate(p, &q);
+  if (s != PISA_OK) return s;
+  if (k == nullptr || pyr == nullptr) return fail(PISA_ERR_INVALID_ARG, "k and pyr must be non-NULL");
+  return hip_status(pisa::launch_build_pyramid(q, k, pyr, stream), "pisa_build_pyramid");
+}
+
+size_t pisa_select_workspace_bytes(const pisa_problem* p) {
+  pisa::Problem q;
+  if (validate(p, &q) != PISA_OK) return 0;
+  if (p->select_algo == PISA_SELECT_FUSED) return 256;
+  return blk2_bytes(q) + pisa::stage2_workspace_bytes(q);
+}
+
+pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, const float* pyr, int32_t* idx,
+                        float* score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  pisa::Problem pr;
+  pisa_status s = validate(p, &pr);
+  if (s != PISA_OK) return s;
+  if (q == nullptr || k == nullptr || pyr == nullptr || idx == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "q, k, pyr and idx must be non-NULL");
+  if (p->select_algo == PISA_SELECT_FUSED)
+    return hip_status(pisa::launch_route(pr, q, k, pyr, idx, score, true, stream), "pisa_select (fused)");
+  const size_t need = blk2_bytes(pr) + pisa::stage2_workspace_bytes(pr);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws == nullptr ? 0 : ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(PISA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int32_t* blk2 = static_cast<int32_t*>(ws);
+  void* ws2 = static_cast<char*>(ws) + blk2_bytes(pr);
+  hipError_t e = pisa::launch_route(pr, q, k, pyr, blk2, nullptr, false, stream);
+  if (e != hipSuccess) return hip_status(e, "pisa_select (stage 1)");
+  return hip_status(pisa::launch_stage2(pr, q, k, blk2, idx, score, ws2, stream), "pisa_select (stage 2)");
+}
+
+size_t pisa_attn_workspace_bytes(const pisa_problem* p) {
+  pisa::Problem q;
+  if (validate(p, &q) != PISA_OK) return 0;
+  return 256;
+}
+
+pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                             void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  pisa::Problem pr;
+  pisa_status s = validate(p, &pr);
+  if (s != PISA_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || o == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "q, k, v, idx and o must be non-NULL");
+  return hip_status(pisa::launch_attn_query(pr, q, k, v, idx, o, lse, stream), "pisa_sparse_attn");
+}
+
+size_t pisa_flat_workspace_bytes(const pisa_problem* p) {
+  pisa::Problem q;
+  if (validate(p, &q) != PISA_OK) return 0;
+  return 256;
+}
+
+pisa_status pisa_flat_select(const pisa_problem* p, const void* q, const float* pyr, int32_t* idx, float* score,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  pisa::Problem pr;
+  pisa_status s = validate(p, &pr);
+  if (s != PISA_OK) return s;
+  if (q == nullptr || pyr == nullptr || idx == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "q, pyr and idx must be non-NULL");
+  return hip_status(pisa::launch_flat(pr, q, pyr, idx, score, stream), "pisa_flat_select");
+}
+
+pisa_status pisa_decode_step(const pisa_decode_problem* p, void* k_cache, void* v_cache, float* pyr, int32_t* len,
+                             const void* q_new, const void* k_new, const void* v_new, void* o, int32_t* idx,
+                             float* score, int32_t* err, hipStream_t stream) {
+  if (p == nullptr) return fail(PISA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->S < 1 || p->cap < 1 || p->Hq < 1 || p->Hkv < 1 || p->D < 1 || p->C < 1 || p->K < 1)
+    return fail(PISA_ERR_INVALID_ARG, "S, cap, Hq, Hkv, D, C, K must be >= 1");
+  if (p->Hq % p->Hkv != 0) return fail(PISA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->dtype != PISA_F32 && p->dtype != PISA_BF16) return fail(PISA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (!(p->scale >= 0.f) || !isfinite(p->scale)) return fail(PISA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  const int32_t G = p->Hq / p->Hkv;
+  if (p->g != 2) return fail(PISA_ERR_UNSUPPORTED, "merge factor g must be 2 (got %d)", p->g);
+  if (p->D != 64 && p->D != 128) return fail(PISA_ERR_UNSUPPORTED, "head dim D must be 64 or 128 (got %d)", p->D);
+  if (!supported_group(G)) return fail(PISA_ERR_UNSUPPORTED, "G_Q = Hq/Hkv must be 1, 2, 4, 8 or 16 (got %d)", G);
+  if (p->K > 32) return fail(PISA_ERR_UNSUPPORTED, "K must be <= 32 (got %d)", p->K);
+  if (p->C > 128) return fail(PISA_ERR_UNSUPPORTED, "C must be <= 128 (got %d)", p->C);
+  if (k_cache == nullptr || v_cache == nullptr || pyr == nullptr || len == nullptr || q_new == nullptr ||
+      k_new == nullptr || v_new == nullptr || o == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "k_cache, v_cache, pyr, len, q_new, k_new, v_new and o must be non-NULL");
+  pisa::DecodeArgs a{};
+  a.S = p->S;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.G = G;
+  a.D = p->D;
+  a.C = p->C;
+  a.K = p->K;
+  a.dtype = p->dtype;
+  a.cap = p->cap;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
+  a.geo = make_geom(p->cap, p->C);
+  return hip_status(pisa::launch_decode(a, k_cache, v_cache, pyr, len, q_new, k_new, v_new, o, idx, score, err, stream),
+                    "pisa_decode_step");
+}
+
+}  // extern "C"

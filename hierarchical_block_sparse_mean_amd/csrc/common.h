@@ -1,0 +1,196 @@
+// Device helpers shared by the PISA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace pisa {
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// round to nearest even (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- element access: T is float (fp32) or uint16_t (bf16 bits) ----------
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* out) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* out) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float load1(const T* p);
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ void store1(T* p, float v);
+template <>
+__device__ __forceinline__ void store1<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store1<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// ---- wave-level primitives ------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Orders LDS traffic between lanes of one wave (no cross-wave effect).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// reductions inside aligned groups of `W` lanes (W a power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// log(exp(a) + exp(b)) with -inf handled
+__device__ __forceinline__ float lse2(float a, float b) {
+  const float m = fmaxf(a, b);
+  if (m == -INFINITY) return -INFINITY;
+  return m + __logf(__expf(a - m) + __expf(b - m));
+}
+
+// ---- total order of every top-K: score descending, then index ascending ---
+// 64-bit key, larger = better.  Invalid entries use key 0.
+__device__ __forceinline__ uint32_t float_order(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t score_key(float score, int32_t idx) {
+  return ((uint64_t)float_order(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ int32_t key_index(uint64_t key) {
+  return (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+}
+__device__ __forceinline__ float key_score(uint64_t key) { return float_from_order((uint32_t)(key >> 32)); }
+// key ordering a kept set by index ascending, carrying the score
+__device__ __forceinline__ uint64_t index_key(int32_t idx, float score) {
+  return ((uint64_t)(0xFFFFFFFFu - (uint32_t)idx) << 32) | float_order(score);
+}
+__device__ __forceinline__ int32_t index_key_index(uint64_t key) {
+  return (int32_t)(0xFFFFFFFFu - (uint32_t)(key >> 32));
+}
+__device__ __forceinline__ float index_key_score(uint64_t key) { return float_from_order((uint32_t)key); }
+
+// Bitonic sort of one 64-bit key per lane, descending across the wave
+// (lane 0 ends with the largest key).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t other = shfl_xor_u64(key, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;
+      const bool take_max = (lower == desc);
+      key = take_max ? (key > other ? key : other) : (key < other ? key : other);
+    }
+  }
+  return key;
+}
+
+// ---- pyramid geometry (capacity layout, see pisa.h) -----------------------
+__host__ __device__ __forceinline__ int64_t level_rows(int64_t n, int32_t C, int32_t l) {
+  // M_l(n) = ceil(n / (C * 2^(l-1)))
+  const int64_t span = (int64_t)C << (l - 1);
+  return (n + span - 1) / span;
+}
+__host__ __device__ __forceinline__ int32_t num_levels(int64_t n, int32_t C) {
+  int64_t m = (n + C - 1) / C;
+  int32_t L = 1;
+  while (m > 1) {
+    m = (m + 1) >> 1;
+    ++L;
+  }
+  return L;
+}
+
+constexpr int kMaxLevels = 40;
+
+// Per-call pyramid geometry passed to kernels by value.
+struct PyrGeom {
+  int64_t level_off[kMaxLevels + 1];  // first row of level l (1-based) in a head
+  int64_t rows;                       // rows per (b, h) head (capacity layout)
+  int32_t levels_cap;                 // L(cap)
+};
+
+// ---- MFMA tiles -----------------------------------------------------------
+// One 16x16 output tile accumulated over a 32-wide slice of the contraction.
+// Fragment convention (both dtypes): lane l feeds row/column (l % 16) and
+// eight contraction elements chosen by the caller for lane group l / 16; A and
+// B must use the same choice.  Output: lane l holds rows 4*(l/16)+i, column
+// l % 16, i = 0..3.
+__device__ __forceinline__ floatx4 mma16x16x32(const float* a8, const float* b8, floatx4 acc) {
+  // fp32 inputs: eight K=4 MFMAs, step i pairs element i of every lane group
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a8[i], b8[i], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ floatx4 mma16x16x32(const bf16x8 a, const bf16x8 b, floatx4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+}  // namespace pisa

@@ -1,0 +1,81 @@
+// Host-side launchers of the PISA kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace pisa {
+
+// A validated problem (see pisa.h for the meaning of each field).
+struct Problem {
+  int32_t B, N, Hq, Hkv, G, D, C, K;
+  bool causal;
+  int32_t dtype;  // 0 fp32, 1 bf16
+  float scale;
+  int64_t cap;     // k/v row stride in tokens and pyramid capacity
+  int32_t L;       // levels of N tokens
+  int32_t q_tile;  // stage-2 queries per MFMA tile
+  PyrGeom geo;
+};
+
+// Calls fn(T*, integral_constant<D>, integral_constant<G>) for the runtime
+// dtype / head dim / group size.  Returns hipErrorInvalidValue if unsupported.
+template <typename Fn>
+hipError_t dispatch_tdg(int32_t dtype, int32_t D, int32_t G, Fn&& fn) {
+  auto with_g = [&](auto tp, auto dc) -> hipError_t {
+    switch (G) {
+      case 1: return fn(tp, dc, std::integral_constant<int, 1>{});
+      case 2: return fn(tp, dc, std::integral_constant<int, 2>{});
+      case 4: return fn(tp, dc, std::integral_constant<int, 4>{});
+      case 8: return fn(tp, dc, std::integral_constant<int, 8>{});
+      case 16: return fn(tp, dc, std::integral_constant<int, 16>{});
+      default: return hipErrorInvalidValue;
+    }
+  };
+  auto with_d = [&](auto tp) -> hipError_t {
+    switch (D) {
+      case 64: return with_g(tp, std::integral_constant<int, 64>{});
+      case 128: return with_g(tp, std::integral_constant<int, 128>{});
+      default: return hipErrorInvalidValue;
+    }
+  };
+  if (dtype == 1) return with_d(static_cast<uint16_t*>(nullptr));
+  return with_d(static_cast<float*>(nullptr));
+}
+
+// pyramid.hip
+hipError_t launch_build_pyramid(const Problem& p, const void* k, float* pyr, hipStream_t stream);
+
+// route.hip: one wave per (b, h, t); fused = all levels incl. raw-key leaves
+// (writes idx/score), else stage 1 (writes the kept level-2 blocks to idx).
+hipError_t launch_route(const Problem& p, const void* q, const void* k, const float* pyr, int32_t* idx,
+                        float* score, bool fused, hipStream_t stream);
+// route.hip: query-major attention, one wave per (b, h, t)
+hipError_t launch_attn_query(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
+                             void* o, float* lse, hipStream_t stream);
+
+// select2.hip: stage 2 (query clusters, MFMA leaf scoring) and final top-K
+size_t stage2_workspace_bytes(const Problem& p);
+hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const int32_t* blk2, int32_t* idx,
+                         float* score, void* ws, hipStream_t stream);
+
+// flat.hip
+hipError_t launch_flat(const Problem& p, const void* q, const float* pyr, int32_t* idx, float* score,
+                       hipStream_t stream);
+
+// decode.hip
+struct DecodeArgs {
+  int32_t S, Hq, Hkv, G, D, C, K, dtype;
+  int64_t cap;
+  float scale;
+  PyrGeom geo;
+};
+hipError_t launch_decode(const DecodeArgs& a, void* k_cache, void* v_cache, float* pyr, int32_t* len,
+                         const void* q_new, const void* k_new, const void* v_new, void* o, int32_t* idx,
+                         float* score, int32_t* err, hipStream_t stream);
+
+}  // namespace pisa

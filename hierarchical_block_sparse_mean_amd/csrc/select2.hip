@@ -1,0 +1,420 @@
+// Stage 2 of the two-stage selector and the final top-K.
+//
+// "Block Sparse Attention with Log-Linear Complexity" (PISA), hyper.ai page,
+// section "kernel implementation": after stage 1 every query has at most gK
+// candidate leaves; queries that must score the same candidate key block are
+// grouped into clusters, each cluster is cut into tiles of queries, one
+// program loads a key tile once and reuses it for a (Q_tile * G_Q) x d query
+// tile (the (Q_tile G_Q) x d times d x C contraction), applies the LSE over
+// the keys per query head and sums over the G_Q heads; a last kernel applies
+// top-K per (query, KV head).  The leaf score is the exact raw-key LSE
+// (section "coarse-to-fine top-K selection", score equation at level 1).
+//
+// Design on gfx950: a cluster is a kept level-2 block (its two sibling leaves
+// are always candidates together), so one key tile of 2C keys serves both
+// leaves and each query row is read once per pair of leaves.  Tiles are 16
+// MFMA rows = 16 / G_Q queries x G_Q heads (v_mfma_f32_16x16x32_bf16; fp32
+// inputs use v_mfma_f32_16x16x4_f32).  The key tile sits in LDS with a
+// 16-byte row pad so that the 16 lanes of a fragment read hit distinct banks.
+#include "kernels.h"
+
+namespace pisa {
+
+constexpr int kS2Waves = 4;
+constexpr int kS2Chunk = 256;  // queries of one cluster per workgroup
+constexpr int kTopkWaves = 4;
+
+// ---- workspace layout -------------------------------------------------------
+struct S2Layout {
+  int64_t ncl;      // clusters = B * Hkv * M2
+  int64_t max_pairs;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_scores, total;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static S2Layout s2_layout(const Problem& p) {
+  S2Layout s{};
+  const int64_t M2 = level_rows(p.N, p.C, 2);
+  s.ncl = (int64_t)p.B * p.Hkv * M2;
+  s.max_pairs = (int64_t)p.B * p.Hkv * p.N * p.K;
+  size_t off = 0;
+  s.off_counts = off;
+  off = align256(off + sizeof(int32_t) * s.ncl);
+  s.off_cursor = off;
+  off = align256(off + sizeof(int32_t) * s.ncl);
+  s.off_offsets = off;
+  off = align256(off + sizeof(int32_t) * (s.ncl + 1));
+  s.off_chunks = off;
+  off = align256(off + sizeof(int32_t) * (s.ncl + 1));
+  s.off_pairs = off;
+  off = align256(off + sizeof(int32_t) * s.max_pairs);
+  s.off_scores = off;
+  off = align256(off + sizeof(float) * 2 * s.max_pairs);
+  s.total = off;
+  return s;
+}
+
+size_t stage2_workspace_bytes(const Problem& p) { return s2_layout(p).total; }
+
+// ---- cluster construction: histogram, scan, scatter --------------------------
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void cluster_count_kernel(const int32_t* __restrict__ blk2, int64_t entries, int32_t NK, int64_t M2,
+                                     int32_t* counts) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t j2 = blk2[e];
+    if (j2 >= 0) atomicAdd(&counts[(e / NK) * M2 + j2], 1);
+  }
+}
+
+// Single-workgroup exclusive scans: offsets of the pairs and of the chunks.
+__global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __restrict__ counts, int64_t ncl,
+                                                            int32_t* offsets, int32_t* chunk_off) {
+  __shared__ int32_t s_a[1024], s_b[1024];
+  __shared__ int32_t carry_a, carry_b;
+  if (threadIdx.x == 0) {
+    carry_a = 0;
+    carry_b = 0;
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < ncl; base += 1024) {
+    const int64_t i = base + threadIdx.x;
+    const int32_t c = (i < ncl) ? counts[i] : 0;
+    s_a[threadIdx.x] = c;
+    s_b[threadIdx.x] = (c + kS2Chunk - 1) / kS2Chunk;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int32_t va = (threadIdx.x >= (unsigned)o) ? s_a[threadIdx.x - o] : 0;
+      const int32_t vb = (threadIdx.x >= (unsigned)o) ? s_b[threadIdx.x - o] : 0;
+      __syncthreads();
+      s_a[threadIdx.x] += va;
+      s_b[threadIdx.x] += vb;
+      __syncthreads();
+    }
+    if (i < ncl) {
+      offsets[i] = carry_a + s_a[threadIdx.x] - c;
+      chunk_off[i] = carry_b + s_b[threadIdx.x] - (c + kS2Chunk - 1) / kS2Chunk;
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) {
+      carry_a += s_a[1023];
+      carry_b += s_b[1023];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    offsets[ncl] = carry_a;
+    chunk_off[ncl] = carry_b;
+  }
+}
+
+__global__ void cluster_fill_kernel(const int32_t* __restrict__ blk2, int64_t entries, int32_t N, int32_t K,
+                                    int64_t M2, const int32_t* __restrict__ offsets, int32_t* cursor,
+                                    int32_t* pairs) {
+  const int64_t NK = (int64_t)N * K;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t j2 = blk2[e];
+    if (j2 < 0) continue;
+    const int64_t c = (e / NK) * M2 + j2;
+    const int32_t pos = atomicAdd(&cursor[c], 1);
+    pairs[offsets[c] + pos] = (int32_t)(e % NK);  // t * K + slot
+  }
+}
+
+// ---- MFMA fragments ---------------------------------------------------------
+template <typename T>
+struct Frag;
+template <>
+struct Frag<uint16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    v = *reinterpret_cast<const bf16x8*>(&z);
+  }
+};
+template <>
+struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float* p) { load8<float>(p, v); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+};
+__device__ __forceinline__ floatx4 mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, floatx4 acc) {
+  return mma16x16x32(a.v, b.v, acc);
+}
+__device__ __forceinline__ floatx4 mma(const Frag<float>& a, const Frag<float>& b, floatx4 acc) {
+  return mma16x16x32(a.v, b.v, acc);
+}
+
+struct S2Args {
+  const void* q;
+  const void* k;
+  const int32_t* offsets;
+  const int32_t* chunk_off;
+  const int32_t* pairs;
+  float* scores;  // [B][Hkv][N][K][2]
+  int64_t ncl, M1, M2;
+  int32_t B, N, Hq, Hkv, C, K;
+  int32_t causal;
+  int64_t cap;
+  float scale;
+};
+
+// NCB: 16-key column blocks covering the 2C keys of a tile (2C <= 16 NCB).
+template <typename T, int D, int G, int NCB>
+__global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
+  constexpr int NS = D / 32;           // 32-wide contraction steps
+  constexpr int TQ = 16 / G;           // queries per 16-row tile
+  constexpr int PITCH = D + 16 / sizeof(T);  // LDS row pitch (elements)
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* s_k = reinterpret_cast<T*>(smem_raw);  // [2C][PITCH]
+  __shared__ int32_t s_t[kS2Waves][16];
+  __shared__ int32_t s_slot[kS2Waves][16];
+
+  const int64_t chunk = blockIdx.x;
+  if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
+  // cluster c with chunk_off[c] <= chunk < chunk_off[c + 1]
+  int64_t lo = 0, hi = a.ncl;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a.chunk_off[mid] <= chunk) lo = mid;
+    else hi = mid;
+  }
+  const int64_t c = lo;
+  const int64_t bh = c / a.M2;
+  const int64_t j2 = c % a.M2;
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kS2Chunk;
+  const int64_t p_end_c = a.offsets[c + 1];
+  const int64_t p_end = p_begin + kS2Chunk < p_end_c ? p_begin + kS2Chunk : p_end_c;
+
+  // key tile: leaves 2*j2 and 2*j2+1 (2C rows, zero rows past the sequence)
+  const int C = a.C;
+  const int rows = 2 * C;
+  const int ncb = (rows + 15) / 16;
+  const T* kh = static_cast<const T*>(a.k) + bh * a.cap * D;
+  const int64_t key0 = 2 * j2 * (int64_t)C;
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
+  for (int i = threadIdx.x; i < ncb * 16 * (D / EPV); i += blockDim.x) {
+    const int r = i / (D / EPV), d = (i % (D / EPV)) * EPV;
+    const int64_t key = key0 + r;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < rows && key < a.N) v = *reinterpret_cast<const uint4*>(kh + key * D + d);
+    *reinterpret_cast<uint4*>(s_k + r * PITCH + d) = v;
+  }
+  __syncthreads();
+
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+  const T* qb = static_cast<const T*>(a.q);
+  for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += (int64_t)kS2Waves * TQ) {
+    const int nq = (int)((p_end - tile) < TQ ? (p_end - tile) : TQ);
+    if (lane < TQ) {
+      const int32_t pr = (lane < nq) ? a.pairs[tile + lane] : -1;
+      s_t[w][lane] = pr >= 0 ? pr / a.K : -1;
+      s_slot[w][lane] = pr >= 0 ? pr % a.K : -1;
+    }
+    wave_sync();
+    // A fragments: row = col (0..15) -> query col / G, head col % G
+    const int qi_a = col / G, hh = col % G;
+    const int32_t ta = s_t[w][qi_a < TQ ? qi_a : 0];
+    Frag<T> fa[NS];
+    if (qi_a < nq) {
+      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + ta) * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fa[s].load(qrow + g * (D / 4) + 8 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fa[s].zero();
+    }
+    // S = Q K^T, 16 rows x 2C columns
+    floatx4 acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (cb < ncb) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          Frag<T> fb;
+          fb.load(s_k + (cb * 16 + col) * PITCH + g * (D / 4) + 8 * s);
+          acc[cb] = mma(fa[s], fb, acc[cb]);
+        }
+      }
+    }
+    // masked LSE over each leaf's keys, per row (query head)
+    float lse[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+      const int qi = row / G;
+      const int64_t t = (qi < nq) ? s_t[w][qi] : -1;
+      float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int cc = cb * 16 + col;
+        const int l = cc >= C ? 1 : 0;
+        const int64_t leaf = 2 * j2 + l;
+        const int64_t key = leaf * C + (cc - l * C);
+        const bool valid = cb < ncb && cc < rows && leaf < a.M1 && key < a.N && (!a.causal || key <= t) && t >= 0;
+        const float x = valid ? acc[cb][i] * a.scale : -INFINITY;
+        acc[cb][i] = x;
+        mx[l] = fmaxf(mx[l], x);
+      }
+      mx[0] = group_max<16>(mx[0]);
+      mx[1] = group_max<16>(mx[1]);
+      float sm[2] = {0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int cc = cb * 16 + col;
+        const int l = cc >= C ? 1 : 0;
+        const float x = acc[cb][i];
+        if (x != -INFINITY) sm[l] += __expf(x - mx[l]);
+      }
+      sm[0] = group_sum<16>(sm[0]);
+      sm[1] = group_sum<16>(sm[1]);
+#pragma unroll
+      for (int l = 0; l < 2; ++l) lse[i][l] = (mx[l] == -INFINITY) ? -INFINITY : mx[l] + __logf(sm[l]);
+    }
+    // sum over the G heads of each query and write the pair's two leaf scores
+    float* out_base = a.scores + bh * (int64_t)a.N * a.K * 2;
+    if (G <= 4) {
+#pragma unroll
+      for (int qq = 0; qq < 4 / G; ++qq) {
+        float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          u0 += lse[qq * G + i][0];
+          u1 += lse[qq * G + i][1];
+        }
+        const int qi = (4 * g) / G + qq;
+        if (col == qq && qi < nq) {
+          const int64_t o = ((int64_t)s_t[w][qi] * a.K + s_slot[w][qi]) * 2;
+          out_base[o] = u0;
+          out_base[o + 1] = u1;
+        }
+      }
+    } else {
+      float u0 = lse[0][0] + lse[1][0] + lse[2][0] + lse[3][0];
+      float u1 = lse[0][1] + lse[1][1] + lse[2][1] + lse[3][1];
+      u0 += __shfl_xor(u0, 16);
+      u1 += __shfl_xor(u1, 16);
+      if (G == 16) {
+        u0 += __shfl_xor(u0, 32);
+        u1 += __shfl_xor(u1, 32);
+      }
+      const int qi = (4 * g) / G;
+      const bool writer = (G == 8) ? ((g & 1) == 0 && col == 0) : (lane == 0);
+      if (writer && qi < nq) {
+        const int64_t o = ((int64_t)s_t[w][qi] * a.K + s_slot[w][qi]) * 2;
+        out_base[o] = u0;
+        out_base[o + 1] = u1;
+      }
+    }
+    wave_sync();
+  }
+}
+
+// ---- final top-K per (b, h, t) ------------------------------------------------
+struct TopkArgs {
+  const int32_t* blk2;
+  const float* scores;
+  int32_t* idx;
+  float* score;
+  int32_t B, N, Hkv, K;
+};
+
+__global__ __launch_bounds__(kTopkWaves* kWave) void final_topk_kernel(TopkArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * kTopkWaves + threadIdx.x / kWave;
+  const int64_t total = (int64_t)a.B * a.Hkv * a.N;
+  if (wid >= total) return;
+  const int lane = lane_id();
+  const int slot = lane >> 1, l = lane & 1;
+  uint64_t key = 0ull;
+  if (slot < a.K) {
+    const int32_t j2 = a.blk2[wid * a.K + slot];
+    if (j2 >= 0) {
+      const float sc = a.scores[(wid * a.K + slot) * 2 + l];
+      if (sc != -INFINITY) key = score_key(sc, 2 * j2 + l);
+    }
+  }
+  key = wave_sort_desc(key);
+  const bool kept = lane < a.K && key != 0ull;
+  uint64_t k2 = kept ? index_key(key_index(key), key_score(key)) : 0ull;
+  k2 = wave_sort_desc(k2);
+  if (lane < a.K) {
+    const bool v = k2 != 0ull;
+    a.idx[wid * a.K + lane] = v ? index_key_index(k2) : -1;
+    if (a.score) a.score[wid * a.K + lane] = v ? index_key_score(k2) : -INFINITY;
+  }
+}
+
+hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const int32_t* blk2, int32_t* idx,
+                         float* score, void* ws, hipStream_t stream) {
+  const S2Layout L = s2_layout(p);
+  char* base = static_cast<char*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
+  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
+  int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
+  float* scores = reinterpret_cast<float*>(base + L.off_scores);
+  const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
+  const int64_t entries = (int64_t)p.B * p.Hkv * p.N * p.K;
+  const unsigned ew_blocks = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
+  const unsigned cl_blocks = (unsigned)((L.ncl + 255) / 256 < 65536 ? (L.ncl + 255) / 256 : 65536);
+
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, stream, counts, L.ncl, 0);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, stream, cursor, L.ncl, 0);
+  hipLaunchKernelGGL(cluster_count_kernel, dim3(ew_blocks), dim3(256), 0, stream, blk2, entries, p.N * p.K, M2,
+                     counts);
+  hipLaunchKernelGGL(cluster_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, L.ncl, offsets, chunk_off);
+  hipLaunchKernelGGL(cluster_fill_kernel, dim3(ew_blocks), dim3(256), 0, stream, blk2, entries, p.N, p.K, M2,
+                     offsets, cursor, pairs);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  S2Args a{q, k, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, p.B, p.N, p.Hq, p.Hkv, p.C, p.K,
+           p.causal ? 1 : 0, p.cap, p.scale};
+  const int64_t max_chunks = (entries + kS2Chunk - 1) / kS2Chunk + L.ncl;
+  err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    constexpr int D = decltype(dc)::value;
+    constexpr int G = decltype(gc)::value;
+    const size_t lds = (size_t)((2 * p.C + 15) / 16 * 16) * (D + 16 / sizeof(T)) * sizeof(T);
+    auto run = [&](auto kern) -> hipError_t {
+      if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3((unsigned)max_chunks), dim3(kS2Waves * kWave), lds, stream, a);
+      return hipSuccess;
+    };
+    hipError_t e;
+    if (p.C <= 32)
+      e = run(leaf_score_kernel<T, D, G, 4>);
+    else if (p.C <= 64)
+      e = run(leaf_score_kernel<T, D, G, 8>);
+    else
+      e = run(leaf_score_kernel<T, D, G, 16>);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  });
+  if (err != hipSuccess) return err;
+  TopkArgs ta{blk2, scores, idx, score, p.B, p.N, p.Hkv, p.K};
+  const int64_t waves = (int64_t)p.B * p.Hkv * p.N;
+  hipLaunchKernelGGL(final_topk_kernel, dim3((unsigned)((waves + kTopkWaves - 1) / kTopkWaves)),
+                     dim3(kTopkWaves * kWave), 0, stream, ta);
+  return hipGetLastError();
+}
+
+}  // namespace pisa

@@ -1,0 +1,172 @@
+/*
+ * pisa.h -- C ABI of the PISA hot path on AMD Instinct MI355X (gfx950).
+ *
+ * PISA ("Block Sparse Attention with Log-Linear Complexity") selects, for every
+ * query, K key blocks of C tokens by a coarse-to-fine top-K descent over a
+ * mean-pooled key pyramid, scoring blocks by log-sum-exp, then runs softmax
+ * attention over the raw keys and values of the selected blocks.  Citations
+ * refer to the hyper.ai page of the paper (the only page with definitions),
+ * by section:
+ *   [BSA] block-sparse attention (o_t equation; flat selection cost)
+ *   [PYR] pyramid key-block hierarchy (level sizes, Concat, mean pooling)
+ *   [SEL] coarse-to-fine top-K selection (initial set, expansion, gK bound,
+ *         keep-all rule, LSE block score)
+ *   [KER] kernel implementation (GQA score sum, two-stage train/prefill
+ *         kernels, query clusters and Q_tile, fused decode kernel)
+ *
+ * Conventions (all entry points):
+ *   - Pointers are DEVICE memory unless stated.  The caller owns every buffer;
+ *     the library never allocates device memory, never synchronises the
+ *     stream, and launches only on `stream` (asynchronously).
+ *   - Tensors are dense row-major.  q: [B][Hq][N][D]; k, v: [B][Hkv][cap][D]
+ *     (cap = problem.cap, or N when cap is 0); o: [B][Hq][N][D].
+ *   - Element types: PISA_F32 (float) or PISA_BF16 (bfloat16 bit patterns,
+ *     uint16_t).  All accumulation is fp32; summaries are stored in fp32.
+ *   - Query head h' belongs to KV head h' / G_Q with G_Q = Hq / Hkv.
+ *   - Indices are 0-based.  Leaf j holds tokens [jC, min(jC + C, N)).
+ *   - Causal problems: a block at any level is valid for query t iff its first
+ *     token is <= t; keys i > t are masked in leaf scores and attention.
+ *   - Ties in every top-K are broken toward the lower block index.
+ *   - Arguments are validated on the host before any launch; an invalid one
+ *     returns PISA_ERR_INVALID_ARG, an unsupported shape PISA_ERR_UNSUPPORTED,
+ *     a too-small workspace PISA_ERR_WORKSPACE, a HIP launch failure
+ *     PISA_ERR_HIP.  Outputs are undefined unless PISA_OK is returned.
+ *     pisa_last_error() then describes the problem (thread-local string).
+ *   - Supported in this version: g == 2 (the page's merge factor), D in
+ *     {64, 128}, G_Q in {1, 2, 4, 8, 16}, 1 <= K <= 32, 1 <= C <= 128.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_ERR_INVALID_ARG = 1,
+  PISA_ERR_UNSUPPORTED = 2,
+  PISA_ERR_WORKSPACE = 3,
+  PISA_ERR_HIP = 4
+} pisa_status;
+
+typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+/* Selection schedule; every schedule returns identical results. */
+typedef enum {
+  PISA_SELECT_AUTO = 0,      /* two-stage                                     */
+  PISA_SELECT_TWO_STAGE = 1, /* [KER] stage 1 routing, query clusters, MFMA
+                                leaf scoring, final top-K                    */
+  PISA_SELECT_FUSED = 2      /* one program per (query, KV head) walks every
+                                level and scores raw leaf keys itself ([KER]
+                                decode design)                               */
+} pisa_select_algo;
+
+typedef struct {
+  int32_t B, N, Hq, Hkv, D; /* batch, tokens, query heads, KV heads, head dim */
+  int32_t C;                /* leaf block size (the first merge factor, [PYR]) */
+  int32_t g;                /* merge factor above the leaves; must be 2        */
+  int32_t K;                /* blocks kept per level ([SEL])                   */
+  int32_t causal;           /* 0 or 1                                          */
+  int32_t dtype;            /* pisa_dtype of q, k, v, o                         */
+  float scale;              /* logit scale; 0 => 1/sqrt(D)                      */
+  int32_t q_tile;           /* stage-2 queries per MFMA tile; 0 => 16/G_Q.
+                               Only changes the schedule, never the result.    */
+  int32_t cap;              /* token capacity of k/v rows and of the pyramid;
+                               0 => N.  Must be >= N.                           */
+  int32_t select_algo;      /* pisa_select_algo                                 */
+} pisa_problem;
+
+/* ---- key pyramid [PYR] ------------------------------------------------- *
+ * Layout: float pyr[B][Hkv][R][D], R = sum over levels l = 1..L(cap) of
+ * M_l(cap), M_1(n) = ceil(n / C), M_{l+1} = ceil(M_l / 2), L(n) the first
+ * level with one block.  Level l of head (b, h) starts at row
+ * sum_{l' < l} M_{l'}(cap).  Level 1 holds leaf means of raw keys; level l+1
+ * holds the mean of each block's existing children (a ragged parent averages
+ * its children's summaries, the mean-pooling equation taken literally).     */
+size_t pisa_pyramid_bytes(const pisa_problem* p);
+int32_t pisa_levels(int64_t n, int32_t C);                 /* L(n)            */
+int64_t pisa_level_rows(int64_t n, int32_t C, int32_t l);  /* M_l(n)          */
+int64_t pisa_level_offset(int64_t cap, int32_t C, int32_t l); /* first row    */
+
+/* Builds levels 1..L(N) of every (b, h) from k[b][h][0..N) (row stride cap).
+ * [PYR] level-0 equation, level-size ceiling equation, mean-pooling equation.
+ * Rows beyond M_l(N) are left untouched.                                      */
+pisa_status pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyr,
+                               hipStream_t stream);
+
+/* ---- selection [SEL], [KER] --------------------------------------------- *
+ * For every (b, h, t): start from the coarsest level's single block; at each
+ * level drop invalid blocks, keep all if <= K remain, else score each block
+ * by sum over the G_Q query heads of h of the log-sum-exp over its valid
+ * children of q . child_summary * scale (at level 1 the children are the raw
+ * keys: the exact raw-key LSE), keep the top K and expand them into their
+ * children.  Output: idx[B][Hkv][N][K] int32 leaf indices, ascending, -1
+ * padded; score (may be NULL) the GQA-summed leaf LSE of each kept leaf
+ * (-inf padded).  Reads pyr built by pisa_build_pyramid for the same k.
+ * ws: device workspace of at least pisa_select_workspace_bytes(p) bytes
+ * (256-byte aligned); its contents on entry do not matter.                  */
+size_t pisa_select_workspace_bytes(const pisa_problem* p);
+pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, const float* pyr,
+                        int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* ---- block-sparse attention [BSA] --------------------------------------- *
+ * o[b][h'][t] = sum_i softmax_i(q . k_i * scale) v_i over the keys i of the
+ * leaves idx[b][h'/G_Q][t][*] (entries < 0 ignored; keys i > t masked when
+ * causal).  o has the input dtype; lse (may be NULL) is float [B][Hq][N], the
+ * log-sum-exp of the attended logits.  A query with no attended key gets
+ * o = 0 and lse = -inf.  ws: at least pisa_attn_workspace_bytes(p) bytes.   */
+size_t pisa_attn_workspace_bytes(const pisa_problem* p);
+pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k, const void* v,
+                             const int32_t* idx, void* o, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ---- flat single-level selector (measurement baseline) [BSA] ------------ *
+ * Scores every valid leaf j by sum over the G_Q query heads of
+ * q_{h',t} . P_1[j] * scale and keeps the top K (same order and output
+ * format as pisa_select).  Reads level 1 of pyr.                            */
+size_t pisa_flat_workspace_bytes(const pisa_problem* p);
+pisa_status pisa_flat_select(const pisa_problem* p, const void* q, const float* pyr, int32_t* idx,
+                             float* score, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- decode [KER] decode paragraph --------------------------------------- *
+ * One generated token per sequence.  For each sequence s with n = len[s]
+ * cached tokens (n < cap): writes k_new/v_new at row n of the caches,
+ * recomputes the mean of leaf n / C and of its ancestors (growing a level when
+ * the leaf count crosses a power of two), then selects for the new query at
+ * t = n (every block of the n + 1 tokens is valid) with one fused program per
+ * (s, h), runs attention over the selected leaves into o[s][h'][D] and finally
+ * sets len[s] = n + 1.  The pyramid must hold the pyramid of the first n
+ * tokens (pisa_build_pyramid with N = n, cap = cap initialises it).
+ * k_cache, v_cache: [S][Hkv][cap][D]; pyr: [S][Hkv][R(cap)][D] fp32;
+ * len: [S] int32 (device); q_new: [S][Hq][D]; k_new, v_new: [S][Hkv][D];
+ * o: [S][Hq][D]; idx: [S][Hkv][K] (may be NULL); score likewise.
+ * err (may be NULL): device int32 set to 1 if some len[s] >= cap (that
+ * sequence is then left untouched); never cleared by the library.          */
+typedef struct {
+  int32_t S, cap, Hq, Hkv, D;
+  int32_t C, g, K;
+  int32_t dtype;
+  float scale; /* 0 => 1/sqrt(D) */
+} pisa_decode_problem;
+
+pisa_status pisa_decode_step(const pisa_decode_problem* p, void* k_cache, void* v_cache, float* pyr,
+                             int32_t* len, const void* q_new, const void* k_new, const void* v_new,
+                             void* o, int32_t* idx, float* score, int32_t* err, hipStream_t stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* pisa_last_error(void);
+/* Library version string (static storage). */
+const char* pisa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

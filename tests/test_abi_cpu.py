@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point declared in include/pisa.h, its geometry helpers agree with
+the oracle's independent ones, and invalid arguments are rejected on the host
+with the documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from hierarchical_block_sparse_mean_amd import pisa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "pisa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(pisa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pisa.LIB_PATH):
+        from hierarchical_block_sparse_mean_amd.build import build_library
+        build_library()
+    return pisa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(pisa.EXPORTS)
+    assert lib.pisa_version().decode().startswith("pisa-mi355x")
+
+
+@pytest.mark.parametrize("n,C", [(1, 64), (64, 64), (65, 64), (1000, 64), (1024, 64), (131072, 64), (262144, 128),
+                                 (131073, 64), (7, 3), (330, 64)])
+def test_geometry_matches_oracle(lib, n, C):
+    L = lib.pisa_levels(n, C)
+    assert L == oracle.levels(n, C)
+    off = 0
+    for l in range(1, L + 1):
+        assert lib.pisa_level_rows(n, C, l) == oracle.level_rows(n, C, l)
+        assert lib.pisa_level_offset(n, C, l) == off
+        off += lib.pisa_level_rows(n, C, l)
+    assert lib.pisa_level_offset(n, C, L + 1) == -1
+
+
+def _p(**kw):
+    base = dict(B=1, N=1024, Hq=4, Hkv=1, D=64, C=64, K=4, causal=False, dtype="f32")
+    base.update(kw)
+    return pisa.Problem(**base)
+
+
+FAKE = 4096  # a non-NULL address; validation must reject before using it
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), pisa.PISA_ERR_INVALID_ARG),
+    (dict(N=0), pisa.PISA_ERR_INVALID_ARG),
+    (dict(K=0), pisa.PISA_ERR_INVALID_ARG),
+    (dict(C=0), pisa.PISA_ERR_INVALID_ARG),
+    (dict(g=3), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(D=96), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(Hq=12, Hkv=4), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(K=33), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(C=256), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(cap=100), pisa.PISA_ERR_INVALID_ARG),
+    (dict(q_tile=3), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(select_algo=7), pisa.PISA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), pisa.PISA_ERR_INVALID_ARG),
+])
+def test_invalid_problem_rejected(lib, kw, status):
+    p = _p(**kw).c()
+    rc = lib.pisa_build_pyramid(ctypes.byref(p), FAKE, FAKE, None)
+    assert rc == status, lib.pisa_last_error()
+    assert lib.pisa_last_error()
+    assert lib.pisa_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == status
+    assert lib.pisa_pyramid_bytes(ctypes.byref(p)) == 0
+
+
+def test_null_pointers_and_small_workspace(lib):
+    p = _p().c()
+    assert lib.pisa_build_pyramid(ctypes.byref(p), None, FAKE, None) == pisa.PISA_ERR_INVALID_ARG
+    assert lib.pisa_select(ctypes.byref(p), FAKE, None, FAKE, FAKE, None, FAKE, 1 << 40, None) == pisa.PISA_ERR_INVALID_ARG
+    need = lib.pisa_select_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert lib.pisa_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == pisa.PISA_ERR_WORKSPACE
+    assert "workspace" in lib.pisa_last_error().decode()
+    assert lib.pisa_sparse_attn(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 256, None) == \
+        pisa.PISA_ERR_INVALID_ARG
+    assert lib.pisa_flat_select(ctypes.byref(p), None, FAKE, FAKE, None, FAKE, 256, None) == pisa.PISA_ERR_INVALID_ARG
+    assert lib.pisa_build_pyramid(None, FAKE, FAKE, None) == pisa.PISA_ERR_INVALID_ARG
+
+
+def test_decode_validation(lib):
+    d = pisa.DecodeProblem(S=2, cap=100, Hq=4, Hkv=1, D=64, C=64, K=4, dtype="f32")
+    args = [FAKE] * 7
+    assert lib.pisa_decode_step(None, *args, FAKE, None, None, None, None) == pisa.PISA_ERR_INVALID_ARG
+    bad = pisa.DecodeProblem(S=2, cap=100, Hq=4, Hkv=1, D=64, C=64, K=64, dtype="f32").c()
+    assert lib.pisa_decode_step(ctypes.byref(bad), *args, FAKE, None, None, None, None) == pisa.PISA_ERR_UNSUPPORTED
+    bad = pisa.DecodeProblem(S=2, cap=100, Hq=4, Hkv=1, D=64, C=64, K=4, dtype="f32").c()
+    assert lib.pisa_decode_step(ctypes.byref(bad), FAKE, None, *([FAKE] * 5), FAKE, None, None, None, None) == \
+        pisa.PISA_ERR_INVALID_ARG
+
+
+def test_pyramid_bytes(lib):
+    p = _p(N=1000, cap=1100)
+    rows = sum(oracle.level_rows(1100, 64, l) for l in range(1, oracle.levels(1100, 64) + 1))
+    assert lib.pisa_pyramid_bytes(ctypes.byref(p.c())) == 4 * rows * 64
+
+
+def test_product_has_no_oracle_dependency():
+    pkg = os.path.join(ROOT, "hierarchical_block_sparse_mean_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp", ".c")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    text = f.read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "pisa_oracle" not in text and "libpisa_oracle" not in text, fn
