@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""PISA prefill benchmark on one MI355X (gfx950).
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: key pyramid (pisa_build_pyramid), two-stage
+selection (pisa_select) and block-sparse attention (pisa_sparse_attn).
+Default workload: prefill N=131072, B=1, Hq=32, Hkv=8, d=128, C=64, g=2,
+K=16, bf16, causal, planted needle leaves.  Prints ONE JSON line.
+
+Also measured in the same process: the flat single-level selector on the same
+inputs (leaf pooling + flat top-K), per-kernel times from HIP events recorded
+on the launch stream (library timer), the roofline of the dominant kernel,
+and the CPU oracle timed on a bounded sample of query positions (with a
+parity summary of the GPU outputs at those positions).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"hbm_GBps": 8000.0, "mfma_bf16_TFLOPs": 2500.0, "mfma_f32_TFLOPs": 157.3}
+METRIC = "PISA select+sparse-attn prefill tokens/s and select ms at 128K/256K, 1 GPU"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flat", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy first (reference for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def dev(x):
+    import numpy as np
+    import torch
+
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def attended_keys(idx, N: int, C: int, causal: bool):
+    """Sum over (b, h, t, slot) of the keys attention reads for that leaf."""
+    import torch
+
+    j = idx.long()
+    t = torch.arange(N, device=idx.device).view(1, 1, N, 1)
+    lo = j * C
+    hi = torch.clamp(lo + C, max=N)
+    if causal:
+        hi = torch.minimum(hi, t + 1)
+    keys = torch.where(j >= 0, torch.clamp(hi - lo, min=0), torch.zeros_like(j))
+    return int(keys.sum().item())
+
+
+def stage1_scored_keys(blk2, N: int, C: int, causal: bool):
+    """Keys scored by stage 2: both leaves of every kept level-2 block."""
+    import torch
+
+    j2 = blk2.long()
+    t = torch.arange(N, device=blk2.device).view(1, 1, N, 1)
+    total = 0
+    pairs = int((j2 >= 0).sum().item())
+    for l in (0, 1):
+        lo = (2 * j2 + l) * C
+        hi = torch.clamp(lo + C, max=N)
+        if causal:
+            hi = torch.minimum(hi, t + 1)
+        total += int(torch.where(j2 >= 0, torch.clamp(hi - lo, min=0), torch.zeros_like(j2)).sum().item())
+    return total, pairs
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head with no "
+              "collective, see DESIGN.md", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from hierarchical_block_sparse_mean_amd import inputs as I
+    from hierarchical_block_sparse_mean_amd import pisa
+
+    torch.cuda.set_device(0)
+    w = I.workload(args.workload)
+    if w.steps:
+        raise SystemExit("bench.py times prefill workloads; decode is measured by its own tests")
+    log(f"workload {w.name}: B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} C={w.C} K={w.K} {w.dtype} "
+        f"causal={w.causal} needles={w.needles}")
+    t0 = time.perf_counter()
+    data = I.generate(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+    q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype)
+    pyr = pisa.alloc_pyramid(p)
+    ws = pisa.workspace(pisa.select_workspace_bytes(p))
+    idx = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device="cuda")
+    score = torch.empty_like(idx, dtype=torch.float32)
+    o = torch.empty_like(q)
+    attn_ws = pisa.workspace(pisa.attn_workspace_bytes(p))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB write done")
+        del src, dst
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pisa.build_pyramid(p, k, pyr)
+        if ev:
+            ev[1].record()
+        pisa.select(p, q, k, pyr, idx=idx, score=score, ws=ws)
+        if ev:
+            ev[2].record()
+        pisa.sparse_attn(p, q, k, v, idx, o=o, lse=None, ws=attn_ws, with_lse=False)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    pisa.timer_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kernels = pisa.timer_report()
+    pisa.timer_enable(False)
+    stage = {"pyramid": 0.0, "select": 0.0, "attention": 0.0}
+    for e in evs:
+        stage["pyramid"] += e[0].elapsed_time(e[1])
+        stage["select"] += e[1].elapsed_time(e[2])
+        stage["attention"] += e[2].elapsed_time(e[3])
+    stage = {kk: vv / args.steps for kk, vv in stage.items()}
+    ms_per_step = wall * 1000.0 / args.steps
+    tokens = w.B * w.N
+    value = tokens / (ms_per_step / 1000.0)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, stages {stage}")
+    per_kernel = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
+                  for name, (n, tot) in kernels.items()}
+
+    # ---- algorithmic work of the kernels -----------------------------------
+    G = w.gq
+    esize = 2 if w.dtype == "bf16" else 4
+    mfma_peak = PEAK["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else PEAK["mfma_f32_TFLOPs"]
+    blk2 = ws[: w.B * w.Hkv * w.N * w.K * 4].view(torch.int32).view(w.B, w.Hkv, w.N, w.K)
+    scored_keys, s1_pairs = stage1_scored_keys(blk2, w.N, w.C, w.causal)
+    attn_keys = attended_keys(idx, w.N, w.C, w.causal)
+    M = [pisa.level_rows(w.N, w.C, l) for l in range(1, pisa.levels(w.N, w.C) + 1)]
+    work = {
+        # 4 d flops per attended (query head, key): q.k and p.v
+        "attn_query": ("mfma", 4.0 * w.D * G * attn_keys, "TFLOP/s",
+                       f"4*d flops per attended (query head, key) pair; {attn_keys * G} pairs"),
+        # 2 d flops per scored (query head, raw key)
+        "leaf_score": ("mfma", 2.0 * w.D * G * scored_keys, "TFLOP/s",
+                       f"2*d flops per scored (query head, raw key); {scored_keys * G} pairs from {s1_pairs} "
+                       "(query, level-2 block) pairs"),
+        # read every key once, write leaf means and the four levels above them
+        "pyr_leaf": ("hbm", float(w.B * w.Hkv * (w.N * w.D * esize + sum(M[:5]) * w.D * 4)), "GB/s",
+                     "N*d*elem read + (M1+..+M5)*d*4 written per (b, h)"),
+    }
+    dominant = max(per_kernel, key=lambda n: per_kernel[n]["ms_per_step"])
+    roofline = None
+    if dominant in work:
+        bound, amount, unit, note = work[dominant]
+        avg_s = per_kernel[dominant]["avg_ms"] / 1000.0
+        per_launch = amount  # one launch per step for these kernels
+        if unit == "TFLOP/s":
+            achieved, peak = per_launch / avg_s / 1e12, mfma_peak
+        else:
+            achieved, peak = per_launch / avg_s / 1e9, PEAK["hbm_GBps"]
+        roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+                    "unit": unit, "frac": round(achieved / peak, 5), "traffic": None,
+                    "avg_launch_ms": round(per_kernel[dominant]["avg_ms"], 4), "work_per_launch": amount,
+                    "work_note": note}
+
+    # ---- flat single-level selector on the same inputs ------------------------
+    flat_ms = None
+    if not args.no_flat:
+        fidx = torch.empty_like(idx)
+        for _ in range(max(1, args.warmup)):
+            pisa.build_pyramid(p, k, pyr)
+            pisa.flat_select(p, q, pyr, idx=fidx, with_score=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            pisa.build_pyramid(p, k, pyr)
+            pisa.flat_select(p, q, pyr, idx=fidx, with_score=False)
+        e1.record()
+        torch.cuda.synchronize()
+        flat_ms = e0.elapsed_time(e1) / args.steps
+        log(f"flat selector (leaf pooling + flat top-K): {flat_ms:.3f} ms")
+        # re-run the PISA step so idx/score/o hold its outputs for the parity summary
+        step()
+        torch.cuda.synchronize()
+
+    # ---- CPU oracle on a bounded sample, with a parity summary -----------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        op = oracle.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal)
+        rng = np.random.default_rng(w.seed + 99)
+
+        def sample(n):
+            base = np.linspace(0, w.N, n, endpoint=False)
+            return np.unique(np.minimum(w.N - 1, (base + rng.uniform(0, w.N / n)).astype(np.int64)))
+
+        # calibrate the per-position cost (two sizes, so the per-head pyramid
+        # build cancels), then size the sample to about cpu_seconds of wall time
+        def timed(n):
+            tt = sample(n)
+            ta = time.perf_counter()
+            ii, _, _, _ = oracle.select(op, data["q"], data["k"], ts=tt)
+            oracle.attention(op, data["q"], data["k"], data["v"], ii, ts=tt)
+            return time.perf_counter() - ta
+
+        t_small, t_big = timed(64), timed(512)
+        per_pos = max((t_big - t_small) / 448.0, 1e-5)
+        fixed = max(t_small - 64 * per_pos, 0.0)
+        n_main = int(min(16384, max(256, (args.cpu_seconds - fixed) / per_pos)))
+        ts = sample(n_main)
+        log(f"oracle sample: {len(ts)} positions (calibration: {per_pos * 1e3:.2f} ms/position, {fixed:.2f}s fixed)")
+        t_a = time.perf_counter()
+        o_idx, o_score, o_gap, cnt = oracle.select(op, data["q"], data["k"], ts=ts)
+        o_o, _ = oracle.attention(op, data["q"], data["k"], data["v"], o_idx, ts=ts)
+        t_cpu = time.perf_counter() - t_a
+        cpu = {"value": round(len(ts) / t_cpu, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"{len(ts)} query positions spread evenly over t in [0, {w.N}), every (b, KV head); "
+                         f"oracle pyramid per head + selection + attention, fp64, {t_cpu:.1f}s wall"}
+        g_idx = idx.cpu().numpy()[:, :, ts]
+        g_score = score.cpu().numpy()[:, :, ts].astype(np.float64)
+        same = (g_idx == o_idx).all(-1)
+        exempt = o_gap < 1e-3
+        m = same[..., None] & (o_idx >= 0)
+        serr = float((np.abs(g_score[m] - o_score[m]) / np.maximum(1.0, np.abs(o_score[m]))).max()) if m.any() else 0.0
+        okh = np.repeat(same, G, axis=1)
+        g_o = o.float().cpu().numpy()[:, :, ts].astype(np.float64)
+        aerr = float(np.abs(g_o - o_o).max(axis=-1)[okh].max()) if okh.any() else 0.0
+        parity = {"positions": int(len(ts)), "non_exempt_mismatches": int((~same & ~exempt).sum()),
+                  "exempt_fraction": round(float(exempt.mean()), 5), "exact_match_rate": round(float(same.mean()), 5),
+                  "max_score_rel_err": serr, "max_attn_abs_err": aerr,
+                  "oracle_child_dots_per_query": cnt["child_dots"] / max(1, cnt["queries"]),
+                  "oracle_leaf_pairs_per_query": cnt["leaf_pairs"] / max(1, cnt["queries"])}
+        log(f"parity on sample: {parity}")
+
+    select_ms = stage["pyramid"] + stage["select"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.D, "C": w.C, "g": 2,
+                   "K": w.K, "causal": w.causal, "needles": w.needles, "select": "two_stage"},
+        "select_ms": round(select_ms, 4),
+        "flat_select_ms": None if flat_ms is None else round(flat_ms, 4),
+        "stage_ms": {kk: round(vv, 4) for kk, vv in stage.items()},
+        "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 4), "launches_per_step": vv["launches"] / args.steps}
+                    for kk, vv in per_kernel.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

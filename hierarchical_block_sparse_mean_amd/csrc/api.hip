@@ -1,10 +1,14 @@
 // C ABI of the PISA hot path: argument validation, pyramid geometry,
 // workspace layout and kernel launches.  See include/pisa.h for the contract.
 #include <math.h>
+#include <string.h>
 
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/pisa.h"
 #include "kernels.h"
@@ -95,9 +99,88 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
 
 size_t blk2_bytes(const pisa::Problem& q) { return align256(sizeof(int32_t) * (size_t)q.B * q.Hkv * q.N * q.K); }
 
+// ---- per-kernel timer ------------------------------------------------------
+struct TimerRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_timer_mu;
+bool g_timer_on = false;
+std::vector<TimerRecord> g_records;
+std::vector<hipEvent_t> g_event_pool;
+hipEvent_t g_open_start = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
 
+namespace pisa {
+void timer_begin(const char* name, hipStream_t stream) {
+  (void)name;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (!g_timer_on) return;
+  g_open_start = take_event();
+  if (g_open_start) hipEventRecord(g_open_start, stream);
+}
+void timer_end(const char* name, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (!g_timer_on || g_open_start == nullptr) return;
+  hipEvent_t stop = take_event();
+  if (stop == nullptr) return;
+  hipEventRecord(stop, stream);
+  g_records.push_back({name, g_open_start, stop});
+  g_open_start = nullptr;
+}
+}  // namespace pisa
+
 extern "C" {
+
+void pisa_timer_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (auto& r : g_records) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_records.clear();
+  g_timer_on = on != 0;
+}
+
+int32_t pisa_timer_report(char* buf, size_t cap) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  std::map<std::string, std::pair<int64_t, double>> agg;
+  for (auto& r : g_records) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      auto& a = agg[r.name];
+      a.first += 1;
+      a.second += ms;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_records.clear();
+  std::string out;
+  char line[256];
+  for (auto& kv : agg) {
+    snprintf(line, sizeof line, "%s\t%lld\t%.6f\n", kv.first.c_str(), (long long)kv.second.first, kv.second.second);
+    out += line;
+  }
+  if (buf != nullptr && cap > 0) {
+    const size_t n = out.size() < cap - 1 ? out.size() : cap - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return (int32_t)agg.size();
+}
 
 const char* pisa_last_error(void) { return g_last_error.c_str(); }
 

@@ -137,11 +137,12 @@ hipError_t launch_decode(const DecodeArgs& d, void* k_cache, void* v_cache, floa
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
-    hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3((unsigned)((int64_t)d.S * d.Hkv)), dim3(kWave), 0, stream, a);
+    PISA_LAUNCH("decode", stream, (decode_kernel<T, D, G>), dim3((unsigned)((int64_t)d.S * d.Hkv)), dim3(kWave), 0,
+                a);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_bump_kernel, dim3((d.S + 255) / 256), dim3(256), 0, stream, len, d.S, d.cap);
+  PISA_LAUNCH("decode_bump", stream, decode_bump_kernel, dim3((d.S + 255) / 256), dim3(256), 0, len, d.S, d.cap);
   return hipGetLastError();
 }
 

@@ -84,7 +84,7 @@ hipError_t launch_flat(const Problem& p, const void* q, const float* pyr, int32_
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
-    hipLaunchKernelGGL((flat_kernel<T, D, G>), dim3((unsigned)blocks), dim3(kFlatWaves * kWave), 0, stream, a);
+    PISA_LAUNCH("flat", stream, (flat_kernel<T, D, G>), dim3((unsigned)blocks), dim3(kFlatWaves * kWave), 0, a);
     return hipGetLastError();
   });
 }

@@ -10,6 +10,18 @@
 
 namespace pisa {
 
+// Optional per-kernel timing: when enabled (pisa_timer_enable), every launch
+// made through PISA_LAUNCH is bracketed by two HIP events recorded on the
+// launch stream.
+void timer_begin(const char* name, hipStream_t stream);
+void timer_end(const char* name, hipStream_t stream);
+#define PISA_LAUNCH(name, stream, kernel, grid, block, lds, ...)                  \
+  do {                                                                          \
+    ::pisa::timer_begin(name, stream);                                          \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);          \
+    ::pisa::timer_end(name, stream);                                            \
+  } while (0)
+
 // A validated problem (see pisa.h for the meaning of each field).
 struct Problem {
   int32_t B, N, Hq, Hkv, G, D, C, K;

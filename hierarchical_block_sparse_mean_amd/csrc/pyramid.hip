@@ -131,12 +131,12 @@ hipError_t launch_build_pyramid(const Problem& p, const void* k, float* pyr, hip
   auto leaf = [&](auto tp, auto dc) {
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
-    hipLaunchKernelGGL((pyr_leaf_kernel<T, D>), dim3((unsigned)leaf_blocks), dim3(256), 0, stream, a);
+    PISA_LAUNCH("pyr_leaf", stream, (pyr_leaf_kernel<T, D>), dim3((unsigned)leaf_blocks), dim3(256), 0, a);
     err = hipGetLastError();
     for (int32_t lb = 1 + kLeafLevels; err == hipSuccess && lb < p.L; lb += kUpLevels) {
       const int64_t mb = level_rows(p.N, p.C, lb);
       const int64_t blocks = (int64_t)a.BH * ((mb + kUpChunk - 1) / kUpChunk);
-      hipLaunchKernelGGL((pyr_up_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a, lb);
+      PISA_LAUNCH("pyr_up", stream, (pyr_up_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, a, lb);
       err = hipGetLastError();
     }
   };

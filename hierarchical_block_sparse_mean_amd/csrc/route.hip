@@ -85,10 +85,11 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
     if (fused)
-      hipLaunchKernelGGL((route_kernel<T, D, G, true>), dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, stream, a);
+      PISA_LAUNCH("route_fused", stream, (route_kernel<T, D, G, true>), dim3((unsigned)blocks),
+                  dim3(kRouteWaves * kWave), 0, a);
     else
-      hipLaunchKernelGGL((route_kernel<T, D, G, false>), dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, stream,
-                         a);
+      PISA_LAUNCH("route_stage1", stream, (route_kernel<T, D, G, false>), dim3((unsigned)blocks),
+                  dim3(kRouteWaves * kWave), 0, a);
     return hipGetLastError();
   });
 }
@@ -138,7 +139,8 @@ hipError_t launch_attn_query(const Problem& p, const void* q, const void* k, con
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
-    hipLaunchKernelGGL((attn_query_kernel<T, D, G>), dim3((unsigned)blocks), dim3(kRouteWaves * kWave), 0, stream, a);
+    PISA_LAUNCH("attn_query", stream, (attn_query_kernel<T, D, G>), dim3((unsigned)blocks),
+                dim3(kRouteWaves * kWave), 0, a);
     return hipGetLastError();
   });
 }

@@ -372,13 +372,14 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   const unsigned ew_blocks = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
   const unsigned cl_blocks = (unsigned)((L.ncl + 255) / 256 < 65536 ? (L.ncl + 255) / 256 : 65536);
 
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, stream, counts, L.ncl, 0);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, stream, cursor, L.ncl, 0);
-  hipLaunchKernelGGL(cluster_count_kernel, dim3(ew_blocks), dim3(256), 0, stream, blk2, entries, p.N * p.K, M2,
-                     counts);
-  hipLaunchKernelGGL(cluster_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, L.ncl, offsets, chunk_off);
-  hipLaunchKernelGGL(cluster_fill_kernel, dim3(ew_blocks), dim3(256), 0, stream, blk2, entries, p.N, p.K, M2,
-                     offsets, cursor, pairs);
+  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, counts, L.ncl, 0);
+  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, cursor, L.ncl, 0);
+  PISA_LAUNCH("cluster_count", stream, cluster_count_kernel, dim3(ew_blocks), dim3(256), 0, blk2, entries,
+              p.N * p.K, M2, counts);
+  PISA_LAUNCH("cluster_scan", stream, cluster_scan_kernel, dim3(1), dim3(1024), 0, counts, L.ncl, offsets,
+              chunk_off);
+  PISA_LAUNCH("cluster_fill", stream, cluster_fill_kernel, dim3(ew_blocks), dim3(256), 0, blk2, entries, p.N, p.K,
+              M2, offsets, cursor, pairs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -396,7 +397,7 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
       }
-      hipLaunchKernelGGL(kern, dim3((unsigned)max_chunks), dim3(kS2Waves * kWave), lds, stream, a);
+      PISA_LAUNCH("leaf_score", stream, kern, dim3((unsigned)max_chunks), dim3(kS2Waves * kWave), lds, a);
       return hipSuccess;
     };
     hipError_t e;
@@ -412,8 +413,8 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   if (err != hipSuccess) return err;
   TopkArgs ta{blk2, scores, idx, score, p.B, p.N, p.Hkv, p.K};
   const int64_t waves = (int64_t)p.B * p.Hkv * p.N;
-  hipLaunchKernelGGL(final_topk_kernel, dim3((unsigned)((waves + kTopkWaves - 1) / kTopkWaves)),
-                     dim3(kTopkWaves * kWave), 0, stream, ta);
+  PISA_LAUNCH("final_topk", stream, final_topk_kernel, dim3((unsigned)((waves + kTopkWaves - 1) / kTopkWaves)),
+              dim3(kTopkWaves * kWave), 0, ta);
   return hipGetLastError();
 }
 

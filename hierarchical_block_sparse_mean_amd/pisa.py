@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "PISA_OK", 1: "PISA_ERR_INVALID_ARG", 2: "PISA_ERR_UNSUPPORTE
 EXPORTS = [
     "pisa_pyramid_bytes", "pisa_levels", "pisa_level_rows", "pisa_level_offset", "pisa_build_pyramid",
     "pisa_select_workspace_bytes", "pisa_select", "pisa_attn_workspace_bytes", "pisa_sparse_attn",
-    "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_last_error", "pisa_version",
+    "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
+    "pisa_last_error", "pisa_version",
 ]
 
 
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
         "pisa_flat_workspace_bytes": ([P], sz),
         "pisa_flat_select": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_decode_step": ([DP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "pisa_timer_enable": ([i32], None),
+        "pisa_timer_report": ([ctypes.c_char_p, sz], i32),
         "pisa_last_error": ([], ctypes.c_char_p),
         "pisa_version": ([], ctypes.c_char_p),
     }
@@ -297,6 +300,23 @@ def decode_step(p: DecodeProblem, k_cache, v_cache, pyr, length, q_new, k_new, v
                                    length.data_ptr(), q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                                    o.data_ptr(), _ptr(idx), _ptr(score), _ptr(err), _stream(stream)))
     return o, idx, score
+
+
+def timer_enable(on: bool) -> None:
+    """Start (clearing earlier records) or stop per-kernel HIP event timing."""
+    load().pisa_timer_enable(1 if on else 0)
+
+
+def timer_report() -> dict:
+    """{kernel: (launches, total_ms)} of the launches recorded since
+    timer_enable(True); waits for their events and clears the records."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    load().pisa_timer_report(buf, len(buf))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split("\t")
+        out[name] = (int(n), float(ms))
+    return out
 
 
 def default_scale(D: int) -> float:

@@ -160,6 +160,18 @@ pisa_status pisa_decode_step(const pisa_decode_problem* p, void* k_cache, void* 
                              int32_t* len, const void* q_new, const void* k_new, const void* v_new,
                              void* o, int32_t* idx, float* score, int32_t* err, hipStream_t stream);
 
+/* ---- diagnostics ----------------------------------------------------------- *
+ * Per-kernel timer.  pisa_timer_enable(1) clears earlier records and makes
+ * every kernel launch of the library record a HIP event pair on its launch
+ * stream (a few microseconds of overhead per launch); pisa_timer_enable(0)
+ * stops and clears.  pisa_timer_report waits for the recorded events, writes
+ * one line "kernel<TAB>launches<TAB>total_ms" per kernel name into buf (host
+ * memory, NUL-terminated, truncated to cap bytes), clears the records and
+ * returns the number of kernel names.  Process-wide, not for use from several
+ * host threads at once.                                                      */
+void pisa_timer_enable(int32_t on);
+int32_t pisa_timer_report(char* buf, size_t cap);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* pisa_last_error(void);
 /* Library version string (static storage). */

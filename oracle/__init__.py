@@ -78,6 +78,7 @@ def load(path: str = _LIB_PATH):
     lib.oracle_flat_select.argtypes = [P, vp, vp, vp, i64, vp, vp]
     lib.oracle_flat_select.restype = ctypes.c_int
     lib.oracle_counter_len.argtypes, lib.oracle_counter_len.restype = [], ctypes.c_int
+    lib.oracle_threads.argtypes, lib.oracle_threads.restype = [], ctypes.c_int
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -118,6 +119,11 @@ def _ts(p: Problem, ts) -> np.ndarray:
     if ts is None:
         return np.arange(p.N, dtype=np.int32)
     return np.ascontiguousarray(np.asarray(ts, dtype=np.int32))
+
+
+def threads(lib=None) -> int:
+    """Host threads used by the oracle's parallel loops."""
+    return (lib or load()).oracle_threads()
 
 
 def levels(n: int, C: int, lib=None) -> int:

@@ -48,6 +48,7 @@
  * (bf16 inputs are widened bit-exactly).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -515,3 +516,6 @@ int oracle_build_pyramid(const oracle_problem* p, const void* k, double* pyr) {
 }
 
 int oracle_counter_len(void) { return CNT_LEN; }
+
+/* Host threads the oracle's parallel loops use. */
+int oracle_threads(void) { return omp_get_max_threads(); }
