@@ -67,6 +67,7 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return fail(PISA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (p->cap != 0 && p->cap < p->N) return fail(PISA_ERR_INVALID_ARG, "cap (%d) must be 0 or >= N (%d)", p->cap, p->N);
   if (p->select_algo < 0 || p->select_algo > 2) return fail(PISA_ERR_INVALID_ARG, "unknown select_algo %d", p->select_algo);
+  if (p->attn_algo < 0 || p->attn_algo > 2) return fail(PISA_ERR_INVALID_ARG, "unknown attn_algo %d", p->attn_algo);
   if (p->q_tile < 0) return fail(PISA_ERR_INVALID_ARG, "q_tile must be >= 0");
   const int32_t G = p->Hq / p->Hkv;
   if (p->g != 2) return fail(PISA_ERR_UNSUPPORTED, "merge factor g must be 2 (got %d)", p->g);
@@ -243,19 +244,24 @@ pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, con
 size_t pisa_attn_workspace_bytes(const pisa_problem* p) {
   pisa::Problem q;
   if (validate(p, &q) != PISA_OK) return 0;
-  return 256;
+  if (p->attn_algo == PISA_ATTN_QUERY_MAJOR) return 256;
+  return pisa::attn_leaf_workspace_bytes(q);
 }
 
 pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
                              void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   pisa::Problem pr;
   pisa_status s = validate(p, &pr);
   if (s != PISA_OK) return s;
   if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || o == nullptr)
     return fail(PISA_ERR_INVALID_ARG, "q, k, v, idx and o must be non-NULL");
-  return hip_status(pisa::launch_attn_query(pr, q, k, v, idx, o, lse, stream), "pisa_sparse_attn");
+  if (p->attn_algo == PISA_ATTN_QUERY_MAJOR)
+    return hip_status(pisa::launch_attn_query(pr, q, k, v, idx, o, lse, stream), "pisa_sparse_attn (query-major)");
+  const size_t need = pisa::attn_leaf_workspace_bytes(pr);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws == nullptr ? 0 : ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(PISA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return hip_status(pisa::launch_attn_leaf(pr, q, k, v, idx, o, lse, ws, stream), "pisa_sparse_attn (leaf-major)");
 }
 
 size_t pisa_flat_workspace_bytes(const pisa_problem* p) {

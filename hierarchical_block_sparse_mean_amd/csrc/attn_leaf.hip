@@ -1,0 +1,342 @@
+// Leaf-major block-sparse attention on MFMA ("Block Sparse Attention with
+// Log-Linear Complexity", hyper.ai page, section "block-sparse attention",
+// the o_t equation: softmax over the raw keys of the kept blocks, applied to
+// their raw values).
+//
+// The kept (query, leaf) pairs are grouped by leaf (the same histogram / scan
+// / scatter as the selector's clusters).  One workgroup holds a leaf's C keys
+// (row-major) and values (transposed) in LDS and streams the queries that
+// kept it, 16 MFMA columns = 16 / G_Q queries x G_Q heads at a time:
+//   S^T = K Q^T        (C x 16, v_mfma_f32_16x16x32_bf16, fp32 accumulate)
+//   P^T = exp(S^T - m) per column (the accumulator layout already is the
+//                      B-operand layout of the next product: no LDS trip)
+//   O^T = V^T P^T      (d x 16)
+// and writes a partial (m, l, O) per (query, slot, head).  A merge pass per
+// (query, KV head) combines the K partials into o and lse.  Partial O is
+// stored in the input dtype (bf16 rounding is far inside the bf16 tolerance).
+// Work is done in chunks of KV heads so the partial buffers stay bounded and
+// one chunk's queries stay cache-resident.
+#include "kernels.h"
+
+namespace pisa {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
+constexpr size_t kAttnBudget = (size_t)8 << 30;  // partial buffers per head chunk
+
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct AttnLayout {
+  int64_t heads;  // (b, h) heads per chunk
+  int64_t M1, ncl, slots;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_m, off_l, off_o, total;
+};
+
+static AttnLayout attn_layout(const Problem& p) {
+  AttnLayout L{};
+  const size_t osz = p.dtype == 1 ? 2 : 4;
+  L.M1 = level_rows(p.N, p.C, 1);
+  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * (8 + p.D * osz)) + (size_t)L.M1 * 16;
+  const int64_t BH = (int64_t)p.B * p.Hkv;
+  int64_t hmax = (int64_t)(kAttnBudget / per_head);
+  if (hmax < 1) hmax = 1;
+  if (hmax > BH) hmax = BH;
+  const int64_t nchunks = (BH + hmax - 1) / hmax;
+  L.heads = (BH + nchunks - 1) / nchunks;
+  L.ncl = L.heads * L.M1;
+  L.slots = L.heads * (int64_t)p.N * p.K;
+  size_t off = 0;
+  L.off_counts = off;
+  off = a256(off + 4 * (size_t)L.ncl);
+  L.off_cursor = off;
+  off = a256(off + 4 * (size_t)L.ncl);
+  L.off_offsets = off;
+  off = a256(off + 4 * (size_t)(L.ncl + 1));
+  L.off_chunks = off;
+  off = a256(off + 4 * (size_t)(L.ncl + 1));
+  L.off_pairs = off;
+  off = a256(off + 4 * (size_t)L.slots);
+  L.off_m = off;
+  off = a256(off + 4 * (size_t)L.slots * p.G);
+  L.off_l = off;
+  off = a256(off + 4 * (size_t)L.slots * p.G);
+  L.off_o = off;
+  off = a256(off + osz * (size_t)L.slots * p.G * p.D);
+  L.total = off;
+  return L;
+}
+
+size_t attn_leaf_workspace_bytes(const Problem& p) { return attn_layout(p).total; }
+
+struct AttnLeafArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* offsets;
+  const int32_t* chunk_off;
+  const int32_t* pairs;
+  float* pm;   // [heads][N][K][G]
+  float* pl;
+  void* po;    // [heads][N][K][G][D] (input dtype)
+  int64_t ncl, M1, head0;
+  int32_t N, Hq, Hkv, C, K;
+  int32_t causal;
+  int64_t cap;
+  float scale;
+};
+
+// NKB: 16-key blocks covering the leaf (even, C <= 16 NKB).
+template <typename T, int D, int G, int NKB>
+__global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafArgs a) {
+  constexpr int NS = D / 32;                   // contraction steps of S
+  constexpr int TQ = 16 / G;                   // queries per 16-column tile
+  constexpr int CP = NKB * 16;                 // keys held (zero padded)
+  constexpr int KP = D + 16 / (int)sizeof(T);  // K row pitch
+  constexpr int VP = CP + 16 / (int)sizeof(T); // V^T row pitch
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
+  T* s_vt = s_k + CP * KP;                   // [D][VP]
+  __shared__ int32_t s_t[kAttnWaves][16];
+  __shared__ int32_t s_slot[kAttnWaves][16];
+
+  const int64_t chunk = blockIdx.x;
+  if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
+  int64_t lo = 0, hi = a.ncl;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a.chunk_off[mid] <= chunk) lo = mid;
+    else hi = mid;
+  }
+  const int64_t c = lo;
+  const int64_t hl = c / a.M1;  // head within the chunk
+  const int64_t j = c % a.M1;   // leaf
+  const int64_t bh = a.head0 + hl;
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kAttnChunk;
+  const int64_t p_end_c = a.offsets[c + 1];
+  const int64_t p_end = p_begin + kAttnChunk < p_end_c ? p_begin + kAttnChunk : p_end_c;
+
+  const int C = a.C;
+  const int64_t key0 = j * (int64_t)C;
+  const int nkeys = (int)((a.N - key0) < C ? (a.N - key0) : C);
+  const T* kh = static_cast<const T*>(a.k) + bh * a.cap * D;
+  const T* vh = static_cast<const T*>(a.v) + bh * a.cap * D;
+  constexpr int EPV = 16 / sizeof(T);
+  for (int i = threadIdx.x; i < CP * (D / EPV); i += blockDim.x) {
+    const int r = i / (D / EPV), d = (i % (D / EPV)) * EPV;
+    uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (r < nkeys) {
+      kv = *reinterpret_cast<const uint4*>(kh + (key0 + r) * D + d);
+      vv = *reinterpret_cast<const uint4*>(vh + (key0 + r) * D + d);
+    }
+    *reinterpret_cast<uint4*>(s_k + r * KP + d) = kv;
+    const T* ve = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s_vt[(d + e) * VP + r] = ve[e];
+  }
+  __syncthreads();
+
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+  const int qi = col / G, hh = col % G;
+  const T* qb = static_cast<const T*>(a.q);
+  for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += (int64_t)kAttnWaves * TQ) {
+    const int nq = (int)((p_end - tile) < TQ ? (p_end - tile) : TQ);
+    if (lane < TQ) {
+      const int32_t pr = (lane < nq) ? a.pairs[tile + lane] : -1;
+      s_t[w][lane] = pr >= 0 ? pr / a.K : -1;
+      s_slot[w][lane] = pr >= 0 ? pr % a.K : -1;
+    }
+    wave_sync();
+    const bool live = qi < nq;
+    const int64_t t = live ? s_t[w][qi] : -1;
+    // B operand of S^T = K Q^T: this lane's query-head column
+    Frag<T> fq[NS];
+    if (live) {
+      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fq[s].load(qrow + g * (D / 4) + 8 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fq[s].zero();
+    }
+    floatx4 acc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        Frag<T> fk;
+        fk.load(s_k + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+        acc[kb] = mma(fk, fq[s], acc[kb]);
+      }
+    }
+    // column softmax statistics (keys are rows 4g+i of each 16-key block)
+    const int64_t lim = live ? (a.causal ? (t - key0 + 1 < nkeys ? t - key0 + 1 : nkeys) : nkeys) : 0;
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb * 16 + 4 * g + i;
+        const float x = key < lim ? acc[kb][i] * a.scale : -INFINITY;
+        acc[kb][i] = x;
+        m = fmaxf(m, x);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float l = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = (acc[kb][i] == -INFINITY) ? 0.f : __expf(acc[kb][i] - m);
+        acc[kb][i] = pv;
+        l += pv;
+      }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    // O^T = V^T P^T, contraction over 32 keys = 16-key blocks (2s, 2s+1)
+    floatx4 oacc[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < NKB / 2; ++sp) {
+      const float pk[8] = {acc[2 * sp][0],     acc[2 * sp][1],     acc[2 * sp][2],     acc[2 * sp][3],
+                           acc[2 * sp + 1][0], acc[2 * sp + 1][1], acc[2 * sp + 1][2], acc[2 * sp + 1][3]};
+      Frag<T> fp;
+      fp.set(pk);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        Frag<T> fv;
+        const T* row = s_vt + (db * 16 + col) * VP;
+        fv.load4x2(row + (2 * sp) * 16 + 4 * g, row + (2 * sp + 1) * 16 + 4 * g);
+        oacc[db] = mma(fv, fp, oacc[db]);
+      }
+    }
+    // partial record of (query, slot, head): rows 4g+i of d-block db
+    if (live) {
+      const int64_t rec = ((hl * a.N + t) * a.K + s_slot[w][qi]) * G + hh;
+      T* po = static_cast<T*>(a.po) + rec * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store1<T>(po + db * 16 + 4 * g + i, oacc[db][i]);
+      if (g == 0) {
+        a.pm[rec] = m;
+        a.pl[rec] = l;
+      }
+    }
+    wave_sync();
+  }
+}
+
+// ---- merge the K partials of every (query, KV head) ---------------------------
+struct MergeArgs {
+  const int32_t* idx;
+  const float* pm;
+  const float* pl;
+  const void* po;
+  void* o;
+  float* lse;
+  int64_t head0, heads, M1;
+  int32_t N, Hq, Hkv, K;
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (wid >= a.heads * a.N) return;
+  const int lane = lane_id();
+  const int64_t hl = wid / a.N, t = wid % a.N;
+  const int64_t bh = a.head0 + hl;
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  const int32_t* sel = a.idx + (bh * a.N + t) * a.K;
+  const T* po = static_cast<const T*>(a.po);
+  for (int e0 = lane * 8; e0 < G * D; e0 += kWave * 8) {
+    const int hh = e0 / D, d = e0 % D;
+    float M = -INFINITY;
+    for (int s = 0; s < a.K; ++s)
+      if (sel[s] >= 0 && sel[s] < a.M1) M = fmaxf(M, a.pm[((hl * a.N + t) * a.K + s) * G + hh]);
+    float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int s = 0; s < a.K; ++s) {
+        if (sel[s] < 0 || sel[s] >= a.M1) continue;
+        const int64_t rec = ((hl * a.N + t) * a.K + s) * G + hh;
+        const float ms = a.pm[rec];
+        if (ms == -INFINITY) continue;
+        const float wgt = __expf(ms - M);
+        L += wgt * a.pl[rec];
+        float v[8];
+        load8<T>(po + rec * D + d, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    T* out = static_cast<T*>(a.o) + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D + d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store1<T>(out + i, acc[i] * inv);
+    if (a.lse != nullptr && d == 0)
+      a.lse[((int64_t)b * a.Hq + h * G + hh) * a.N + t] = L > 0.f ? M + __logf(L) : -INFINITY;
+  }
+}
+
+hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
+                            void* o, float* lse, void* ws, hipStream_t stream) {
+  const AttnLayout L = attn_layout(p);
+  char* base = static_cast<char*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
+  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
+  int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
+  float* pm = reinterpret_cast<float*>(base + L.off_m);
+  float* pl = reinterpret_cast<float*>(base + L.off_l);
+  void* po = base + L.off_o;
+  const int64_t BH = (int64_t)p.B * p.Hkv;
+  for (int64_t head0 = 0; head0 < BH; head0 += L.heads) {
+    const int64_t heads = (BH - head0) < L.heads ? (BH - head0) : L.heads;
+    const int64_t entries = heads * p.N * p.K;
+    const int64_t ncl = heads * L.M1;
+    hipError_t err = launch_clusters(idx + head0 * p.N * p.K, entries, p.N, p.K, L.M1, ncl, kAttnChunk, counts, cursor,
+                                     offsets, chunk_off, pairs, stream);
+    if (err != hipSuccess) return err;
+    AttnLeafArgs aa{q, k, v, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, head0, p.N, p.Hq, p.Hkv, p.C, p.K,
+                    p.causal ? 1 : 0, p.cap, p.scale};
+    MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
+    const int64_t max_chunks = (entries + kAttnChunk - 1) / kAttnChunk + ncl;
+    err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
+      using T = std::remove_pointer_t<decltype(tp)>;
+      constexpr int D = decltype(dc)::value;
+      constexpr int G = decltype(gc)::value;
+      auto run = [&](auto kern, int nkb) -> hipError_t {
+        const size_t lds = ((size_t)nkb * 16 * (D + 16 / sizeof(T)) + (size_t)D * (nkb * 16 + 16 / sizeof(T))) *
+                           sizeof(T);
+        if (lds > 65536) {
+          hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (e != hipSuccess) return e;
+        }
+        PISA_LAUNCH("attn_leaf", stream, kern, dim3((unsigned)max_chunks), dim3(kAttnWaves * kWave), lds, aa);
+        return hipGetLastError();
+      };
+      hipError_t e;
+      if (p.C <= 32)
+        e = run(attn_leaf_kernel<T, D, G, 2>, 2);
+      else if (p.C <= 64)
+        e = run(attn_leaf_kernel<T, D, G, 4>, 4);
+      else
+        e = run(attn_leaf_kernel<T, D, G, 8>, 8);
+      if (e != hipSuccess) return e;
+      const int64_t waves = heads * p.N;
+      PISA_LAUNCH("attn_merge", stream, (attn_merge_kernel<T, D, G>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                  ma);
+      return hipGetLastError();
+    });
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pisa

@@ -193,4 +193,57 @@ __device__ __forceinline__ floatx4 mma16x16x32(const bf16x8 a, const bf16x8 b, f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+// ---- MFMA operand fragments (8 contraction elements per lane) ---------------
+template <typename T>
+struct Frag;
+template <>
+struct Frag<uint16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  // elements 0..3 from p0, 4..7 from p1 (each 8-byte aligned)
+  __device__ __forceinline__ void load4x2(const uint16_t* p0, const uint16_t* p1) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p0);
+    const uint2 b = *reinterpret_cast<const uint2*>(p1);
+    const uint4 u = {a.x, a.y, b.x, b.y};
+    v = *reinterpret_cast<const bf16x8*>(&u);
+  }
+  // round eight fp32 values to bf16 (nearest even)
+  __device__ __forceinline__ void set(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+    const uint4 u = {w[0], w[1], w[2], w[3]};
+    v = *reinterpret_cast<const bf16x8*>(&u);
+  }
+  __device__ __forceinline__ void zero() {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    v = *reinterpret_cast<const bf16x8*>(&z);
+  }
+};
+template <>
+struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float* p) { load8<float>(p, v); }
+  __device__ __forceinline__ void load4x2(const float* p0, const float* p1) {
+    const float4 a = *reinterpret_cast<const float4*>(p0);
+    const float4 b = *reinterpret_cast<const float4*>(p1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void set(const float* x) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = x[i];
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+};
+__device__ __forceinline__ floatx4 mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, floatx4 acc) {
+  return mma16x16x32(a.v, b.v, acc);
+}
+__device__ __forceinline__ floatx4 mma(const Frag<float>& a, const Frag<float>& b, floatx4 acc) {
+  return mma16x16x32(a.v, b.v, acc);
+}
+
 }  // namespace pisa

@@ -75,6 +75,17 @@ size_t stage2_workspace_bytes(const Problem& p);
 hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const int32_t* blk2, int32_t* idx,
                          float* score, void* ws, hipStream_t stream);
 
+// select2.hip: (query, slot) entries keys[e] in [0, M) (or -1) -> CSR of
+// clusters per (head, key value) with chunk offsets for `chunk`-sized work units
+hipError_t launch_clusters(const int32_t* keys, int64_t entries, int32_t N, int32_t K, int64_t M, int64_t ncl,
+                           int32_t chunk, int32_t* counts, int32_t* cursor, int32_t* offsets, int32_t* chunk_off,
+                           int32_t* pairs, hipStream_t stream);
+
+// attn_leaf.hip: leaf-major MFMA attention with a merge pass
+size_t attn_leaf_workspace_bytes(const Problem& p);
+hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
+                            void* o, float* lse, void* ws, hipStream_t stream);
+
 // flat.hip
 hipError_t launch_flat(const Problem& p, const void* q, const float* pyr, int32_t* idx, float* score,
                        hipStream_t stream);

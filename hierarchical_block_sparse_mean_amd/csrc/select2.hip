@@ -68,13 +68,13 @@ __global__ void cluster_count_kernel(const int32_t* __restrict__ blk2, int64_t e
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int32_t j2 = blk2[e];
-    if (j2 >= 0) atomicAdd(&counts[(e / NK) * M2 + j2], 1);
+    if (j2 >= 0 && j2 < M2) atomicAdd(&counts[(e / NK) * M2 + j2], 1);
   }
 }
 
 // Single-workgroup exclusive scans: offsets of the pairs and of the chunks.
 __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __restrict__ counts, int64_t ncl,
-                                                            int32_t* offsets, int32_t* chunk_off) {
+                                                            int32_t chunk, int32_t* offsets, int32_t* chunk_off) {
   __shared__ int32_t s_a[1024], s_b[1024];
   __shared__ int32_t carry_a, carry_b;
   if (threadIdx.x == 0) {
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __res
     const int64_t i = base + threadIdx.x;
     const int32_t c = (i < ncl) ? counts[i] : 0;
     s_a[threadIdx.x] = c;
-    s_b[threadIdx.x] = (c + kS2Chunk - 1) / kS2Chunk;
+    s_b[threadIdx.x] = (c + chunk - 1) / chunk;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
       const int32_t va = (threadIdx.x >= (unsigned)o) ? s_a[threadIdx.x - o] : 0;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __res
     }
     if (i < ncl) {
       offsets[i] = carry_a + s_a[threadIdx.x] - c;
-      chunk_off[i] = carry_b + s_b[threadIdx.x] - (c + kS2Chunk - 1) / kS2Chunk;
+      chunk_off[i] = carry_b + s_b[threadIdx.x] - (c + chunk - 1) / chunk;
     }
     __syncthreads();
     if (threadIdx.x == 1023) {
@@ -120,39 +120,27 @@ __global__ void cluster_fill_kernel(const int32_t* __restrict__ blk2, int64_t en
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int32_t j2 = blk2[e];
-    if (j2 < 0) continue;
+    if (j2 < 0 || j2 >= M2) continue;
     const int64_t c = (e / NK) * M2 + j2;
     const int32_t pos = atomicAdd(&cursor[c], 1);
     pairs[offsets[c] + pos] = (int32_t)(e % NK);  // t * K + slot
   }
 }
 
-// ---- MFMA fragments ---------------------------------------------------------
-template <typename T>
-struct Frag;
-template <>
-struct Frag<uint16_t> {
-  bf16x8 v;
-  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
-  __device__ __forceinline__ void zero() {
-    const uint4 z = {0u, 0u, 0u, 0u};
-    v = *reinterpret_cast<const bf16x8*>(&z);
-  }
-};
-template <>
-struct Frag<float> {
-  float v[8];
-  __device__ __forceinline__ void load(const float* p) { load8<float>(p, v); }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  }
-};
-__device__ __forceinline__ floatx4 mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, floatx4 acc) {
-  return mma16x16x32(a.v, b.v, acc);
-}
-__device__ __forceinline__ floatx4 mma(const Frag<float>& a, const Frag<float>& b, floatx4 acc) {
-  return mma16x16x32(a.v, b.v, acc);
+hipError_t launch_clusters(const int32_t* keys, int64_t entries, int32_t N, int32_t K, int64_t M, int64_t ncl,
+                           int32_t chunk, int32_t* counts, int32_t* cursor, int32_t* offsets, int32_t* chunk_off,
+                           int32_t* pairs, hipStream_t stream) {
+  const unsigned ew_blocks = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
+  const unsigned cl_blocks = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
+  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, counts, ncl, 0);
+  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, cursor, ncl, 0);
+  PISA_LAUNCH("cluster_count", stream, cluster_count_kernel, dim3(ew_blocks), dim3(256), 0, keys, entries, N * K, M,
+              counts);
+  PISA_LAUNCH("cluster_scan", stream, cluster_scan_kernel, dim3(1), dim3(1024), 0, counts, ncl, chunk, offsets,
+              chunk_off);
+  PISA_LAUNCH("cluster_fill", stream, cluster_fill_kernel, dim3(ew_blocks), dim3(256), 0, keys, entries, N, K, M,
+              offsets, cursor, pairs);
+  return hipGetLastError();
 }
 
 struct S2Args {
@@ -369,18 +357,8 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   float* scores = reinterpret_cast<float*>(base + L.off_scores);
   const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
   const int64_t entries = (int64_t)p.B * p.Hkv * p.N * p.K;
-  const unsigned ew_blocks = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
-  const unsigned cl_blocks = (unsigned)((L.ncl + 255) / 256 < 65536 ? (L.ncl + 255) / 256 : 65536);
-
-  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, counts, L.ncl, 0);
-  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, cursor, L.ncl, 0);
-  PISA_LAUNCH("cluster_count", stream, cluster_count_kernel, dim3(ew_blocks), dim3(256), 0, blk2, entries,
-              p.N * p.K, M2, counts);
-  PISA_LAUNCH("cluster_scan", stream, cluster_scan_kernel, dim3(1), dim3(1024), 0, counts, L.ncl, offsets,
-              chunk_off);
-  PISA_LAUNCH("cluster_fill", stream, cluster_fill_kernel, dim3(ew_blocks), dim3(256), 0, blk2, entries, p.N, p.K,
-              M2, offsets, cursor, pairs);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_clusters(blk2, entries, p.N, p.K, M2, L.ncl, kS2Chunk, counts, cursor, offsets, chunk_off,
+                                   pairs, stream);
   if (err != hipSuccess) return err;
 
   S2Args a{q, k, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, p.B, p.N, p.Hq, p.Hkv, p.C, p.K,

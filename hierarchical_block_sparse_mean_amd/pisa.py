@@ -24,6 +24,7 @@ _lib = None
 PISA_OK, PISA_ERR_INVALID_ARG, PISA_ERR_UNSUPPORTED, PISA_ERR_WORKSPACE, PISA_ERR_HIP = range(5)
 PISA_F32, PISA_BF16 = 0, 1
 SELECT_AUTO, SELECT_TWO_STAGE, SELECT_FUSED = 0, 1, 2
+ATTN_AUTO, ATTN_LEAF_MAJOR, ATTN_QUERY_MAJOR = 0, 1, 2
 STATUS_NAMES = {0: "PISA_OK", 1: "PISA_ERR_INVALID_ARG", 2: "PISA_ERR_UNSUPPORTED", 3: "PISA_ERR_WORKSPACE",
                 4: "PISA_ERR_HIP"}
 
@@ -47,6 +48,7 @@ class CProblem(ctypes.Structure):
         ("D", ctypes.c_int32), ("C", ctypes.c_int32), ("g", ctypes.c_int32), ("K", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q_tile", ctypes.c_int32), ("cap", ctypes.c_int32), ("select_algo", ctypes.c_int32),
+        ("attn_algo", ctypes.c_int32),
     ]
 
 
@@ -117,11 +119,12 @@ class Problem:
     q_tile: int = 0
     cap: int = 0
     select_algo: int = SELECT_AUTO
+    attn_algo: int = ATTN_AUTO
 
     def c(self) -> CProblem:
         return CProblem(self.B, self.N, self.Hq, self.Hkv, self.D, self.C, self.g, self.K, int(self.causal),
                         PISA_BF16 if self.dtype == "bf16" else PISA_F32, self.scale, self.q_tile, self.cap,
-                        self.select_algo)
+                        self.select_algo, self.attn_algo)
 
     @property
     def torch_dtype(self):

@@ -67,6 +67,15 @@ typedef enum {
                                 decode design)                               */
 } pisa_select_algo;
 
+/* Attention schedule; both return the same result (up to fp32 rounding). */
+typedef enum {
+  PISA_ATTN_AUTO = 0,        /* leaf-major                                    */
+  PISA_ATTN_LEAF_MAJOR = 1,  /* kept (query, leaf) pairs grouped by leaf; one
+                                workgroup streams a leaf's queries through
+                                MFMA and a merge pass combines the partials  */
+  PISA_ATTN_QUERY_MAJOR = 2  /* one wave per (query, KV head); no workspace   */
+} pisa_attn_algo;
+
 typedef struct {
   int32_t B, N, Hq, Hkv, D; /* batch, tokens, query heads, KV heads, head dim */
   int32_t C;                /* leaf block size (the first merge factor, [PYR]) */
@@ -80,6 +89,7 @@ typedef struct {
   int32_t cap;              /* token capacity of k/v rows and of the pyramid;
                                0 => N.  Must be >= N.                           */
   int32_t select_algo;      /* pisa_select_algo                                 */
+  int32_t attn_algo;        /* pisa_attn_algo                                   */
 } pisa_problem;
 
 /* ---- key pyramid [PYR] ------------------------------------------------- *
@@ -118,8 +128,8 @@ pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, con
 
 /* ---- block-sparse attention [BSA] --------------------------------------- *
  * o[b][h'][t] = sum_i softmax_i(q . k_i * scale) v_i over the keys i of the
- * leaves idx[b][h'/G_Q][t][*] (entries < 0 ignored; keys i > t masked when
- * causal).  o has the input dtype; lse (may be NULL) is float [B][Hq][N], the
+ * leaves idx[b][h'/G_Q][t][*] (entries < 0 or >= ceil(N/C) ignored; keys
+ * i > t masked when causal).  o has the input dtype; lse (may be NULL) is float [B][Hq][N], the
  * log-sum-exp of the attended logits.  A query with no attended key gets
  * o = 0 and lse = -inf.  ws: at least pisa_attn_workspace_bytes(p) bytes.   */
 size_t pisa_attn_workspace_bytes(const pisa_problem* p);

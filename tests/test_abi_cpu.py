@@ -72,6 +72,7 @@ FAKE = 4096  # a non-NULL address; validation must reject before using it
     (dict(cap=100), pisa.PISA_ERR_INVALID_ARG),
     (dict(q_tile=3), pisa.PISA_ERR_UNSUPPORTED),
     (dict(select_algo=7), pisa.PISA_ERR_INVALID_ARG),
+    (dict(attn_algo=-1), pisa.PISA_ERR_INVALID_ARG),
     (dict(scale=-1.0), pisa.PISA_ERR_INVALID_ARG),
 ])
 def test_invalid_problem_rejected(lib, kw, status):
@@ -93,6 +94,10 @@ def test_null_pointers_and_small_workspace(lib):
     assert "workspace" in lib.pisa_last_error().decode()
     assert lib.pisa_sparse_attn(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 256, None) == \
         pisa.PISA_ERR_INVALID_ARG
+    need_a = lib.pisa_attn_workspace_bytes(ctypes.byref(p))
+    assert need_a > 256
+    assert lib.pisa_sparse_attn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need_a - 1, None) == \
+        pisa.PISA_ERR_WORKSPACE
     assert lib.pisa_flat_select(ctypes.byref(p), None, FAKE, FAKE, None, FAKE, 256, None) == pisa.PISA_ERR_INVALID_ARG
     assert lib.pisa_build_pyramid(None, FAKE, FAKE, None) == pisa.PISA_ERR_INVALID_ARG
 

@@ -103,12 +103,14 @@ def test_select(name, algo):
     log(f"  exempt fraction {ex:.4f}, exact-match rate {rate:.4f}")
 
 
+@pytest.mark.parametrize("algo", [pisa.ATTN_LEAF_MAJOR, pisa.ATTN_QUERY_MAJOR], ids=["leaf_major", "query_major"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_attention(name):
+def test_attention(name, algo):
     c = case_data(name)
     w = c["w"]
-    log(f"[test_attention {name}]")
+    log(f"[test_attention {name} algo={algo}]")
     p = _problem(w)
+    p.attn_algo = algo
     # feed the oracle's selection, so attention parity does not depend on ties
     ts = c["ts"]
     full_idx = np.full((w.B, w.Hkv, w.N, w.K), -1, np.int32)
