@@ -29,7 +29,7 @@ static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct AttnLayout {
   int64_t heads;  // (b, h) heads per chunk
   int64_t M1, ncl, slots;
-  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_m, off_l, off_o, total;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_m, off_l, off_o, off_hist, total;
 };
 
 static AttnLayout attn_layout(const Problem& p) {
@@ -62,6 +62,8 @@ static AttnLayout attn_layout(const Problem& p) {
   off = a256(off + 4 * (size_t)L.slots * p.G);
   L.off_o = off;
   off = a256(off + osz * (size_t)L.slots * p.G * p.D);
+  L.off_hist = off;
+  off = a256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.M1));
   L.total = off;
   return L;
 }
@@ -72,6 +74,7 @@ struct AttnLeafArgs {
   const void* q;
   const void* k;
   const void* v;
+  const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
   const int32_t* pairs;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kAttnChunk;
-  const int64_t p_end_c = a.offsets[c + 1];
+  const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
   const int64_t p_end = p_begin + kAttnChunk < p_end_c ? p_begin + kAttnChunk : p_end_c;
 
   const int C = a.C;
@@ -299,10 +302,10 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     const int64_t heads = (BH - head0) < L.heads ? (BH - head0) : L.heads;
     const int64_t entries = heads * p.N * p.K;
     const int64_t ncl = heads * L.M1;
-    hipError_t err = launch_clusters(idx + head0 * p.N * p.K, entries, p.N, p.K, L.M1, ncl, kAttnChunk, counts, cursor,
-                                     offsets, chunk_off, pairs, stream);
+    const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
+    hipError_t err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, L.M1, kAttnChunk, cb, stream);
     if (err != hipSuccess) return err;
-    AttnLeafArgs aa{q, k, v, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, head0, p.N, p.Hq, p.Hkv, p.C, p.K,
+    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, head0, p.N, p.Hq, p.Hkv, p.C, p.K,
                     p.causal ? 1 : 0, p.cap, p.scale};
     MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
     const int64_t max_chunks = (entries + kAttnChunk - 1) / kAttnChunk + ncl;

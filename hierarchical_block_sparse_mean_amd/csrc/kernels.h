@@ -75,11 +75,21 @@ size_t stage2_workspace_bytes(const Problem& p);
 hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const int32_t* blk2, int32_t* idx,
                          float* score, void* ws, hipStream_t stream);
 
-// select2.hip: (query, slot) entries keys[e] in [0, M) (or -1) -> CSR of
-// clusters per (head, key value) with chunk offsets for `chunk`-sized work units
-hipError_t launch_clusters(const int32_t* keys, int64_t entries, int32_t N, int32_t K, int64_t M, int64_t ncl,
-                           int32_t chunk, int32_t* counts, int32_t* cursor, int32_t* offsets, int32_t* chunk_off,
-                           int32_t* pairs, hipStream_t stream);
+// cluster.hip: entries keys[head * NK + e] in [0, M) (or -1) -> per cluster
+// c = head * M + j: counts[c], offsets[c] (first pair; pairs hold e = t*K +
+// slot), chunk_off[c] (first work chunk of `chunk` pairs; chunk_off[ncl] is
+// the total).  cursor: ncl int32; hist: cluster_scratch_bytes() bytes.
+struct ClusterBufs {
+  int32_t* counts;
+  int32_t* cursor;
+  int32_t* offsets;
+  int32_t* chunk_off;
+  int32_t* pairs;
+  int32_t* hist;
+};
+size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t M);
+hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int64_t M, int32_t chunk,
+                           const ClusterBufs& b, hipStream_t stream);
 
 // attn_leaf.hip: leaf-major MFMA attention with a merge pass
 size_t attn_leaf_workspace_bytes(const Problem& p);

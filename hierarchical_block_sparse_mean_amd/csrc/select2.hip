@@ -28,7 +28,7 @@ constexpr int kTopkWaves = 4;
 struct S2Layout {
   int64_t ncl;      // clusters = B * Hkv * M2
   int64_t max_pairs;
-  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_scores, total;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_scores, off_hist, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -51,101 +51,18 @@ static S2Layout s2_layout(const Problem& p) {
   off = align256(off + sizeof(int32_t) * s.max_pairs);
   s.off_scores = off;
   off = align256(off + sizeof(float) * 2 * s.max_pairs);
+  s.off_hist = off;
+  off = align256(off + cluster_scratch_bytes((int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, M2));
   s.total = off;
   return s;
 }
 
 size_t stage2_workspace_bytes(const Problem& p) { return s2_layout(p).total; }
 
-// ---- cluster construction: histogram, scan, scatter --------------------------
-__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
-__global__ void cluster_count_kernel(const int32_t* __restrict__ blk2, int64_t entries, int32_t NK, int64_t M2,
-                                     int32_t* counts) {
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t j2 = blk2[e];
-    if (j2 >= 0 && j2 < M2) atomicAdd(&counts[(e / NK) * M2 + j2], 1);
-  }
-}
-
-// Single-workgroup exclusive scans: offsets of the pairs and of the chunks.
-__global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __restrict__ counts, int64_t ncl,
-                                                            int32_t chunk, int32_t* offsets, int32_t* chunk_off) {
-  __shared__ int32_t s_a[1024], s_b[1024];
-  __shared__ int32_t carry_a, carry_b;
-  if (threadIdx.x == 0) {
-    carry_a = 0;
-    carry_b = 0;
-  }
-  __syncthreads();
-  for (int64_t base = 0; base < ncl; base += 1024) {
-    const int64_t i = base + threadIdx.x;
-    const int32_t c = (i < ncl) ? counts[i] : 0;
-    s_a[threadIdx.x] = c;
-    s_b[threadIdx.x] = (c + chunk - 1) / chunk;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      const int32_t va = (threadIdx.x >= (unsigned)o) ? s_a[threadIdx.x - o] : 0;
-      const int32_t vb = (threadIdx.x >= (unsigned)o) ? s_b[threadIdx.x - o] : 0;
-      __syncthreads();
-      s_a[threadIdx.x] += va;
-      s_b[threadIdx.x] += vb;
-      __syncthreads();
-    }
-    if (i < ncl) {
-      offsets[i] = carry_a + s_a[threadIdx.x] - c;
-      chunk_off[i] = carry_b + s_b[threadIdx.x] - (c + chunk - 1) / chunk;
-    }
-    __syncthreads();
-    if (threadIdx.x == 1023) {
-      carry_a += s_a[1023];
-      carry_b += s_b[1023];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    offsets[ncl] = carry_a;
-    chunk_off[ncl] = carry_b;
-  }
-}
-
-__global__ void cluster_fill_kernel(const int32_t* __restrict__ blk2, int64_t entries, int32_t N, int32_t K,
-                                    int64_t M2, const int32_t* __restrict__ offsets, int32_t* cursor,
-                                    int32_t* pairs) {
-  const int64_t NK = (int64_t)N * K;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t j2 = blk2[e];
-    if (j2 < 0 || j2 >= M2) continue;
-    const int64_t c = (e / NK) * M2 + j2;
-    const int32_t pos = atomicAdd(&cursor[c], 1);
-    pairs[offsets[c] + pos] = (int32_t)(e % NK);  // t * K + slot
-  }
-}
-
-hipError_t launch_clusters(const int32_t* keys, int64_t entries, int32_t N, int32_t K, int64_t M, int64_t ncl,
-                           int32_t chunk, int32_t* counts, int32_t* cursor, int32_t* offsets, int32_t* chunk_off,
-                           int32_t* pairs, hipStream_t stream) {
-  const unsigned ew_blocks = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
-  const unsigned cl_blocks = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
-  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, counts, ncl, 0);
-  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cl_blocks), dim3(256), 0, cursor, ncl, 0);
-  PISA_LAUNCH("cluster_count", stream, cluster_count_kernel, dim3(ew_blocks), dim3(256), 0, keys, entries, N * K, M,
-              counts);
-  PISA_LAUNCH("cluster_scan", stream, cluster_scan_kernel, dim3(1), dim3(1024), 0, counts, ncl, chunk, offsets,
-              chunk_off);
-  PISA_LAUNCH("cluster_fill", stream, cluster_fill_kernel, dim3(ew_blocks), dim3(256), 0, keys, entries, N, K, M,
-              offsets, cursor, pairs);
-  return hipGetLastError();
-}
-
 struct S2Args {
   const void* q;
   const void* k;
+  const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
   const int32_t* pairs;
@@ -182,7 +99,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
   const int64_t j2 = c % a.M2;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kS2Chunk;
-  const int64_t p_end_c = a.offsets[c + 1];
+  const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
   const int64_t p_end = p_begin + kS2Chunk < p_end_c ? p_begin + kS2Chunk : p_end_c;
 
   // key tile: leaves 2*j2 and 2*j2+1 (2C rows, zero rows past the sequence)
@@ -357,11 +274,10 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   float* scores = reinterpret_cast<float*>(base + L.off_scores);
   const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
   const int64_t entries = (int64_t)p.B * p.Hkv * p.N * p.K;
-  hipError_t err = launch_clusters(blk2, entries, p.N, p.K, M2, L.ncl, kS2Chunk, counts, cursor, offsets, chunk_off,
-                                   pairs, stream);
+  const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
+  hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, M2, kS2Chunk, cb, stream);
   if (err != hipSuccess) return err;
-
-  S2Args a{q, k, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, p.B, p.N, p.Hq, p.Hkv, p.C, p.K,
+  S2Args a{q, k, counts, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, p.B, p.N, p.Hq, p.Hkv, p.C, p.K,
            p.causal ? 1 : 0, p.cap, p.scale};
   const int64_t max_chunks = (entries + kS2Chunk - 1) / kS2Chunk + L.ncl;
   err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
