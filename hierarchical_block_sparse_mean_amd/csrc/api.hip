@@ -203,7 +203,8 @@ int64_t pisa_level_offset(int64_t cap, int32_t C, int32_t l) {
 size_t pisa_pyramid_bytes(const pisa_problem* p) {
   pisa::Problem q;
   if (validate(p, &q) != PISA_OK) return 0;
-  return sizeof(float) * (size_t)q.B * q.Hkv * q.geo.rows * q.D;
+  // fp32 rows, their fp16 block-floating-point copy, one int32 exponent per row
+  return (size_t)q.B * q.Hkv * q.geo.rows * (q.D * (sizeof(float) + 2) + sizeof(int32_t));
 }
 
 pisa_status pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyr, hipStream_t stream) {

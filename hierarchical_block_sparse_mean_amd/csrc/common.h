@@ -23,6 +23,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+// Power-of-two exponent e of a row whose largest magnitude is mx, such that
+// mx * 2^-e lies in [2^14, 2^15): the row scaled by 2^-e fits fp16 with full
+// relative precision (block floating point; scaling by 2^-e is exact).
+__device__ __forceinline__ int row_exponent(float mx) {
+  if (!(mx > 0.f)) return 0;
+  int e;
+  frexpf(mx, &e);  // mx = m * 2^e, m in [0.5, 1)
+  return e - 15;
+}
+__device__ __forceinline__ _Float16 to_f16_scaled(float x, int e) { return (_Float16)ldexpf(x, -e); }
+
 // ---- element access: T is float (fp32) or uint16_t (bf16 bits) ----------
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* out);
@@ -191,6 +204,9 @@ __device__ __forceinline__ floatx4 mma16x16x32(const float* a8, const float* b8,
 }
 __device__ __forceinline__ floatx4 mma16x16x32(const bf16x8 a, const bf16x8 b, floatx4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma16x16x32(const halfx8 a, const halfx8 b, floatx4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
 
 // ---- MFMA operand fragments (8 contraction elements per lane) ---------------

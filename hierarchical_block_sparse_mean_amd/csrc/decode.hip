@@ -19,6 +19,8 @@ struct DecodeKArgs {
   void* k_cache;
   void* v_cache;
   float* pyr;
+  _Float16* f16;  // block-floating-point copy of the summaries
+  int32_t* ex;    // its per-row exponents
   const int32_t* len;
   const void* q_new;
   const void* k_new;
@@ -55,6 +57,21 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeKArgs a) {
   const T* knew = static_cast<const T*>(a.k_new) + sh * D;
   const T* vnew = static_cast<const T*>(a.v_new) + sh * D;
   float* pbase = a.pyr + sh * a.geo.rows * D;
+  _Float16* hbase = a.f16 + sh * a.geo.rows * D;
+  int32_t* xbase = a.ex + sh * a.geo.rows;
+  // writes summary row `row` (this lane's DPL dims in v) and its fp16 copy
+  auto put_row = [&](int64_t row, const float* v) {
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      pbase[row * D + lane * DPL + e] = v[e];
+      mx = fmaxf(mx, fabsf(v[e]));
+    }
+    const int ex = row_exponent(wave_max(mx));
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) hbase[row * D + lane * DPL + e] = to_f16_scaled(v[e], ex);
+    if (lane == 0) xbase[row] = ex;
+  };
 
   // 1. append k, v at row n
   for (int d = lane; d < D; d += kWave) {
@@ -79,10 +96,8 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeKArgs a) {
     float v[DPL];
     load_dims<T, DPL>(knew + lane * DPL, v);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      cur[e] = (acc[e] + v[e]) / cnt;
-      pbase[(a.geo.level_off[1] + j) * D + lane * DPL + e] = cur[e];
-    }
+    for (int e = 0; e < DPL; ++e) cur[e] = (acc[e] + v[e]) / cnt;
+    put_row(a.geo.level_off[1] + j, cur);
   }
   // 3. ancestors: node j >> (l-1) of level l is the mean of its existing children
   const int32_t L1 = num_levels(n1, a.C);
@@ -99,8 +114,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeKArgs a) {
       }
     }
     node >>= 1;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) pbase[(a.geo.level_off[l] + node) * D + lane * DPL + e] = cur[e];
+    put_row(a.geo.level_off[l] + node, cur);
   }
   __threadfence();  // the path rows are read back below by this wave
 
@@ -131,7 +145,9 @@ __global__ void decode_bump_kernel(int32_t* len, int32_t S, int64_t cap) {
 hipError_t launch_decode(const DecodeArgs& d, void* k_cache, void* v_cache, float* pyr, int32_t* len,
                          const void* q_new, const void* k_new, const void* v_new, void* o, int32_t* idx,
                          float* score, int32_t* err, hipStream_t stream) {
-  DecodeKArgs a{k_cache, v_cache, pyr, len, q_new, k_new, v_new, o, idx, score, err,
+  const int64_t plane = (int64_t)d.S * d.Hkv * d.geo.rows * d.D;
+  _Float16* f16 = reinterpret_cast<_Float16*>(pyr + plane);
+  DecodeKArgs a{k_cache, v_cache, pyr, f16, reinterpret_cast<int32_t*>(f16 + plane), len, q_new, k_new, v_new, o, idx, score, err,
                 d.S, d.Hq, d.Hkv, d.C, d.K, d.cap, d.scale, d.geo};
   hipError_t e = dispatch_tdg(d.dtype, d.D, d.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
     using T = std::remove_pointer_t<decltype(tp)>;

@@ -20,6 +20,8 @@ constexpr int kUpLevels = 6;
 struct PyrArgs {
   const void* k;
   float* pyr;
+  _Float16* f16;  // block-floating-point copy: row * 2^-ex[row] in fp16
+  int32_t* ex;    // per-row exponent (row index = element index / D)
   int64_t n;    // tokens
   int64_t cap;  // k row stride in tokens
   int32_t BH, C, L;
@@ -28,9 +30,23 @@ struct PyrArgs {
 
 // Builds levels lo+1 .. hi of the chunk from level lo held in buf (cnt0 rows,
 // first global index first0) and writes them to global memory.
+// fp16 block-floating-point copy of LDS rows [0, cnt) (global rows row0..),
+// one wave per row.
+template <int D>
+__device__ __forceinline__ void put_f16_rows(const PyrArgs& a, const float* rows, int cnt, int64_t row0) {
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave, lane = lane_id();
+  for (int p = w; p < cnt; p += nw) {
+    float mx = 0.f;
+    for (int d = lane; d < D; d += kWave) mx = fmaxf(mx, fabsf(rows[p * D + d]));
+    const int e = row_exponent(wave_max(mx));
+    for (int d = lane; d < D; d += kWave) a.f16[(row0 + p) * D + d] = to_f16_scaled(rows[p * D + d], e);
+    if (lane == 0) a.ex[row0 + p] = e;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void build_levels_in_lds(float* buf0, float* buf1, int cnt0, int64_t first0,
-                                                    int32_t lo, int32_t hi, const PyrArgs& a, float* head) {
+                                                    int32_t lo, int32_t hi, const PyrArgs& a, int64_t head) {
   float* cur = buf0;
   float* nxt = buf1;
   int cnt = cnt0;
@@ -40,16 +56,18 @@ __device__ __forceinline__ void build_levels_in_lds(float* buf0, float* buf1, in
     const int64_t m_par = level_rows(a.n, a.C, l);
     const int pcnt = (cnt + 1) / 2;
     const int64_t pfirst = first / 2;
-    float* dst = head + (a.geo.level_off[l] + pfirst) * D;
+    const int64_t dst = head + (a.geo.level_off[l] + pfirst) * D;
+    const int pvalid = (int)((m_par - pfirst) < pcnt ? (m_par - pfirst) : pcnt);
     for (int i = threadIdx.x; i < pcnt * D; i += blockDim.x) {
       const int p = i / D, d = i % D;
       if (pfirst + p >= m_par) continue;
       const float c0 = cur[(2 * p) * D + d];
       const float v = (first + 2 * p + 1 < m_child) ? (c0 + cur[(2 * p + 1) * D + d]) * 0.5f : c0;
       nxt[p * D + d] = v;
-      dst[p * D + d] = v;
+      a.pyr[dst + p * D + d] = v;
     }
     __syncthreads();
+    put_f16_rows<D>(a, nxt, pvalid, dst / D);
     float* tmp = cur;
     cur = nxt;
     nxt = tmp;
@@ -69,7 +87,7 @@ __global__ __launch_bounds__(256) void pyr_leaf_kernel(PyrArgs a) {
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int rsub = lane / LPR, d0 = (lane % LPR) * 8;
   const T* kh = static_cast<const T*>(a.k) + (int64_t)bh * a.cap * D;
-  float* head = a.pyr + (int64_t)bh * a.geo.rows * D;
+  const int64_t head = (int64_t)bh * a.geo.rows * D;
   const int64_t M1 = level_rows(a.n, a.C, 1);
   for (int li = w; li < kLeafChunk; li += 4) {
     const int64_t j = chunk * kLeafChunk + li;
@@ -89,15 +107,21 @@ __global__ __launch_bounds__(256) void pyr_leaf_kernel(PyrArgs a) {
 #pragma unroll
       for (int o = LPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
     if (lane < LPR) {
-      const float inv_cnt = (float)cnt;
-      float* dst = head + (a.geo.level_off[1] + j) * D + d0;
+      const float cnt_f = (float)cnt;
+      const int64_t dst = head + (a.geo.level_off[1] + j) * D + d0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float mval = acc[e] / inv_cnt;
+        const float mval = acc[e] / cnt_f;
         s_a[li * D + d0 + e] = mval;
-        dst[e] = mval;
+        a.pyr[dst + e] = mval;
       }
     }
+  }
+  __syncthreads();
+  {
+    const int64_t first = chunk * kLeafChunk;
+    const int nleaf = (int)((M1 - first) < kLeafChunk ? (M1 - first) : kLeafChunk);
+    put_f16_rows<D>(a, s_a, nleaf, (head + (a.geo.level_off[1] + first) * D) / D);
   }
   __syncthreads();
   const int64_t first = chunk * kLeafChunk;
@@ -112,11 +136,11 @@ __global__ __launch_bounds__(256) void pyr_up_kernel(PyrArgs a, int32_t base_lev
   __shared__ float s_b[kUpChunk / 2 * D];
   const int bh = (int)(blockIdx.x % a.BH);
   const int64_t chunk = blockIdx.x / a.BH;
-  float* head = a.pyr + (int64_t)bh * a.geo.rows * D;
+  const int64_t head = (int64_t)bh * a.geo.rows * D;
   const int64_t mb = level_rows(a.n, a.C, base_level);
   const int64_t first = chunk * kUpChunk;
   const int cnt0 = (int)((mb - first) < kUpChunk ? (mb - first) : kUpChunk);
-  const float* src = head + (a.geo.level_off[base_level] + first) * D;
+  const float* src = a.pyr + head + (a.geo.level_off[base_level] + first) * D;
   for (int i = threadIdx.x; i < cnt0 * D; i += blockDim.x) s_a[i] = src[i];
   __syncthreads();
   const int32_t hi = a.L < base_level + kUpLevels ? a.L : base_level + kUpLevels;
@@ -124,7 +148,10 @@ __global__ __launch_bounds__(256) void pyr_up_kernel(PyrArgs a, int32_t base_lev
 }
 
 hipError_t launch_build_pyramid(const Problem& p, const void* k, float* pyr, hipStream_t stream) {
-  PyrArgs a{k, pyr, p.N, p.cap, p.B * p.Hkv, p.C, p.L, p.geo};
+  const int64_t plane = (int64_t)p.B * p.Hkv * p.geo.rows * p.D;
+  _Float16* f16 = reinterpret_cast<_Float16*>(pyr + plane);
+  int32_t* ex = reinterpret_cast<int32_t*>(f16 + plane);
+  PyrArgs a{k, pyr, f16, ex, p.N, p.cap, p.B * p.Hkv, p.C, p.L, p.geo};
   const int64_t M1 = level_rows(p.N, p.C, 1);
   const int64_t leaf_blocks = (int64_t)a.BH * ((M1 + kLeafChunk - 1) / kLeafChunk);
   hipError_t err = hipSuccess;

@@ -15,6 +15,8 @@ struct RouteArgs {
   const void* q;
   const void* k;
   const float* pyr;
+  const _Float16* f16;  // block-floating-point copy of the summaries
+  const int32_t* ex;
   int32_t* idx;
   float* score;
   int32_t B, N, Hq, Hkv, C, K, L;
@@ -76,9 +78,151 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
   }
 }
 
+// ---- stage 1 on MFMA (bf16 inputs) -------------------------------------------
+// Scores of the candidates of level l: q_h' . P_{l-1}[r] for the <= 2 nA
+// child rows r, as (16 child rows) x d x (16 columns = the G_Q query heads)
+// v_mfma_f32_16x16x32_f16 tiles.  Rows come from the pyramid's fp16
+// block-floating-point copy (row * 2^-ex[row]); q is bf16, so q * 2^-eq is
+// exact in fp16; the logit is rescaled by 2^(ex + eq) in fp32.  A row costs
+// d * 2 bytes of gather (half the fp32 row).  The sibling LSE is in-lane
+// (accumulator rows 2c, 2c+1) and the GQA sum a shuffle over the G_Q columns.
+template <int D, int G>
+__device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq, const _Float16* hb,
+                                                 const int32_t* xb, const PyrGeom& geo, int64_t n, int64_t t,
+                                                 bool causal, int32_t C, int32_t l, float scale) {
+  constexpr int NS = D / 32;
+  const int lane = lane_id(), g = lane >> 4, col = lane & 15;
+  const int64_t m_child = level_rows(n, C, l - 1);
+  const int64_t child_span = (int64_t)C << (l - 2);
+  const int64_t lvl = geo.level_off[l - 1];
+  for (int rt = 0; rt * 16 < 2 * nA; ++rt) {
+    const int row = 16 * rt + col;
+    const int c = row >> 1;
+    const int64_t r = (c < nA) ? 2 * (int64_t)s.cand[c] + (row & 1) : -1;
+    const bool vrow = (c < nA) && r < m_child && (!causal || r * child_span <= t);
+    const int er = vrow ? xb[lvl + r] : 0;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      halfx8 fa;
+      if (vrow) fa = *reinterpret_cast<const halfx8*>(hb + (lvl + r) * D + g * (D / 4) + 8 * st);
+      else fa = halfx8{0, 0, 0, 0, 0, 0, 0, 0};
+      acc = mma16x16x32(fa, fq[st], acc);
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ri = 16 * rt + 4 * g + i;
+      const int ci = ri >> 1;
+      const int64_t rr = (ci < nA) ? 2 * (int64_t)s.cand[ci] + (ri & 1) : -1;
+      const bool v = (ci < nA) && rr < m_child && (!causal || rr * child_span <= t);
+      const int eri = __shfl(er, 4 * g + i);  // exponent of accumulator row 4g+i
+      x[i] = v ? ldexpf(acc[i], eri + eq) * scale : -INFINITY;
+    }
+    float u0 = lse2(x[0], x[1]), u1 = lse2(x[2], x[3]);
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) {
+      u0 += __shfl_xor(u0, o);
+      u1 += __shfl_xor(u1, o);
+    }
+    const int c0 = 8 * rt + 2 * g;
+    if (col == 0) {
+      if (c0 < nA) s.score[c0] = u0;
+      if (c0 + 1 < nA) s.score[c0 + 1] = u1;
+    }
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArgs a) {
+  constexpr int NS = D / 32;
+  __shared__ RouteLds s_r[kRouteWaves];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  int b, h;
+  int64_t t0;
+  map_query_block(a.Hkv, a.B, b, h, t0);
+  const int64_t t = t0 + w;
+  if (t >= a.N) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int g = lane >> 4, col = lane & 15;
+  // B operand: column col = query head col of the group (zero beyond G_Q),
+  // scaled by 2^-eq into fp16 (exact for bf16 values)
+  float qv[NS][8];
+  float mx = 0.f;
+  if (col < G) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Hq + h * G + col) * a.N + t) * D;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      load8<uint16_t>(qrow + g * (D / 4) + 8 * st, qv[st]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[st][e]));
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[st][e] = 0.f;
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const int eq = row_exponent(mx);
+  halfx8 fq[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fq[st][e] = to_f16_scaled(qv[st][e], eq);
+  const int64_t bh = (int64_t)b * a.Hkv + h;
+  const _Float16* hb = a.f16 + bh * a.geo.rows * D;
+  const int32_t* xb = a.ex + bh * a.geo.rows;
+  RouteLds& s = s_r[w];
+  const bool causal = a.causal != 0;
+  int nA = 1;
+  if (lane == 0) s.cand[0] = 0;
+  int32_t kept = (lane == 0) ? 0 : -1;
+  int nI = 1;
+  wave_sync();
+  for (int32_t l = a.L; l >= 2; --l) {
+    const int64_t ml = level_rows(a.N, a.C, l);
+    const int64_t span = (int64_t)a.C << (l - 1);
+    const int32_t j = (lane < nA) ? s.cand[lane] : -1;
+    const bool valid = j >= 0 && j < ml && (!causal || (int64_t)j * span <= t);
+    const uint64_t mask = __ballot(valid);
+    const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+    nA = __popcll(mask);
+    wave_sync();
+    if (valid) s.cand[pos] = j;
+    wave_sync();
+    if (nA > a.K) {
+      score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, a.N, t, causal, a.C, l, a.scale);
+      wave_sync();
+      uint64_t key = (lane < nA) ? score_key(s.score[lane], s.cand[lane]) : 0ull;
+      key = wave_sort_desc(key);
+      nI = a.K;
+      kept = (lane < nI) ? key_index(key) : -1;
+    } else {
+      nI = nA;
+      kept = (lane < nA) ? s.cand[lane] : -1;
+    }
+    if (l > 2) {
+      wave_sync();
+      if (lane < nI) {
+        s.cand[2 * lane] = 2 * kept;
+        s.cand[2 * lane + 1] = 2 * kept + 1;
+      }
+      nA = 2 * nI;
+      wave_sync();
+    }
+  }
+  uint64_t k2 = (lane < nI) ? index_key(kept, -INFINITY) : 0ull;
+  k2 = wave_sort_desc(k2);
+  if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
+}
+
 hipError_t launch_route(const Problem& p, const void* q, const void* k, const float* pyr, int32_t* idx,
                         float* score, bool fused, hipStream_t stream) {
-  RouteArgs a{q, k, pyr, idx, score, p.B, p.N, p.Hq, p.Hkv, p.C, p.K, p.L, p.causal ? 1 : 0, p.cap, p.scale, p.geo};
+  const int64_t plane = (int64_t)p.B * p.Hkv * p.geo.rows * p.D;
+  const _Float16* f16 = reinterpret_cast<const _Float16*>(pyr + plane);
+  RouteArgs a{q, k, pyr, f16, reinterpret_cast<const int32_t*>(f16 + plane), idx, score, p.B, p.N, p.Hq, p.Hkv, p.C, p.K, p.L, p.causal ? 1 : 0,
+              p.cap, p.scale, p.geo};
   const int64_t blocks = (int64_t)p.B * p.Hkv * ((p.N + kRouteWaves - 1) / kRouteWaves);
   return dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
     using T = std::remove_pointer_t<decltype(tp)>;
@@ -86,6 +230,9 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
     constexpr int G = decltype(gc)::value;
     if (fused)
       PISA_LAUNCH("route_fused", stream, (route_kernel<T, D, G, true>), dim3((unsigned)blocks),
+                  dim3(kRouteWaves * kWave), 0, a);
+    else if (std::is_same<T, uint16_t>::value)
+      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G>), dim3((unsigned)blocks),
                   dim3(kRouteWaves * kWave), 0, a);
     else
       PISA_LAUNCH("route_stage1", stream, (route_kernel<T, D, G, false>), dim3((unsigned)blocks),

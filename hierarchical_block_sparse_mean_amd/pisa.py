@@ -180,7 +180,14 @@ def pyramid_bytes(p: Problem) -> int:
 
 
 def alloc_pyramid(p: Problem, device="cuda") -> torch.Tensor:
-    return torch.empty((p.B, p.Hkv, pyramid_rows(p), p.D), dtype=torch.float32, device=device)
+    """Flat float32 buffer of pisa_pyramid_bytes: fp32 summaries, then their
+    fp16 block-floating-point copy and per-row exponents."""
+    return torch.empty((pyramid_bytes(p) + 3) // 4, dtype=torch.float32, device=device)
+
+
+def pyramid_view(p: Problem, pyr: torch.Tensor) -> torch.Tensor:
+    """fp32 summaries [B][Hkv][R][D] of a pyramid buffer."""
+    return pyr[: p.B * p.Hkv * pyramid_rows(p) * p.D].view(p.B, p.Hkv, pyramid_rows(p), p.D)
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -191,7 +198,7 @@ def build_pyramid(p: Problem, k: torch.Tensor, pyr: torch.Tensor | None = None, 
     _need(k, "k", (p.B, p.Hkv, p.cap_tokens, p.D), p.torch_dtype)
     if pyr is None:
         pyr = alloc_pyramid(p, k.device)
-    _need(pyr, "pyr", (p.B, p.Hkv, pyramid_rows(p), p.D), torch.float32)
+    _need(pyr, "pyr", ((pyramid_bytes(p) + 3) // 4,), torch.float32)
     _check(load().pisa_build_pyramid(ctypes.byref(p.c()), k.data_ptr(), pyr.data_ptr(), _stream(stream)))
     return pyr
 
@@ -200,7 +207,21 @@ def pyramid_level(p: Problem, pyr: torch.Tensor, l: int, n: int | None = None) -
     """View of level l (rows M_l(n)) of a pyramid tensor."""
     n = p.N if n is None else n
     off = level_offset(p.cap_tokens, p.C, l)
-    return pyr[:, :, off:off + level_rows(n, p.C, l), :]
+    return pyramid_view(p, pyr)[:, :, off:off + level_rows(n, p.C, l), :]
+
+
+def pyramid_f16_level(p: Problem, pyr: torch.Tensor, l: int, n: int | None = None) -> torch.Tensor:
+    """Level l of the fp16 block-floating-point copy, decoded to float32
+    (f16 * 2^ex)."""
+    n = p.N if n is None else n
+    off = level_offset(p.cap_tokens, p.C, l)
+    R = pyramid_rows(p)
+    plane = p.B * p.Hkv * R * p.D
+    raw = pyr.view(torch.int16)
+    f16 = raw[2 * plane: 3 * plane].view(torch.float16).view(p.B, p.Hkv, R, p.D)
+    ex = raw[3 * plane: 3 * plane + 2 * p.B * p.Hkv * R].view(torch.int32).view(p.B, p.Hkv, R)
+    rows = slice(off, off + level_rows(n, p.C, l))
+    return torch.ldexp(f16[:, :, rows, :].float(), ex[:, :, rows, None].float())
 
 
 def select_workspace_bytes(p: Problem) -> int:

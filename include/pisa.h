@@ -93,7 +93,11 @@ typedef struct {
 } pisa_problem;
 
 /* ---- key pyramid [PYR] ------------------------------------------------- *
- * Layout: float pyr[B][Hkv][R][D], R = sum over levels l = 1..L(cap) of
+ * Layout: float pyr[B][Hkv][R][D], then a block-floating-point copy read by
+ * the bf16 routing kernel: fp16 f16[B][Hkv][R][D] = row * 2^-ex[row] and
+ * int32 ex[B][Hkv][R] (the row's largest magnitude scaled into [2^14, 2^15));
+ * pisa_pyramid_bytes covers all three.
+ * R = sum over levels l = 1..L(cap) of
  * M_l(cap), M_1(n) = ceil(n / C), M_{l+1} = ceil(M_l / 2), L(n) the first
  * level with one block.  Level l of head (b, h) starts at row
  * sum_{l' < l} M_{l'}(cap).  Level 1 holds leaf means of raw keys; level l+1

@@ -116,7 +116,7 @@ def test_decode_validation(lib):
 def test_pyramid_bytes(lib):
     p = _p(N=1000, cap=1100)
     rows = sum(oracle.level_rows(1100, 64, l) for l in range(1, oracle.levels(1100, 64) + 1))
-    assert lib.pisa_pyramid_bytes(ctypes.byref(p.c())) == 4 * rows * 64
+    assert lib.pisa_pyramid_bytes(ctypes.byref(p.c())) == rows * (64 * 6 + 4)
 
 
 def test_product_has_no_oracle_dependency():

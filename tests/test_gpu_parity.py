@@ -87,6 +87,10 @@ def test_pyramid(name):
         err = np.abs(got - ref)
         lim = 2e-6 * np.maximum(1.0, np.abs(ref)) + 2e-6
         assert (err <= lim).all(), f"level {l}: max err {err.max():.3g}"
+        # fp16 block-floating-point copy: within half an fp16 ulp of the row max
+        rec = to_host_f64(pisa.pyramid_f16_level(p, pyr, l))
+        rowmax = np.abs(got).max(axis=-1, keepdims=True)
+        assert (np.abs(rec - got) <= 2.0 ** -11 * rowmax + 1e-30).all(), f"level {l}: fp16 copy"
 
 
 @pytest.mark.parametrize("algo", [pisa.SELECT_TWO_STAGE, pisa.SELECT_FUSED], ids=["two_stage", "fused"])
