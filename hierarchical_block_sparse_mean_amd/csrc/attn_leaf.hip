@@ -101,6 +101,8 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
   T* s_vt = s_k + CP * KP;                   // [D][VP]
   __shared__ int32_t s_t[kAttnWaves][16];
   __shared__ int32_t s_slot[kAttnWaves][16];
+  // a tile's 16 output columns x D, staged so each lane stores 16-byte pieces
+  __shared__ __align__(16) T s_o[kAttnWaves][16][D + 16 / sizeof(T)];
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -217,17 +219,28 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
         oacc[db] = mma(fv, fp, oacc[db]);
       }
     }
-    // partial record of (query, slot, head): rows 4g+i of d-block db
-    if (live) {
+    // partial record of (query, slot, head): column col holds rows 4g+i of
+    // each d-block; stage the 16 x D tile in LDS, then store whole rows
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store1<T>(&s_o[w][col][db * 16 + 4 * g + i], oacc[db][i]);
+    if (live && g == 0) {
       const int64_t rec = ((hl * a.N + t) * a.K + s_slot[w][qi]) * G + hh;
-      T* po = static_cast<T*>(a.po) + rec * D;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store1<T>(po + db * 16 + 4 * g + i, oacc[db][i]);
-      if (g == 0) {
-        a.pm[rec] = m;
-        a.pl[rec] = l;
+      a.pm[rec] = m;
+      a.pl[rec] = l;
+    }
+    wave_sync();
+    {
+      constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte piece
+      constexpr int PER_COL = D / CH;
+      for (int i = lane; i < 16 * PER_COL; i += kWave) {
+        const int cc = i / PER_COL, piece = i % PER_COL;
+        const int qc = cc / G;
+        if (qc >= nq) continue;
+        const int64_t rec = ((hl * a.N + s_t[w][qc]) * a.K + s_slot[w][qc]) * G + (cc % G);
+        *reinterpret_cast<uint4*>(static_cast<T*>(a.po) + rec * D + piece * CH) =
+            *reinterpret_cast<const uint4*>(&s_o[w][cc][piece * CH]);
       }
     }
     wave_sync();
@@ -246,40 +259,69 @@ struct MergeArgs {
   int32_t N, Hq, Hkv, K;
 };
 
+// One wave per (query, KV head): m and l of the K slots x G heads go through
+// LDS; each lane then owns 8 output dims of one head and issues the loads of
+// all its slots' partial rows before combining them.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  __shared__ float s_m[4][32 * G], s_l[4][32 * G];
+  __shared__ int32_t s_ok[4][32];
+  const int w = threadIdx.x / kWave;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + w;
   if (wid >= a.heads * a.N) return;
   const int lane = lane_id();
   const int64_t hl = wid / a.N, t = wid % a.N;
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int32_t* sel = a.idx + (bh * a.N + t) * a.K;
+  const int64_t rec0 = (hl * a.N + t) * a.K * G;  // record of (slot 0, head 0)
+  for (int i = lane; i < a.K; i += kWave) s_ok[w][i] = (sel[i] >= 0 && sel[i] < a.M1) ? 1 : 0;
+  for (int i = lane; i < a.K * G; i += kWave) {
+    s_m[w][i] = a.pm[rec0 + i];
+    s_l[w][i] = a.pl[rec0 + i];
+  }
+  wave_sync();
   const T* po = static_cast<const T*>(a.po);
   for (int e0 = lane * 8; e0 < G * D; e0 += kWave * 8) {
     const int hh = e0 / D, d = e0 % D;
     float M = -INFINITY;
     for (int s = 0; s < a.K; ++s)
-      if (sel[s] >= 0 && sel[s] < a.M1) M = fmaxf(M, a.pm[((hl * a.N + t) * a.K + s) * G + hh]);
+      if (s_ok[w][s]) M = fmaxf(M, s_m[w][s * G + hh]);
     float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
-      for (int s = 0; s < a.K; ++s) {
-        if (sel[s] < 0 || sel[s] >= a.M1) continue;
-        const int64_t rec = ((hl * a.N + t) * a.K + s) * G + hh;
-        const float ms = a.pm[rec];
-        if (ms == -INFINITY) continue;
-        const float wgt = __expf(ms - M);
-        L += wgt * a.pl[rec];
-        float v[8];
-        load8<T>(po + rec * D + d, v);
+      for (int s0 = 0; s0 < a.K; s0 += 8) {
+        float v[8][8];
+        float wgt[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+        for (int u = 0; u < 8; ++u) {
+          const int s = s0 + u;
+          const bool ok = s < a.K && s_ok[w][s] && s_m[w][s * G + hh] != -INFINITY;
+          wgt[u] = ok ? __expf(s_m[w][s * G + hh] - M) : 0.f;
+          if (ok) load8<T>(po + (rec0 + s * G + hh) * D + d, v[u]);
+          else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+          }
+          if (ok) L += wgt[u] * s_l[w][s * G + hh];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt[u], v[u][i], acc[i]);
       }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     T* out = static_cast<T*>(a.o) + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D + d;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t wv[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) store1<T>(out + i, acc[i] * inv);
+      for (int i = 0; i < 4; ++i)
+        wv[i] = (uint32_t)f32_to_bf16(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16(acc[2 * i + 1] * inv) << 16);
+      *reinterpret_cast<uint4*>(out) = uint4{wv[0], wv[1], wv[2], wv[3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) store1<T>(out + i, acc[i] * inv);
+    }
     if (a.lse != nullptr && d == 0)
       a.lse[((int64_t)b * a.Hq + h * G + hh) * a.N + t] = L > 0.f ? M + __logf(L) : -INFINITY;
   }
