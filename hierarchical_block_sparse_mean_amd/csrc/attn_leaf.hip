@@ -99,8 +99,6 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
   T* s_vt = s_k + CP * KP;                   // [D][VP]
-  __shared__ int32_t s_t[kAttnWaves][16];
-  __shared__ int32_t s_slot[kAttnWaves][16];
   // a tile's 16 output columns x D, staged so each lane stores 16-byte pieces
   __shared__ __align__(16) T s_o[kAttnWaves][16][D + 16 / sizeof(T)];
 
@@ -145,26 +143,30 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
   const int g = lane >> 4, col = lane & 15;
   const int qi = col / G, hh = col % G;
   const T* qb = static_cast<const T*>(a.q);
-  for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += (int64_t)kAttnWaves * TQ) {
-    const int nq = (int)((p_end - tile) < TQ ? (p_end - tile) : TQ);
-    if (lane < TQ) {
-      const int32_t pr = (lane < nq) ? a.pairs[tile + lane] : -1;
-      s_t[w][lane] = pr >= 0 ? pr / a.K : -1;
-      s_slot[w][lane] = pr >= 0 ? pr % a.K : -1;
-    }
-    wave_sync();
-    const bool live = qi < nq;
-    const int64_t t = live ? s_t[w][qi] : -1;
-    // B operand of S^T = K Q^T: this lane's query-head column
-    Frag<T> fq[NS];
-    if (live) {
-      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D;
+  // column col of a tile = query qi (its pair) x head hh; the B operand of
+  // S^T = K Q^T is that query head's row
+  auto load_q = [&](int32_t pr, Frag<T>* f) {
+    if (pr >= 0) {
+      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + pr / a.K) * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) fq[s].load(qrow + g * (D / 4) + 8 * s);
+      for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
     } else {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) fq[s].zero();
+      for (int s = 0; s < NS; ++s) f[s].zero();
     }
+  };
+  const int64_t stride = (int64_t)kAttnWaves * TQ;
+  int64_t tile = p_begin + (int64_t)w * TQ;
+  int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
+  Frag<T> fq[NS];
+  load_q(pr, fq);
+  for (; tile < p_end; tile += stride) {
+    const int64_t nxt = tile + stride;
+    const int32_t pr_n = (nxt + qi < p_end) ? a.pairs[nxt + qi] : -1;
+    Frag<T> fn[NS];
+    load_q(pr_n, fn);
+    const bool live = pr >= 0;
+    const int64_t t = live ? pr / a.K : -1;
     floatx4 acc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
 #pragma unroll
       for (int i = 0; i < 4; ++i) store1<T>(&s_o[w][col][db * 16 + 4 * g + i], oacc[db][i]);
     if (live && g == 0) {
-      const int64_t rec = ((hl * a.N + t) * a.K + s_slot[w][qi]) * G + hh;
+      const int64_t rec = ((hl * a.N + t) * a.K + pr % a.K) * G + hh;
       a.pm[rec] = m;
       a.pl[rec] = l;
     }
@@ -234,16 +236,22 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
     {
       constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte piece
       constexpr int PER_COL = D / CH;
-      for (int i = lane; i < 16 * PER_COL; i += kWave) {
+#pragma unroll
+      for (int it = 0; it < 16 * PER_COL / kWave; ++it) {
+        const int i = it * kWave + lane;
         const int cc = i / PER_COL, piece = i % PER_COL;
-        const int qc = cc / G;
-        if (qc >= nq) continue;
-        const int64_t rec = ((hl * a.N + s_t[w][qc]) * a.K + s_slot[w][qc]) * G + (cc % G);
-        *reinterpret_cast<uint4*>(static_cast<T*>(a.po) + rec * D + piece * CH) =
-            *reinterpret_cast<const uint4*>(&s_o[w][cc][piece * CH]);
+        const int32_t pc = __shfl(pr, cc);  // pair of column cc (lane cc of group 0)
+        if (pc >= 0) {
+          const int64_t rec = ((hl * a.N + pc / a.K) * a.K + pc % a.K) * G + (cc % G);
+          *reinterpret_cast<uint4*>(static_cast<T*>(a.po) + rec * D + piece * CH) =
+              *reinterpret_cast<const uint4*>(&s_o[w][cc][piece * CH]);
+        }
       }
     }
     wave_sync();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) fq[s] = fn[s];
+    pr = pr_n;
   }
 }
 

@@ -74,16 +74,19 @@ struct S2Args {
   float scale;
 };
 
-// NCB: 16-key column blocks covering the 2C keys of a tile (2C <= 16 NCB).
+// NCB: 16-key blocks covering the 2C keys of a tile (2C <= 16 NCB).
+// Transposed tiles: S^T = K Q^T with the keys as MFMA rows (A from LDS) and
+// 16 columns = 16 / G_Q queries x G_Q heads (B = q rows), so the LSE over a
+// leaf's keys is an in-lane reduction plus two cross-group shuffles, and the
+// GQA sum is a shuffle over the G_Q columns of a query.
 template <typename T, int D, int G, int NCB>
 __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
-  constexpr int NS = D / 32;           // 32-wide contraction steps
-  constexpr int TQ = 16 / G;           // queries per 16-row tile
-  constexpr int PITCH = D + 16 / sizeof(T);  // LDS row pitch (elements)
+  constexpr int NS = D / 32;                  // 32-wide contraction steps
+  constexpr int TQ = 16 / G;                  // queries per 16-column tile
+  constexpr int PITCH = D + 16 / sizeof(T);   // LDS row pitch (elements)
+  constexpr float kLog2e = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* s_k = reinterpret_cast<T*>(smem_raw);  // [2C][PITCH]
-  __shared__ int32_t s_t[kS2Waves][16];
-  __shared__ int32_t s_slot[kS2Waves][16];
+  T* s_k = reinterpret_cast<T*>(smem_raw);  // [NCB*16][PITCH]
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -102,129 +105,112 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
   const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
   const int64_t p_end = p_begin + kS2Chunk < p_end_c ? p_begin + kS2Chunk : p_end_c;
 
-  // key tile: leaves 2*j2 and 2*j2+1 (2C rows, zero rows past the sequence)
+  // key tile: leaves 2*j2 and 2*j2+1 are the contiguous keys [key0, key0 + 2C)
   const int C = a.C;
   const int rows = 2 * C;
-  const int ncb = (rows + 15) / 16;
   const T* kh = static_cast<const T*>(a.k) + bh * a.cap * D;
   const int64_t key0 = 2 * j2 * (int64_t)C;
+  const int nkeys = (int)((a.N - key0) < rows ? (a.N - key0) : rows);  // existing keys
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
-  for (int i = threadIdx.x; i < ncb * 16 * (D / EPV); i += blockDim.x) {
+  for (int i = threadIdx.x; i < NCB * 16 * (D / EPV); i += blockDim.x) {
     const int r = i / (D / EPV), d = (i % (D / EPV)) * EPV;
-    const int64_t key = key0 + r;
     uint4 v = {0u, 0u, 0u, 0u};
-    if (r < rows && key < a.N) v = *reinterpret_cast<const uint4*>(kh + key * D + d);
+    if (r < nkeys) v = *reinterpret_cast<const uint4*>(kh + (key0 + r) * D + d);
     *reinterpret_cast<uint4*>(s_k + r * PITCH + d) = v;
   }
   __syncthreads();
 
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
+  const int qi = col / G, hh = col % G;
   const T* qb = static_cast<const T*>(a.q);
-  for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += (int64_t)kS2Waves * TQ) {
-    const int nq = (int)((p_end - tile) < TQ ? (p_end - tile) : TQ);
-    if (lane < TQ) {
-      const int32_t pr = (lane < nq) ? a.pairs[tile + lane] : -1;
-      s_t[w][lane] = pr >= 0 ? pr / a.K : -1;
-      s_slot[w][lane] = pr >= 0 ? pr % a.K : -1;
-    }
-    wave_sync();
-    // A fragments: row = col (0..15) -> query col / G, head col % G
-    const int qi_a = col / G, hh = col % G;
-    const int32_t ta = s_t[w][qi_a < TQ ? qi_a : 0];
-    Frag<T> fa[NS];
-    if (qi_a < nq) {
-      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + ta) * D;
+  const float sl2 = a.scale * kLog2e;  // logits in log2 units
+  float* out_base = a.scores + bh * (int64_t)a.N * a.K * 2;
+  auto load_q = [&](int32_t prq, Frag<T>* f) {
+    if (prq >= 0) {
+      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + prq / a.K) * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) fa[s].load(qrow + g * (D / 4) + 8 * s);
+      for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
     } else {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) fa[s].zero();
+      for (int s = 0; s < NS; ++s) f[s].zero();
     }
-    // S = Q K^T, 16 rows x 2C columns
+  };
+  const int64_t stride = (int64_t)kS2Waves * TQ;
+  int64_t tile = p_begin + (int64_t)w * TQ;
+  int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
+  Frag<T> fq[NS];
+  load_q(pr, fq);
+  for (; tile < p_end; tile += stride) {
+    // prefetch the next tile's pair and query rows
+    const int32_t pr_n = (tile + stride + qi < p_end) ? a.pairs[tile + stride + qi] : -1;
+    Frag<T> fn[NS];
+    load_q(pr_n, fn);
+    // re-read the key fragments from LDS every tile rather than keeping all
+    // of them live in registers (which would cap occupancy at one wave)
+    const T* sk = s_k;
+    asm volatile("" : "+v"(sk));
     floatx4 acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (cb < ncb) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          Frag<T> fb;
-          fb.load(s_k + (cb * 16 + col) * PITCH + g * (D / 4) + 8 * s);
-          acc[cb] = mma(fa[s], fb, acc[cb]);
-        }
+      for (int s = 0; s < NS; ++s) {
+        Frag<T> fk;
+        fk.load(sk + (cb * 16 + col) * PITCH + g * (D / 4) + 8 * s);
+        acc[cb] = mma(fk, fq[s], acc[cb]);
       }
     }
-    // masked LSE over each leaf's keys, per row (query head)
-    float lse[4][2];
+    // keys key_local < lim count for this column's query (t >= key0 + key_local)
+    int lim = 0;
+    if (pr >= 0) {
+      const int64_t t = pr / a.K;
+      lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
+    }
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      const int qi = row / G;
-      const int64_t t = (qi < nq) ? s_t[w][qi] : -1;
-      float mx[2] = {-INFINITY, -INFINITY};
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int cc = cb * 16 + col;
-        const int l = cc >= C ? 1 : 0;
-        const int64_t leaf = 2 * j2 + l;
-        const int64_t key = leaf * C + (cc - l * C);
-        const bool valid = cb < ncb && cc < rows && leaf < a.M1 && key < a.N && (!a.causal || key <= t) && t >= 0;
-        const float x = valid ? acc[cb][i] * a.scale : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int kl = cb * 16 + 4 * g + i;
+        const float x = kl < lim ? acc[cb][i] * sl2 : -INFINITY;
         acc[cb][i] = x;
-        mx[l] = fmaxf(mx[l], x);
+        if (kl < C) mx0 = fmaxf(mx0, x);
+        else mx1 = fmaxf(mx1, x);
       }
-      mx[0] = group_max<16>(mx[0]);
-      mx[1] = group_max<16>(mx[1]);
-      float sm[2] = {0.f, 0.f};
+    mx0 = fmaxf(mx0, __shfl_xor(mx0, 16));
+    mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
+    mx1 = fmaxf(mx1, __shfl_xor(mx1, 16));
+    mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int cc = cb * 16 + col;
-        const int l = cc >= C ? 1 : 0;
-        const float x = acc[cb][i];
-        if (x != -INFINITY) sm[l] += __expf(x - mx[l]);
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kl = cb * 16 + 4 * g + i;
+        if (kl < C) s0 += exp2f(acc[cb][i] - mx0);  // exp2(-inf) = 0
+        else s1 += exp2f(acc[cb][i] - mx1);
       }
-      sm[0] = group_sum<16>(sm[0]);
-      sm[1] = group_sum<16>(sm[1]);
+    s0 += __shfl_xor(s0, 16);
+    s0 += __shfl_xor(s0, 32);
+    s1 += __shfl_xor(s1, 16);
+    s1 += __shfl_xor(s1, 32);
+    constexpr float kLn2 = 0.6931471805599453f;
+    float u0 = (mx0 == -INFINITY) ? -INFINITY : (mx0 + __log2f(s0)) * kLn2;
+    float u1 = (mx1 == -INFINITY) ? -INFINITY : (mx1 + __log2f(s1)) * kLn2;
+    // GQA sum over the G columns of the query
 #pragma unroll
-      for (int l = 0; l < 2; ++l) lse[i][l] = (mx[l] == -INFINITY) ? -INFINITY : mx[l] + __logf(sm[l]);
+    for (int o = 1; o < G; o <<= 1) {
+      u0 += __shfl_xor(u0, o);
+      u1 += __shfl_xor(u1, o);
     }
-    // sum over the G heads of each query and write the pair's two leaf scores
-    float* out_base = a.scores + bh * (int64_t)a.N * a.K * 2;
-    if (G <= 4) {
-#pragma unroll
-      for (int qq = 0; qq < 4 / G; ++qq) {
-        float u0 = 0.f, u1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-          u0 += lse[qq * G + i][0];
-          u1 += lse[qq * G + i][1];
-        }
-        const int qi = (4 * g) / G + qq;
-        if (col == qq && qi < nq) {
-          const int64_t o = ((int64_t)s_t[w][qi] * a.K + s_slot[w][qi]) * 2;
-          out_base[o] = u0;
-          out_base[o + 1] = u1;
-        }
-      }
-    } else {
-      float u0 = lse[0][0] + lse[1][0] + lse[2][0] + lse[3][0];
-      float u1 = lse[0][1] + lse[1][1] + lse[2][1] + lse[3][1];
-      u0 += __shfl_xor(u0, 16);
-      u1 += __shfl_xor(u1, 16);
-      if (G == 16) {
-        u0 += __shfl_xor(u0, 32);
-        u1 += __shfl_xor(u1, 32);
-      }
-      const int qi = (4 * g) / G;
-      const bool writer = (G == 8) ? ((g & 1) == 0 && col == 0) : (lane == 0);
-      if (writer && qi < nq) {
-        const int64_t o = ((int64_t)s_t[w][qi] * a.K + s_slot[w][qi]) * 2;
-        out_base[o] = u0;
-        out_base[o + 1] = u1;
-      }
+    if (g == 0 && hh == 0 && pr >= 0) {
+      out_base[(int64_t)pr * 2] = u0;
+      out_base[(int64_t)pr * 2 + 1] = u1;
     }
-    wave_sync();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) fq[s] = fn[s];
+    pr = pr_n;
   }
 }
 
@@ -284,7 +270,8 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
-    const size_t lds = (size_t)((2 * p.C + 15) / 16 * 16) * (D + 16 / sizeof(T)) * sizeof(T);
+    const int ncb = p.C <= 32 ? 4 : (p.C <= 64 ? 8 : 16);
+    const size_t lds = (size_t)ncb * 16 * (D + 16 / sizeof(T)) * sizeof(T);
     auto run = [&](auto kern) -> hipError_t {
       if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
