@@ -165,6 +165,33 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
   return key;
 }
 
+// Bitonic sort inside aligned groups of N lanes (N a power of two <= 64);
+// lanes [0, N) end in descending order (other groups alternate direction).
+template <int N>
+__device__ __forceinline__ uint64_t group_sort_desc(uint64_t key) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t other = shfl_xor_u64(key, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      key = take_max ? (key > other ? key : other) : (key < other ? key : other);
+    }
+  }
+  return key;
+}
+
+// The K largest keys of lanes [0, 2K) land in lanes [0, K), in no particular
+// order: sort both K-lane halves (opposite directions) and keep the larger of
+// each pair (lane, lane + K).  K a power of two <= 32.
+template <int K>
+__device__ __forceinline__ uint64_t top_half(uint64_t key) {
+  key = group_sort_desc<K>(key);
+  const uint64_t other = shfl_xor_u64(key, K);
+  return ((lane_id() & K) == 0) ? (key > other ? key : other) : key;
+}
+
 // ---- pyramid geometry (capacity layout, see pisa.h) -----------------------
 __host__ __device__ __forceinline__ int64_t level_rows(int64_t n, int32_t C, int32_t l) {
   // M_l(n) = ceil(n / (C * 2^(l-1)))

@@ -88,19 +88,18 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
 // (accumulator rows 2c, 2c+1) and the GQA sum a shuffle over the G_Q columns.
 template <int D, int G>
 __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq, const _Float16* hb,
-                                                 const int32_t* xb, const PyrGeom& geo, int64_t n, int64_t t,
-                                                 bool causal, int32_t C, int32_t l, float scale) {
+                                                 const int32_t* xb, const PyrGeom& geo, int32_t m_child, int32_t tl,
+                                                 int32_t l, float sl2) {
   constexpr int NS = D / 32;
   const int lane = lane_id(), g = lane >> 4, col = lane & 15;
-  const int64_t m_child = level_rows(n, C, l - 1);
-  const int64_t child_span = (int64_t)C << (l - 2);
   const int64_t lvl = geo.level_off[l - 1];
   for (int rt = 0; rt * 16 < 2 * nA; ++rt) {
+    // A row `col` of the tile: child (row & 1) of candidate row >> 1
     const int row = 16 * rt + col;
     const int c = row >> 1;
-    const int64_t r = (c < nA) ? 2 * (int64_t)s.cand[c] + (row & 1) : -1;
-    const bool vrow = (c < nA) && r < m_child && (!causal || r * child_span <= t);
-    const int er = vrow ? xb[lvl + r] : 0;
+    const int32_t r = (c < nA) ? 2 * s.cand[c] + (row & 1) : 0x7fffffff;
+    const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
+    const int32_t er = vrow ? xb[lvl + r] : INT32_MIN;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -109,33 +108,38 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
       else fa = halfx8{0, 0, 0, 0, 0, 0, 0, 0};
       acc = mma16x16x32(fa, fq[st], acc);
     }
+    // accumulator row 4g+i: its exponent (INT32_MIN = invalid child) sits in
+    // lane 4g+i; logits in log2 units
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ri = 16 * rt + 4 * g + i;
-      const int ci = ri >> 1;
-      const int64_t rr = (ci < nA) ? 2 * (int64_t)s.cand[ci] + (ri & 1) : -1;
-      const bool v = (ci < nA) && rr < m_child && (!causal || rr * child_span <= t);
-      const int eri = __shfl(er, 4 * g + i);  // exponent of accumulator row 4g+i
-      x[i] = v ? ldexpf(acc[i], eri + eq) * scale : -INFINITY;
+      const int32_t eri = __shfl(er, 4 * g + i);
+      x[i] = (eri == INT32_MIN) ? -INFINITY : ldexpf(acc[i], eri + eq) * sl2;
     }
-    float u0 = lse2(x[0], x[1]), u1 = lse2(x[2], x[3]);
+    float u[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float m = fmaxf(x[2 * p], x[2 * p + 1]);
+      u[p] = (m == -INFINITY) ? -INFINITY : m + __log2f(exp2f(x[2 * p] - m) + exp2f(x[2 * p + 1] - m));
+    }
 #pragma unroll
     for (int o = 1; o < G; o <<= 1) {
-      u0 += __shfl_xor(u0, o);
-      u1 += __shfl_xor(u1, o);
+      u[0] += __shfl_xor(u[0], o);
+      u[1] += __shfl_xor(u[1], o);
     }
     const int c0 = 8 * rt + 2 * g;
     if (col == 0) {
-      if (c0 < nA) s.score[c0] = u0;
-      if (c0 + 1 < nA) s.score[c0 + 1] = u1;
+      if (c0 < nA) s.score[c0] = u[0];
+      if (c0 + 1 < nA) s.score[c0 + 1] = u[1];
     }
   }
 }
 
-template <int D, int G>
+// KP: K when K is 16 or 32 (top-K by half sorts), else 0 (full wave sort).
+template <int D, int G, int KP>
 __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArgs a) {
   constexpr int NS = D / 32;
+  constexpr float kLog2e = 1.4426950408889634f;
   __shared__ RouteLds s_r[kRouteWaves];
   const int w = threadIdx.x / kWave, lane = lane_id();
   int b, h;
@@ -175,16 +179,18 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
   const int32_t* xb = a.ex + bh * a.geo.rows;
   RouteLds& s = s_r[w];
   const bool causal = a.causal != 0;
+  const float sl2 = a.scale * kLog2e;
   int nA = 1;
   if (lane == 0) s.cand[0] = 0;
   int32_t kept = (lane == 0) ? 0 : -1;
   int nI = 1;
   wave_sync();
   for (int32_t l = a.L; l >= 2; --l) {
-    const int64_t ml = level_rows(a.N, a.C, l);
-    const int64_t span = (int64_t)a.C << (l - 1);
-    const int32_t j = (lane < nA) ? s.cand[lane] : -1;
-    const bool valid = j >= 0 && j < ml && (!causal || (int64_t)j * span <= t);
+    // valid blocks of level l: index < M_l and (causal) first token <= t
+    const int32_t ml = (int32_t)level_rows(a.N, a.C, l);
+    const int32_t tl_blk = causal ? (int32_t)(t / ((int64_t)a.C << (l - 1))) : 0x7fffffff;
+    const int32_t j = (lane < nA) ? s.cand[lane] : 0x7fffffff;
+    const bool valid = j < ml && j <= tl_blk;
     const uint64_t mask = __ballot(valid);
     const int pos = __popcll(mask & ((1ull << lane) - 1ull));
     nA = __popcll(mask);
@@ -192,10 +198,13 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
     if (valid) s.cand[pos] = j;
     wave_sync();
     if (nA > a.K) {
-      score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, a.N, t, causal, a.C, l, a.scale);
+      const int32_t m_child = (int32_t)level_rows(a.N, a.C, l - 1);
+      const int32_t tl = causal ? (int32_t)(t / ((int64_t)a.C << (l - 2))) : 0x7fffffff;
+      score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, m_child, tl, l, sl2);
       wave_sync();
       uint64_t key = (lane < nA) ? score_key(s.score[lane], s.cand[lane]) : 0ull;
-      key = wave_sort_desc(key);
+      if (KP) key = top_half<(KP ? KP : 16)>(key);
+      else key = wave_sort_desc(key);
       nI = a.K;
       kept = (lane < nI) ? key_index(key) : -1;
     } else {
@@ -212,8 +221,9 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
       wave_sync();
     }
   }
-  uint64_t k2 = (lane < nI) ? index_key(kept, -INFINITY) : 0ull;
-  k2 = wave_sort_desc(k2);
+  uint64_t k2 = (lane < nI) ? index_key(kept, 0.f) : 0ull;
+  if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
+  else k2 = wave_sort_desc(k2);
   if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
 }
 
@@ -231,8 +241,14 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
     if (fused)
       PISA_LAUNCH("route_fused", stream, (route_kernel<T, D, G, true>), dim3((unsigned)blocks),
                   dim3(kRouteWaves * kWave), 0, a);
+    else if (std::is_same<T, uint16_t>::value && p.K == 16)
+      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G, 16>), dim3((unsigned)blocks),
+                  dim3(kRouteWaves * kWave), 0, a);
+    else if (std::is_same<T, uint16_t>::value && p.K == 32)
+      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G, 32>), dim3((unsigned)blocks),
+                  dim3(kRouteWaves * kWave), 0, a);
     else if (std::is_same<T, uint16_t>::value)
-      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G>), dim3((unsigned)blocks),
+      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G, 0>), dim3((unsigned)blocks),
                   dim3(kRouteWaves * kWave), 0, a);
     else
       PISA_LAUNCH("route_stage1", stream, (route_kernel<T, D, G, false>), dim3((unsigned)blocks),
