@@ -57,6 +57,40 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+def source_digest() -> str:
+    """Digest of the HIP sources: counter summaries taken from other sources
+    are stale."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hierarchical_block_sparse_mean_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str, per_launch_bytes=None):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<kernel>_<workload>.txt
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy), or None if
+    absent or taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def attended_keys(idx, N: int, C: int, causal: bool):
     """Sum over (b, h, t, slot) of the keys attention reads for that leaf."""
     import torch
@@ -167,40 +201,72 @@ def main() -> int:
     per_kernel = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
                   for name, (n, tot) in kernels.items()}
 
-    # ---- algorithmic work of the kernels -----------------------------------
+    # ---- algorithmic work of the kernels (per step) ----------------------------
     G = w.gq
     esize = 2 if w.dtype == "bf16" else 4
     mfma_peak = PEAK["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else PEAK["mfma_f32_TFLOPs"]
     blk2 = ws[: w.B * w.Hkv * w.N * w.K * 4].view(torch.int32).view(w.B, w.Hkv, w.N, w.K)
     scored_keys, s1_pairs = stage1_scored_keys(blk2, w.N, w.C, w.causal)
     attn_keys = attended_keys(idx, w.N, w.C, w.causal)
+    kept_pairs = int((idx >= 0).sum().item())
     M = [pisa.level_rows(w.N, w.C, l) for l in range(1, pisa.levels(w.N, w.C) + 1)]
+    rc = pisa.route_counts(p, q, k, pyr) if w.dtype == "bf16" else None
+    queries = w.B * w.Hkv * w.N
     work = {
         # 4 d flops per attended (query head, key): q.k and p.v
+        "attn_leaf": ("mfma", 4.0 * w.D * G * attn_keys, "TFLOP/s",
+                      f"4*d flop per attended (query head, key); {attn_keys * G} such pairs"),
         "attn_query": ("mfma", 4.0 * w.D * G * attn_keys, "TFLOP/s",
-                       f"4*d flops per attended (query head, key) pair; {attn_keys * G} pairs"),
+                       f"4*d flop per attended (query head, key); {attn_keys * G} such pairs"),
         # 2 d flops per scored (query head, raw key)
         "leaf_score": ("mfma", 2.0 * w.D * G * scored_keys, "TFLOP/s",
-                       f"2*d flops per scored (query head, raw key); {scored_keys * G} pairs from {s1_pairs} "
-                       "(query, level-2 block) pairs"),
+                       f"2*d flop per scored (query head, raw key); {scored_keys * G} such pairs from {s1_pairs} "
+                       "(query, kept level-2 block) pairs"),
         # read every key once, write leaf means and the four levels above them
         "pyr_leaf": ("hbm", float(w.B * w.Hkv * (w.N * w.D * esize + sum(M[:5]) * w.D * 4)), "GB/s",
                      "N*d*elem read + (M1+..+M5)*d*4 written per (b, h)"),
+        # merge: read G partial rows (d elems + m, l) per kept pair, write o
+        "attn_merge": ("hbm", float(kept_pairs * G * (w.D * esize + 8) + w.B * w.Hq * w.N * w.D * esize), "GB/s",
+                       "per kept (query, leaf): G*(d*elem + 8) bytes of partials read; o written once"),
     }
+    if rc is not None:
+        # per (t, h): the scored child summaries (fp32 rows, d*4 bytes each),
+        # the group's queries and the kept list
+        route_bytes = rc["child_rows"] * w.D * 4 + queries * (G * w.D * esize + w.K * 4)
+        work["route_stage1"] = ("hbm", float(route_bytes), "GB/s",
+                                f"{rc['child_rows']} child summary rows x d*4 B + G*d*elem (q) + K*4 per (t, h); "
+                                f"{rc['child_rows'] / max(1, rc['queries']):.1f} rows and "
+                                f"{rc['scored_levels'] / max(1, rc['queries']):.2f} scored levels per (t, h); "
+                                "rows are served from L2, so the fraction can exceed HBM peak")
     dominant = max(per_kernel, key=lambda n: per_kernel[n]["ms_per_step"])
     roofline = None
     if dominant in work:
         bound, amount, unit, note = work[dominant]
+        launches = per_kernel[dominant]["launches"] / args.steps
+        per_launch = amount / launches
         avg_s = per_kernel[dominant]["avg_ms"] / 1000.0
-        per_launch = amount  # one launch per step for these kernels
         if unit == "TFLOP/s":
             achieved, peak = per_launch / avg_s / 1e12, mfma_peak
         else:
             achieved, peak = per_launch / avg_s / 1e9, PEAK["hbm_GBps"]
         roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
-                    "unit": unit, "frac": round(achieved / peak, 5), "traffic": None,
-                    "avg_launch_ms": round(per_kernel[dominant]["avg_ms"], 4), "work_per_launch": amount,
-                    "work_note": note}
+                    "unit": unit, "frac": round(achieved / peak, 5),
+                    "traffic": traffic_for(dominant, w.name, per_launch_bytes=None),
+                    "avg_launch_ms": round(per_kernel[dominant]["avg_ms"], 4),
+                    "work_per_launch": per_launch, "work_note": note}
+    kernel_rooflines = {}
+    for name, (bound, amount, unit, note) in work.items():
+        if name not in per_kernel:
+            continue
+        launches = per_kernel[name]["launches"] / args.steps
+        avg_s = per_kernel[name]["avg_ms"] / 1000.0
+        per_launch = amount / launches
+        if unit == "TFLOP/s":
+            kernel_rooflines[name] = {"bound": bound, "achieved_TFLOPs": round(per_launch / avg_s / 1e12, 2),
+                                      "frac": round(per_launch / avg_s / 1e12 / mfma_peak, 4)}
+        else:
+            kernel_rooflines[name] = {"bound": bound, "achieved_GBps": round(per_launch / avg_s / 1e9, 1),
+                                      "frac": round(per_launch / avg_s / 1e9 / PEAK["hbm_GBps"], 4)}
 
     # ---- flat single-level selector on the same inputs ------------------------
     flat_ms = None
@@ -296,6 +362,8 @@ def main() -> int:
         "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 4), "launches_per_step": vv["launches"] / args.steps}
                     for kk, vv in per_kernel.items()},
         "roofline": roofline,
+        "kernel_rooflines": kernel_rooflines,
+        "route_work": rc,
         "cpu_baseline": cpu,
         "parity": parity,
     }

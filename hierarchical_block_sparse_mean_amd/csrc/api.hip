@@ -242,6 +242,21 @@ pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, con
   return hip_status(pisa::launch_stage2(pr, q, k, blk2, idx, score, ws2, stream), "pisa_select (stage 2)");
 }
 
+pisa_status pisa_route_counts(const pisa_problem* p, const void* q, const void* k, const float* pyr,
+                              uint64_t* counts, void* ws, size_t ws_bytes, hipStream_t stream) {
+  pisa::Problem pr;
+  pisa_status s = validate(p, &pr);
+  if (s != PISA_OK) return s;
+  if (q == nullptr || k == nullptr || pyr == nullptr || counts == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "q, k, pyr and counts must be non-NULL");
+  if (pr.dtype != PISA_BF16) return fail(PISA_ERR_UNSUPPORTED, "work counters exist for the bf16 stage-1 kernel only");
+  if (ws == nullptr || ws_bytes < blk2_bytes(pr))
+    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed", blk2_bytes(pr));
+  return hip_status(pisa::launch_route(pr, q, k, pyr, static_cast<int32_t*>(ws), nullptr, false, stream,
+                                       reinterpret_cast<unsigned long long*>(counts)),
+                    "pisa_route_counts");
+}
+
 size_t pisa_attn_workspace_bytes(const pisa_problem* p) {
   pisa::Problem q;
   if (validate(p, &q) != PISA_OK) return 0;

@@ -156,17 +156,18 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
     }
   };
   const int64_t stride = (int64_t)kAttnWaves * TQ;
-  int64_t tile = p_begin + (int64_t)w * TQ;
-  int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
-  Frag<T> fq[NS];
-  load_q(pr, fq);
-  for (; tile < p_end; tile += stride) {
-    const int64_t nxt = tile + stride;
-    const int32_t pr_n = (nxt + qi < p_end) ? a.pairs[nxt + qi] : -1;
-    Frag<T> fn[NS];
-    load_q(pr_n, fn);
+  for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += stride) {
+    const int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
+    Frag<T> fq[NS];
+    load_q(pr, fq);
     const bool live = pr >= 0;
     const int64_t t = live ? pr / a.K : -1;
+    // K / V^T fragments are re-read from LDS every tile (an offset opaque to
+    // the compiler keeps them from being held in registers across tiles)
+    int toff = 0;
+    asm volatile("" : "+v"(toff));
+    const T* sk = s_k + toff;
+    const T* svt = s_vt + toff;
     floatx4 acc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -174,35 +175,39 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         Frag<T> fk;
-        fk.load(s_k + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+        fk.load(sk + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
         acc[kb] = mma(fk, fq[s], acc[kb]);
       }
     }
-    // column softmax statistics (keys are rows 4g+i of each 16-key block)
+    // column softmax statistics (keys are rows 4g+i of each 16-key block):
+    // max on the raw dot products, then p = exp2((x - max) * scale*log2e)
     const int64_t lim = live ? (a.causal ? (t - key0 + 1 < nkeys ? t - key0 + 1 : nkeys) : nkeys) : 0;
-    float m = -INFINITY;
+    float mraw = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kb * 16 + 4 * g + i;
-        const float x = key < lim ? acc[kb][i] * a.scale : -INFINITY;
+        const float x = key < lim ? acc[kb][i] : -INFINITY;
         acc[kb][i] = x;
-        m = fmaxf(m, x);
+        mraw = fmaxf(mraw, x);
       }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 16));
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    const float sl2 = a.scale * 1.4426950408889634f;
+    const float nb = -mraw * sl2;
     float l = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = (acc[kb][i] == -INFINITY) ? 0.f : __expf(acc[kb][i] - m);
+        const float pv = exp2f(fmaf(acc[kb][i], sl2, nb));  // exp2(-inf) = 0
         acc[kb][i] = pv;
         l += pv;
       }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    const float m = mraw * a.scale;  // the partial's max logit (natural units)
     // O^T = V^T P^T, contraction over 32 keys = 16-key blocks (2s, 2s+1)
     floatx4 oacc[D / 16];
 #pragma unroll
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
         Frag<T> fv;
-        const T* row = s_vt + (db * 16 + col) * VP;
+        const T* row = svt + (db * 16 + col) * VP;
         fv.load4x2(row + (2 * sp) * 16 + 4 * g, row + (2 * sp + 1) * 16 + 4 * g);
         oacc[db] = mma(fv, fp, oacc[db]);
       }
@@ -249,9 +254,6 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
       }
     }
     wave_sync();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) fq[s] = fn[s];
-    pr = pr_n;
   }
 }
 

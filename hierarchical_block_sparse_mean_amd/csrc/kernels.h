@@ -65,7 +65,7 @@ hipError_t launch_build_pyramid(const Problem& p, const void* k, float* pyr, hip
 // route.hip: one wave per (b, h, t); fused = all levels incl. raw-key leaves
 // (writes idx/score), else stage 1 (writes the kept level-2 blocks to idx).
 hipError_t launch_route(const Problem& p, const void* q, const void* k, const float* pyr, int32_t* idx,
-                        float* score, bool fused, hipStream_t stream);
+                        float* score, bool fused, hipStream_t stream, unsigned long long* counts = nullptr);
 // route.hip: query-major attention, one wave per (b, h, t)
 hipError_t launch_attn_query(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
                              void* o, float* lse, hipStream_t stream);

@@ -12,6 +12,7 @@ namespace pisa {
 constexpr int kRouteWaves = 4;
 
 struct RouteArgs {
+  unsigned long long* counts;  // optional work counters (diagnostics), or null
   const void* q;
   const void* k;
   const float* pyr;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
 template <int D, int G>
 __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq, const _Float16* hb,
                                                  const int32_t* xb, const PyrGeom& geo, int32_t m_child, int32_t tl,
-                                                 int32_t l, float sl2) {
+                                                 int32_t l, float sl2, int64_t* rows_out) {
   constexpr int NS = D / 32;
   const int lane = lane_id(), g = lane >> 4, col = lane & 15;
   const int64_t lvl = geo.level_off[l - 1];
@@ -99,6 +100,7 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
     const int c = row >> 1;
     const int32_t r = (c < nA) ? 2 * s.cand[c] + (row & 1) : 0x7fffffff;
     const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
+    if (rows_out != nullptr) *rows_out += __popcll(__ballot(vrow) & 0xFFFFull);
     const int32_t er = vrow ? xb[lvl + r] : INT32_MIN;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -184,6 +186,8 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
   if (lane == 0) s.cand[0] = 0;
   int32_t kept = (lane == 0) ? 0 : -1;
   int nI = 1;
+  int64_t w_rows = 0, w_cands = 0, w_levels = 0;  // diagnostics only
+  int64_t* rows_ptr = a.counts != nullptr ? &w_rows : nullptr;
   wave_sync();
   for (int32_t l = a.L; l >= 2; --l) {
     // valid blocks of level l: index < M_l and (causal) first token <= t
@@ -200,7 +204,9 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
     if (nA > a.K) {
       const int32_t m_child = (int32_t)level_rows(a.N, a.C, l - 1);
       const int32_t tl = causal ? (int32_t)(t / ((int64_t)a.C << (l - 2))) : 0x7fffffff;
-      score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, m_child, tl, l, sl2);
+      score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, m_child, tl, l, sl2, rows_ptr);
+      w_cands += nA;
+      w_levels += 1;
       wave_sync();
       uint64_t key = (lane < nA) ? score_key(s.score[lane], s.cand[lane]) : 0ull;
       if (KP) key = top_half<(KP ? KP : 16)>(key);
@@ -225,13 +231,20 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
   if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
   else k2 = wave_sort_desc(k2);
   if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
+  if (a.counts != nullptr && lane == 0) {
+    atomicAdd(&a.counts[0], 1ull);
+    atomicAdd(&a.counts[1], (unsigned long long)w_cands);
+    atomicAdd(&a.counts[2], (unsigned long long)w_rows);
+    atomicAdd(&a.counts[3], (unsigned long long)w_levels);
+    atomicAdd(&a.counts[4], (unsigned long long)nI);
+  }
 }
 
 hipError_t launch_route(const Problem& p, const void* q, const void* k, const float* pyr, int32_t* idx,
-                        float* score, bool fused, hipStream_t stream) {
+                        float* score, bool fused, hipStream_t stream, unsigned long long* counts) {
   const int64_t plane = (int64_t)p.B * p.Hkv * p.geo.rows * p.D;
   const _Float16* f16 = reinterpret_cast<const _Float16*>(pyr + plane);
-  RouteArgs a{q, k, pyr, f16, reinterpret_cast<const int32_t*>(f16 + plane), idx, score, p.B, p.N, p.Hq, p.Hkv, p.C, p.K, p.L, p.causal ? 1 : 0,
+  RouteArgs a{counts, q, k, pyr, f16, reinterpret_cast<const int32_t*>(f16 + plane), idx, score, p.B, p.N, p.Hq, p.Hkv, p.C, p.K, p.L, p.causal ? 1 : 0,
               p.cap, p.scale, p.geo};
   const int64_t blocks = (int64_t)p.B * p.Hkv * ((p.N + kRouteWaves - 1) / kRouteWaves);
   return dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {

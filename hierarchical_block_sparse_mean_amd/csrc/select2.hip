@@ -75,11 +75,13 @@ struct S2Args {
 };
 
 // NCB: 16-key blocks covering the 2C keys of a tile (2C <= 16 NCB).
+// CB0: blocks of the first leaf when C is a multiple of 16 (C = 16 CB0), so
+// the leaf of a block is known at compile time; 0 for other C.
 // Transposed tiles: S^T = K Q^T with the keys as MFMA rows (A from LDS) and
 // 16 columns = 16 / G_Q queries x G_Q heads (B = q rows), so the LSE over a
 // leaf's keys is an in-lane reduction plus two cross-group shuffles, and the
 // GQA sum is a shuffle over the G_Q columns of a query.
-template <typename T, int D, int G, int NCB>
+template <typename T, int D, int G, int NCB, int CB0>
 __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
   constexpr int NS = D / 32;                  // 32-wide contraction steps
   constexpr int TQ = 16 / G;                  // queries per 16-column tile
@@ -147,9 +149,11 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
     Frag<T> fn[NS];
     load_q(pr_n, fn);
     // re-read the key fragments from LDS every tile rather than keeping all
-    // of them live in registers (which would cap occupancy at one wave)
-    const T* sk = s_k;
-    asm volatile("" : "+v"(sk));
+    // of them live in registers (which would cap occupancy at one wave): the
+    // offset is opaque to the compiler, the pointer stays an LDS pointer
+    int koff = 0;
+    asm volatile("" : "+v"(koff));
+    const T* sk = s_k + koff;
     floatx4 acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -167,37 +171,41 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
       const int64_t t = pr / a.K;
       lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
     }
+    // masked raw dot products; max per leaf; exp2 of (x - max) * scale*log2e
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kl = cb * 16 + 4 * g + i;
-        const float x = kl < lim ? acc[cb][i] * sl2 : -INFINITY;
+        const float x = kl < lim ? acc[cb][i] : -INFINITY;
         acc[cb][i] = x;
-        if (kl < C) mx0 = fmaxf(mx0, x);
+        const bool first = CB0 ? (cb < CB0) : (kl < C);
+        if (first) mx0 = fmaxf(mx0, x);
         else mx1 = fmaxf(mx1, x);
       }
     mx0 = fmaxf(mx0, __shfl_xor(mx0, 16));
     mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
     mx1 = fmaxf(mx1, __shfl_xor(mx1, 16));
     mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
+    const float nb0 = -mx0 * sl2, nb1 = -mx1 * sl2;
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kl = cb * 16 + 4 * g + i;
-        if (kl < C) s0 += exp2f(acc[cb][i] - mx0);  // exp2(-inf) = 0
-        else s1 += exp2f(acc[cb][i] - mx1);
+        const bool first = CB0 ? (cb < CB0) : (kl < C);
+        if (first) s0 += exp2f(fmaf(acc[cb][i], sl2, nb0));  // exp2(-inf) = 0
+        else s1 += exp2f(fmaf(acc[cb][i], sl2, nb1));
       }
     s0 += __shfl_xor(s0, 16);
     s0 += __shfl_xor(s0, 32);
     s1 += __shfl_xor(s1, 16);
     s1 += __shfl_xor(s1, 32);
     constexpr float kLn2 = 0.6931471805599453f;
-    float u0 = (mx0 == -INFINITY) ? -INFINITY : (mx0 + __log2f(s0)) * kLn2;
-    float u1 = (mx1 == -INFINITY) ? -INFINITY : (mx1 + __log2f(s1)) * kLn2;
+    float u0 = (mx0 == -INFINITY) ? -INFINITY : mx0 * a.scale + __log2f(s0) * kLn2;
+    float u1 = (mx1 == -INFINITY) ? -INFINITY : mx1 * a.scale + __log2f(s1) * kLn2;
     // GQA sum over the G columns of the query
 #pragma unroll
     for (int o = 1; o < G; o <<= 1) {
@@ -282,12 +290,18 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
       return hipSuccess;
     };
     hipError_t e;
-    if (p.C <= 32)
-      e = run(leaf_score_kernel<T, D, G, 4>);
+    if (p.C == 32)
+      e = run(leaf_score_kernel<T, D, G, 4, 2>);
+    else if (p.C == 64)
+      e = run(leaf_score_kernel<T, D, G, 8, 4>);
+    else if (p.C == 128)
+      e = run(leaf_score_kernel<T, D, G, 16, 8>);
+    else if (p.C <= 32)
+      e = run(leaf_score_kernel<T, D, G, 4, 0>);
     else if (p.C <= 64)
-      e = run(leaf_score_kernel<T, D, G, 8>);
+      e = run(leaf_score_kernel<T, D, G, 8, 0>);
     else
-      e = run(leaf_score_kernel<T, D, G, 16>);
+      e = run(leaf_score_kernel<T, D, G, 16, 0>);
     if (e != hipSuccess) return e;
     return hipGetLastError();
   });

@@ -32,6 +32,7 @@ EXPORTS = [
     "pisa_pyramid_bytes", "pisa_levels", "pisa_level_rows", "pisa_level_offset", "pisa_build_pyramid",
     "pisa_select_workspace_bytes", "pisa_select", "pisa_attn_workspace_bytes", "pisa_sparse_attn",
     "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
+    "pisa_route_counts",
     "pisa_last_error", "pisa_version",
 ]
 
@@ -85,6 +86,7 @@ def load(path: str = LIB_PATH):
         "pisa_flat_select": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_decode_step": ([DP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "pisa_timer_enable": ([i32], None),
+        "pisa_route_counts": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_timer_report": ([ctypes.c_char_p, sz], i32),
         "pisa_last_error": ([], ctypes.c_char_p),
         "pisa_version": ([], ctypes.c_char_p),
@@ -341,6 +343,17 @@ def timer_report() -> dict:
         name, n, ms = line.split("\t")
         out[name] = (int(n), float(ms))
     return out
+
+
+def route_counts(p: Problem, q, k, pyr, ws=None, stream=None) -> dict:
+    """Work counters of the stage-1 routing kernel (diagnostic run)."""
+    counts = torch.zeros(5, dtype=torch.int64, device=q.device)
+    if ws is None:
+        ws = workspace(select_workspace_bytes(p), q.device)
+    _check(load().pisa_route_counts(ctypes.byref(p.c()), q.data_ptr(), k.data_ptr(), pyr.data_ptr(),
+                                    counts.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    c = counts.cpu().tolist()
+    return {"queries": c[0], "scored_candidates": c[1], "child_rows": c[2], "scored_levels": c[3], "kept_level2": c[4]}
 
 
 def default_scale(D: int) -> float:

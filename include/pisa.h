@@ -186,6 +186,16 @@ pisa_status pisa_decode_step(const pisa_decode_problem* p, void* k_cache, void* 
 void pisa_timer_enable(int32_t on);
 int32_t pisa_timer_report(char* buf, size_t cap);
 
+/* Work counters of the bf16 stage-1 routing kernel (the same kernel as
+ * pisa_select's stage 1, with counting enabled): adds to the device uint64
+ * counts[5] (caller-zeroed) the number of (query, KV head) routed, the
+ * candidates scored at levels >= 2, the valid child summary rows gathered,
+ * the levels scored, and the kept level-2 blocks.  ws: at least
+ * pisa_select_workspace_bytes(p) bytes (its first part receives the kept
+ * level-2 blocks).  For measurement only; not part of the hot path.          */
+pisa_status pisa_route_counts(const pisa_problem* p, const void* q, const void* k, const float* pyr,
+                              uint64_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* pisa_last_error(void);
 /* Library version string (static storage). */

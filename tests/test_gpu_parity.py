@@ -254,3 +254,17 @@ def test_decode_capacity_flag():
     assert int(err.item()) == 1
     assert int(length.item()) == cap
     assert torch.equal(before, kc)
+
+
+def test_route_counts():
+    """The stage-1 work counters count what the oracle's descent counts."""
+    c = case_data("bf16_g4_n4133")
+    w = c["w"]
+    p = _problem(w)
+    pyr = pisa.build_pyramid(p, c["dev"]["k"])
+    rc = pisa.route_counts(p, c["dev"]["q"], c["dev"]["k"], pyr)
+    _, _, _, cnt = oracle.select(_oproblem(w), c["data"]["q"], c["data"]["k"])
+    assert rc["queries"] == cnt["queries"]
+    # identical descents except on near-tied queries
+    assert abs(rc["scored_candidates"] - cnt["scored_blocks"]) <= 0.002 * cnt["scored_blocks"]
+    assert abs(rc["child_rows"] - cnt["child_dots"]) <= 0.002 * cnt["child_dots"]
