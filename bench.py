@@ -137,7 +137,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     w = I.workload(args.workload)
     if w.steps:
-        raise SystemExit("bench.py times prefill workloads; decode is measured by its own tests")
+        return decode_main(args, w)
     log(f"workload {w.name}: B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} C={w.C} K={w.K} {w.dtype} "
         f"causal={w.causal} needles={w.needles}")
     t0 = time.perf_counter()
@@ -364,6 +364,222 @@ def main() -> int:
         "roofline": roofline,
         "kernel_rooflines": kernel_rooflines,
         "route_work": rc,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def decode_bytes_model(n: int, C: int, K: int, D: int, G: int, esz: int) -> dict:
+    """Algorithmic HBM bytes of one fused decode step for one (sequence, KV
+    head) whose prefix holds n tokens after the append.  Candidate counts
+    follow the descent with every block valid (the new query sees the whole
+    prefix): one root candidate, at each level the children of the kept
+    blocks; a level with more than K candidates is scored.  Children counts
+    assume full sibling pairs, so they may exceed the kernel's by one row per
+    level at a ragged tail."""
+    rows = [-(-n // C)]
+    while rows[-1] > 1:
+        rows.append(-(-rows[-1] // 2))
+    L = len(rows)  # rows[l-1] = M_l
+    summary_rows = 0
+    a = 1
+    for l in range(L, 1, -1):
+        if a > K:
+            summary_rows += min(2 * a, rows[l - 2])
+        kept = min(a, K)
+        a = min(2 * kept, rows[l - 2])
+    leaf_keys = (a if a > K else 0) * C          # level-1 candidates scored on raw keys
+    kept_keys = min(a, K) * C
+    lo = (n - 1) // C * C
+    b = {
+        "q_o": 2 * G * D * esz,
+        "append": 2 * D * esz,
+        "leaf_mean": (n - 1 - lo) * D * esz,
+        "path": (L - 1) * D * 4 + L * (D * 4 + D * 2 + 4),
+        "summaries": summary_rows * D * 4,
+        "leaf_keys": max(leaf_keys, kept_keys) * D * esz,  # keys of the scored (or kept) leaves, read once
+        "values": kept_keys * D * esz,
+        "idx": 2 * K * 4,
+    }
+    b["total"] = sum(b.values())
+    b["levels"] = L
+    b["summary_rows"] = summary_rows
+    return b
+
+
+def decode_main(args, w) -> int:
+    """Fused decode: S sequences with an N-token cached prefix; one step
+    appends one token per sequence (k, v, leaf mean, ancestor path) and runs
+    selection + sparse attention for it in one kernel.  The timed region is
+    K consecutive steps starting from the N-token prefix."""
+    import numpy as np
+    import torch
+
+    from hierarchical_block_sparse_mean_amd import inputs as I
+    from hierarchical_block_sparse_mean_amd import pisa
+
+    if args.steps > w.steps or args.warmup > w.steps:
+        raise SystemExit(f"{w.name} has {w.steps} decode steps; asked for --steps {args.steps} --warmup {args.warmup}")
+    S, cap, G = w.B, w.N + w.steps, w.Hq // w.Hkv
+    log(f"workload {w.name}: S={S} sequences x N={w.N} cached tokens (+{w.steps} steps), Hq={w.Hq} Hkv={w.Hkv} "
+        f"D={w.D} C={w.C} K={w.K} {w.dtype}")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    kc = torch.zeros((S, w.Hkv, cap, w.D), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    t0 = time.perf_counter()
+    for s in range(S):
+        kh, vh = I.decode_prefix(w, s)
+        kc[s, :, : w.N].copy_(dev(kh))
+        vc[s, :, : w.N].copy_(dev(vh))
+        if s % 16 == 15:
+            log(f"cache: {s + 1}/{S} sequences generated and uploaded ({time.perf_counter() - t0:.1f}s)")
+    del kh, vh
+    toks = [I.decode_token(w, st) for st in range(w.steps)]
+    tq = dev(np.stack([t["q"] for t in toks]))
+    tk = dev(np.stack([t["k"] for t in toks]))
+    tv = dev(np.stack([t["v"] for t in toks]))
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
+
+    dp = pisa.DecodeProblem(S, cap, w.Hq, w.Hkv, w.D, w.C, w.K, dtype=w.dtype)
+    pp = dp.prefill_problem(w.N)
+    pyr = pisa.alloc_pyramid(pp)
+    length = torch.empty((S,), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o_all = torch.empty((w.steps, S, w.Hq, w.D), dtype=dt, device="cuda")
+    idx_all = torch.empty((w.steps, S, w.Hkv, w.K), dtype=torch.int32, device="cuda")
+    score_all = torch.empty((w.steps, S, w.Hkv, w.K), dtype=torch.float32, device="cuda")
+
+    def reset():
+        length.fill_(w.N)
+        pisa.build_pyramid(pp, kc, pyr)
+
+    def step(i):
+        pisa.decode_step(dp, kc, vc, pyr, length, tq[i], tk[i], tv[i], o=o_all[i], idx=idx_all[i],
+                         score=score_all[i], err=err)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reset()
+    e1.record()
+    torch.cuda.synchronize()
+    pyr_ms = e0.elapsed_time(e1)
+    log(f"prefix pyramid built in {pyr_ms:.3f} ms")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; cache length and pyramid reset to the prefix")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    pisa.timer_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kernels = pisa.timer_report()
+    pisa.timer_enable(False)
+    if int(err.item()) != 0:
+        raise SystemExit("decode reported a full cache")
+    lat = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1000.0 / args.steps
+    value = S * args.steps / wall
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (events: median {np.median(lat):.4f} ms, "
+        f"p99 {np.percentile(lat, 99):.4f} ms)")
+    per_kernel = {kk: {"launches": vv[0], "avg_ms": vv[1] / max(1, vv[0])} for kk, vv in kernels.items()}
+
+    # roofline of the fused decode kernel, on the modelled bytes of each step
+    esz = 2 if w.dtype == "bf16" else 4
+    per_launch = 0
+    for i in range(args.steps):
+        per_launch += decode_bytes_model(w.N + i + 1, w.C, w.K, w.D, G, esz)["total"] * S * w.Hkv
+    per_launch /= args.steps
+    mid = decode_bytes_model(w.N + 1, w.C, w.K, w.D, G, esz)
+    dk = per_kernel.get("decode")
+    roofline = None
+    if dk:
+        ach = per_launch / (dk["avg_ms"] * 1e-3) / 1e9
+        roofline = {"kernel": "decode", "bound": "hbm", "achieved": round(ach, 2), "peak": PEAK["hbm_GBps"],
+                    "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 5), "traffic": None,
+                    "avg_launch_ms": round(dk["avg_ms"], 5), "work_per_launch": round(per_launch, 1),
+                    "work_note": f"modelled bytes per (sequence, KV head) at n={w.N + 1}: {mid}"}
+
+    # CPU oracle on a few sequences at the first and last timed step, with parity
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        seqs = [0, S // 3, (2 * S) // 3, S - 1][: max(1, min(4, S))]
+        checks = sorted({0, args.steps - 1})
+        g_idx = idx_all.cpu().numpy()
+        g_score = score_all.cpu().numpy().astype(np.float64)
+        g_o = o_all.float().cpu().numpy().astype(np.float64)
+        t_cpu, n_tok = 0.0, 0
+        nonex = mism = total = 0
+        exempt_n = 0
+        serr = aerr = 0.0
+        for s in seqs:
+            kh, vh = I.decode_prefix(w, s)
+            for st in checks:
+                n = w.N + st + 1
+                kp = np.empty((1, w.Hkv, n, w.D), kh.dtype)
+                vp = np.empty_like(kp)
+                kp[0, :, : w.N], vp[0, :, : w.N] = kh, vh
+                for j in range(st + 1):
+                    kp[0, :, w.N + j], vp[0, :, w.N + j] = toks[j]["k"][s], toks[j]["v"][s]
+                ta = time.perf_counter()
+                r_idx, r_score, r_gap, r_o, _ = oracle.decode_reference(
+                    oracle.Problem(1, n, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True), toks[st]["q"][s:s + 1], kp, vp)
+                t_cpu += time.perf_counter() - ta
+                n_tok += 1
+                same = (g_idx[st, s] == r_idx[0]).all(-1)
+                exempt = r_gap[0] < 1e-3
+                total += same.size
+                mism += int((~same).sum())
+                nonex += int((~same & ~exempt).sum())
+                exempt_n += int(exempt.sum())
+                m = same[:, None] & (r_idx[0] >= 0)
+                if m.any():
+                    serr = max(serr, float((np.abs(g_score[st, s][m] - r_score[0][m]) /
+                                            np.maximum(1.0, np.abs(r_score[0][m]))).max()))
+                okh = np.repeat(same, G)
+                if okh.any():
+                    aerr = max(aerr, float(np.abs(g_o[st, s] - r_o[0]).max(-1)[okh].max()))
+        cpu = {"value": round(n_tok / t_cpu, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"{n_tok} decode tokens: sequences {seqs} at steps {checks}; the oracle rebuilds the "
+                         f"prefix pyramid per (sequence, KV head) then selects and attends, fp64, {t_cpu:.1f}s wall"}
+        parity = {"tokens": n_tok, "heads": total, "non_exempt_mismatches": nonex, "exempt": exempt_n,
+                  "exact_match_rate": round(1.0 - mism / max(1, total), 5), "max_score_rel_err": serr,
+                  "max_attn_abs_err": aerr}
+        log(f"parity on sample: {parity}")
+
+    line = {
+        "metric": "PISA fused decode tokens/s (selection + sparse attention per new token), 1 GPU",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "S": S, "N": w.N, "decode_steps": w.steps, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "d": w.D, "C": w.C, "g": 2, "K": w.K},
+        "step_latency_ms": {"median": round(float(np.median(lat)), 5), "p99": round(float(np.percentile(lat, 99)), 5),
+                            "min": round(float(lat.min()), 5), "max": round(float(lat.max()), 5)},
+        "prefix_pyramid_ms": round(pyr_ms, 4),
+        "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 5), "launches_per_step": vv["launches"] / args.steps}
+                    for kk, vv in per_kernel.items()},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -268,12 +268,23 @@ def decode_cache(w: Workload, seqs=None) -> dict:
     return {"k": k, "v": v, "cap": cap, "seqs": seqs}
 
 
+def decode_prefix(w: Workload, s: int) -> tuple[np.ndarray, np.ndarray]:
+    """Cached prefix k, v [Hkv][N][D] of decode sequence ``s`` alone (the
+    same values decode_cache places in row s)."""
+    per_seq = w.Hkv * w.N * w.D
+    k = _tensor(w.seed, STREAM_K, (w.Hkv, w.N, w.D), w.dtype, start=s * per_seq)
+    v = _tensor(w.seed, STREAM_V, (w.Hkv, w.N, w.D), w.dtype, start=s * per_seq)
+    return k, v
+
+
 def decode_token(w: Workload, step: int, seqs=None) -> dict:
     """New q [S][Hq][D], k, v [S][Hkv][D] of decode step ``step``."""
-    seqs = list(range(w.B)) if seqs is None else list(seqs)
     out = {}
     for name, stream, H in (("q", STREAM_DEC_Q, w.Hq), ("k", STREAM_DEC_K, w.Hkv), ("v", STREAM_DEC_V, w.Hkv)):
         per = H * w.D
-        rows = [_tensor(w.seed, stream, (H, w.D), w.dtype, start=(step * w.B + s) * per) for s in seqs]
-        out[name] = np.stack(rows)
+        if seqs is None:  # all sequences of a step are one contiguous element range
+            out[name] = _tensor(w.seed, stream, (w.B, H, w.D), w.dtype, start=step * w.B * per)
+        else:
+            rows = [_tensor(w.seed, stream, (H, w.D), w.dtype, start=(step * w.B + s) * per) for s in seqs]
+            out[name] = np.stack(rows)
     return out

@@ -1,0 +1,144 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (default schedules, whole problem in one call), checked on
+sampled query positions the oracle computes one by one:
+
+* prefill N=131072 (C=64, K=16, planted needle leaves) and N=262144 (C=128,
+  K=32, shared needle spans): selection, reported scores, attention fed by
+  the GPU's own selection, and the flat selector;
+* decode: 64 sequences x 131072 cached tokens, the first two fused steps,
+  on a few sequences, plus the incrementally updated pyramid rows of those
+  sequences against a rebuild.
+
+Positions include the first and last leaves and the ragged edges of the
+causal frontier."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import ATTN_TOL, SCORE_RTOL, check_selection, log, to_dev, to_host_f64
+from hierarchical_block_sparse_mean_amd import inputs as I
+from hierarchical_block_sparse_mean_amd import pisa
+
+pytestmark = pytest.mark.gpu
+
+
+def _positions(w: I.Workload, n_mid: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    edge = np.concatenate([np.arange(0, 3), np.arange(w.C - 2, w.C + 2), np.arange(w.N - 3, w.N)])
+    mid = rng.integers(w.C, w.N, n_mid)
+    return np.unique(np.concatenate([edge, mid]))
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,n_mid", [("prefill_128k", 384), ("prefill_256k", 192)])
+def test_prefill_fullsize_sampled(name, n_mid):
+    w = I.WORKLOADS[name]
+    log(f"[fullsize {name}] generating inputs")
+    data = I.generate(w)
+    q, k, v = (to_dev(data[x]) for x in ("q", "k", "v"))
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype)
+    log(f"[fullsize {name}] GPU pyramid + select + attention + flat")
+    pyr = pisa.build_pyramid(p, k)
+    idx, score = pisa.select(p, q, k, pyr)
+    o, lse = pisa.sparse_attn(p, q, k, v, idx)
+    f_idx, f_score = pisa.flat_select(p, q, pyr)
+    torch.cuda.synchronize()
+    ts = _positions(w, n_mid, w.seed + 7)
+    log(f"[fullsize {name}] oracle on {len(ts)} positions")
+    op = oracle.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal)
+    r_idx, r_score, r_gap, _ = oracle.select(op, data["q"], data["k"], ts=ts)
+    g_idx = idx.cpu().numpy()[:, :, ts]
+    g_score = score.cpu().numpy()[:, :, ts]
+    ex, rate = check_selection(g_idx, g_score, r_idx, r_score, r_gap, name)
+    log(f"  exempt fraction {ex:.4f}, exact-match rate {rate:.4f}")
+    assert rate > 0.97
+    # attention over the GPU's own selection, where it equals the oracle's
+    r_o, r_lse = oracle.attention(op, data["q"], data["k"], data["v"], r_idx, ts=ts)
+    same = np.repeat((g_idx == r_idx).all(-1), w.Hq // w.Hkv, axis=1)
+    got = to_host_f64(o)[:, :, ts]
+    err = np.abs(got - r_o).max(-1)[same].max()
+    assert err <= ATTN_TOL[w.dtype], err
+    lse_err = np.abs(lse.cpu().numpy()[:, :, ts].astype(np.float64) - r_lse)[same].max()
+    assert lse_err <= 1e-4 * max(1.0, np.abs(r_lse).max()), lse_err
+    log(f"  attention max-abs err {err:.3g}, lse err {lse_err:.3g}")
+    # flat selector: identical sets, or near-tied ones whose sorted scores agree
+    rf_idx, rf_score = oracle.flat_select(op, data["q"], data["k"], ts=ts)
+    gf_idx = f_idx.cpu().numpy()[:, :, ts]
+    gf_score = f_score.cpu().numpy()[:, :, ts].astype(np.float64)
+    fsame = (gf_idx == rf_idx).all(-1)
+    assert fsame.mean() > 0.9, fsame.mean()
+    for at in np.argwhere(~fsame):
+        at = tuple(at)
+        a = np.sort(gf_score[at][gf_idx[at] >= 0])
+        b = np.sort(rf_score[at][rf_idx[at] >= 0])
+        assert a.shape == b.shape and np.abs(a - b).max() < 1e-3, (at, gf_idx[at], rf_idx[at])
+    m = fsame[..., None] & (rf_idx >= 0)
+    ferr = np.abs(gf_score[m] - rf_score[m])
+    assert (ferr <= SCORE_RTOL * np.maximum(1, np.abs(rf_score[m]))).all(), ferr.max()
+    log(f"  flat exact-match rate {fsame.mean():.4f}")
+
+
+@pytest.mark.timeout(600)
+def test_decode_fullsize_sampled():
+    w = I.WORKLOADS["decode_128k"]
+    S, cap, G = w.B, w.N + w.steps, w.Hq // w.Hkv
+    steps = 2
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log(f"[fullsize decode] {S} sequences x {w.N} tokens: generating the cache")
+    kc = torch.zeros((S, w.Hkv, cap, w.D), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    for s in range(S):
+        kh, vh = I.decode_prefix(w, s)
+        kc[s, :, : w.N].copy_(to_dev(kh))
+        vc[s, :, : w.N].copy_(to_dev(vh))
+        if s % 16 == 15:
+            log(f"  {s + 1}/{S} sequences uploaded")
+    dp = pisa.DecodeProblem(S, cap, w.Hq, w.Hkv, w.D, w.C, w.K, dtype=w.dtype)
+    pp = dp.prefill_problem(w.N)
+    pyr = pisa.build_pyramid(pp, kc, pisa.alloc_pyramid(pp))
+    length = torch.full((S,), w.N, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    toks = [I.decode_token(w, st) for st in range(steps)]
+    outs = []
+    for st in range(steps):
+        idx = torch.empty((S, w.Hkv, w.K), dtype=torch.int32, device="cuda")
+        score = torch.empty((S, w.Hkv, w.K), dtype=torch.float32, device="cuda")
+        o, _, _ = pisa.decode_step(dp, kc, vc, pyr, length, to_dev(toks[st]["q"]), to_dev(toks[st]["k"]),
+                                   to_dev(toks[st]["v"]), idx=idx, score=score, err=err)
+        outs.append((idx, score, o))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert (length.cpu().numpy() == w.N + steps).all()
+    n_final = w.N + steps
+    pr = dp.prefill_problem(n_final)
+    rebuilt = pisa.build_pyramid(pr, kc, pisa.alloc_pyramid(pr))
+    torch.cuda.synchronize()
+    for s in (0, S // 2, S - 1):
+        log(f"[fullsize decode] oracle on sequence {s}")
+        kh, vh = I.decode_prefix(w, s)
+        kp = np.zeros((1, w.Hkv, n_final, w.D), kh.dtype)
+        vp = np.zeros_like(kp)
+        kp[0, :, : w.N], vp[0, :, : w.N] = kh, vh
+        for st in range(steps):
+            kp[0, :, w.N + st], vp[0, :, w.N + st] = toks[st]["k"][s], toks[st]["v"][s]
+        for st in range(steps):
+            n = w.N + st + 1
+            r_idx, r_score, r_gap, r_o, _ = oracle.decode_reference(
+                oracle.Problem(1, n, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True), toks[st]["q"][s:s + 1],
+                np.ascontiguousarray(kp[:, :, :n]), np.ascontiguousarray(vp[:, :, :n]))
+            idx, score, o = outs[st]
+            g_idx = idx.cpu().numpy()[s:s + 1]
+            check_selection(g_idx[:, :, None], score.cpu().numpy()[s:s + 1, :, None], r_idx[:, :, None],
+                            r_score[:, :, None], r_gap[:, :, None], f"decode seq {s} step {st}")
+            same = np.repeat((g_idx == r_idx).all(-1), G, axis=1)
+            got = to_host_f64(o)[s:s + 1]
+            if same.any():
+                assert np.abs(got - r_o).max(-1)[same].max() <= ATTN_TOL[w.dtype]
+        # the incrementally updated pyramid of this sequence equals a rebuild
+        for l in range(1, pisa.levels(n_final, w.C) + 1):
+            a = to_host_f64(pisa.pyramid_level(pr, pyr, l, n_final)[s])
+            b = to_host_f64(pisa.pyramid_level(pr, rebuilt, l, n_final)[s])
+            assert np.abs(a - b).max() <= 1e-6 * max(1.0, np.abs(b).max()), f"seq {s} level {l}"
