@@ -5,13 +5,21 @@
 // to the leaves, scoring raw key blocks directly).  Attention over the kept
 // leaves runs in the same program.
 //
-// One wave per (sequence, KV head).  The new token's k/v rows are appended to
-// the caches; the current leaf's mean is recomputed from its raw keys (so the
-// cached pyramid stays equal to a rebuild over the prefix), then each
-// ancestor on the path is recomputed from its children.
-#include "attend.h"
+// One workgroup of NW waves per (sequence, KV head):
+//   1. append k, v at row n; the current leaf's mean from its raw keys (rows
+//      summed across the waves), then each ancestor on the path from its
+//      children (sibling rows fetched by all waves at once), so the cached
+//      pyramid stays equal to a rebuild over the prefix;
+//   2. the descent for the new query (t = n, every block valid): the child
+//      rows of a scored level are spread over all waves, 8 lanes per fp32
+//      row; wave 0 keeps the top K and expands them;
+//   3. leaf level: each candidate leaf's C raw keys against the G_Q query
+//      heads on MFMA (keys as rows, heads as columns), its per-head max and
+//      log-sum-exp kept in LDS; wave 0 keeps the final top K;
+//   4. attention: the per-head max and denominator over the kept leaves come
+//      from those LDS values, so every wave's partial output over its leaves
+//      is already on the common scale; partials add through LDS.
 #include "kernels.h"
-#include "route.h"
 
 namespace pisa {
 
@@ -35,106 +43,395 @@ struct DecodeKArgs {
   PyrGeom geo;
 };
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kWave) void decode_kernel(DecodeKArgs a) {
-  __shared__ float s_q[G * D];
-  __shared__ RouteLds s_r;
-  __shared__ AttendLds<D, G> s_a;
-  constexpr int DPL = D / kWave;
+constexpr int kDecMaxCand = 64;  // 2K, K <= 32
+
+// Raw dot products of the keys [lo, hi) of one leaf with the G query heads:
+// S^T tile kb holds keys lo + 16kb + 4(lane/16) + i (i = 0..3) in column
+// lane % 16 = head.  Row newpos is read from knew (the appended token).
+template <typename T, int D, int NKB>
+__device__ __forceinline__ void leaf_dots(const Frag<T>* fq, const T* kbase, const T* knew, int64_t newpos, int64_t lo,
+                                          int64_t hi, floatx4* acc) {
+  constexpr int NS = D / 32;
   const int lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int64_t r = lo + kb * 16 + col;
+    const T* row = (r == newpos) ? knew : kbase + r * D;
+    Frag<T> fk[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (r < hi) fk[s].load(row + g * (D / 4) + 8 * s);
+      else fk[s].zero();
+    }
+    acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[kb] = mma(fk[s], fq[s], acc[kb]);
+  }
+}
+
+template <typename T, int D, int G, int NW, int NKB>
+__global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
+  constexpr int DPL = D / kWave;  // dims per lane in whole-row work
+  constexpr int NS = D / 32;
+  constexpr int CP = NKB * 16;    // keys per leaf tile
+  constexpr int LPR = D / 8;      // lanes per V row in the PV product
+  constexpr int RPI = kWave / LPR;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __align__(16) float s_q[G * D];
+  __shared__ int32_t s_cand[kDecMaxCand];
+  __shared__ float s_score[kDecMaxCand];
+  __shared__ float s_lm[kDecMaxCand][G];  // per candidate leaf and head: max logit
+  __shared__ float s_ll[kDecMaxCand][G];  // and log-sum-exp
+  __shared__ int32_t s_sel[32], s_slot[32];
+  __shared__ float s_M[G], s_L[G];
+  __shared__ int32_t s_state[2];  // level, candidate count
+  __shared__ __align__(16) float s_p[NW][CP][G];
+  constexpr int kUpdFloats = NW * D + (kMaxLevels + 1) * D;  // leaf-mean partials + sibling rows
+  constexpr int kOutFloats = NW * G * D;                     // partial outputs
+  __shared__ __align__(16) float s_u[kUpdFloats > kOutFloats ? kUpdFloats : kOutFloats];
+  float* s_mean = s_u;           // [NW][D]
+  float* s_sib = s_u + NW * D;   // [level][D]
+  float* s_o = s_u;              // [NW][G][D], after the update phase
+
+  const int w = threadIdx.x / kWave, lane = lane_id();
   const int64_t bid = blockIdx.x;
   const int h = (int)(bid % a.Hkv);
   const int s = (int)(bid / a.Hkv);
   const int64_t n = a.len[s];
-  if (n < 0 || n >= a.cap) {
-    if (lane == 0 && a.err != nullptr) a.err[0] = 1;
+  if (n < 0 || n >= a.cap) {  // uniform over the workgroup
+    if (threadIdx.x == 0 && a.err != nullptr) a.err[0] = 1;
     return;
   }
   const int64_t n1 = n + 1;
+  const int C = a.C, K = a.K;
   const int64_t sh = (int64_t)s * a.Hkv + h;
   T* kbase = static_cast<T*>(a.k_cache) + sh * a.cap * D;
   T* vbase = static_cast<T*>(a.v_cache) + sh * a.cap * D;
   const T* knew = static_cast<const T*>(a.k_new) + sh * D;
   const T* vnew = static_cast<const T*>(a.v_new) + sh * D;
+  const T* qn = static_cast<const T*>(a.q_new) + ((int64_t)s * a.Hq + h * G) * D;
   float* pbase = a.pyr + sh * a.geo.rows * D;
   _Float16* hbase = a.f16 + sh * a.geo.rows * D;
   int32_t* xbase = a.ex + sh * a.geo.rows;
-  // writes summary row `row` (this lane's DPL dims in v) and its fp16 copy
-  auto put_row = [&](int64_t row, const float* v) {
-    float mx = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      pbase[row * D + lane * DPL + e] = v[e];
-      mx = fmaxf(mx, fabsf(v[e]));
-    }
-    const int ex = row_exponent(wave_max(mx));
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) hbase[row * D + lane * DPL + e] = to_f16_scaled(v[e], ex);
-    if (lane == 0) xbase[row] = ex;
-  };
 
-  // 1. append k, v at row n
-  for (int d = lane; d < D; d += kWave) {
-    kbase[n * D + d] = knew[d];
-    vbase[n * D + d] = vnew[d];
-  }
-  // 2. leaf mean of leaf n / C over its raw keys (the new key read from k_new)
-  const int64_t j = n / a.C;
-  const int64_t lo = j * a.C;
-  const float cnt = (float)(n1 - lo);
-  float cur[DPL];
+  // ---- 1. append, leaf mean, ancestor path ---------------------------------
+  const int64_t j_leaf = n / C;
+  const int64_t lo_leaf = j_leaf * C;
+  const int32_t L1 = num_levels(n1, C);
+  if (w == 0)
+    for (int d = lane; d < D; d += kWave) {
+      kbase[n * D + d] = knew[d];
+      vbase[n * D + d] = vnew[d];
+    }
+  for (int i = threadIdx.x; i < G * D; i += NW * kWave) s_q[i] = load1<T>(qn + i);
   {
     float acc[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    for (int64_t i = lo; i < n; ++i) {
+    for (int64_t i = lo_leaf + w; i < n; i += NW) {
       float v[DPL];
-      load_dims<T, DPL>(kbase + i * D + lane * DPL, v);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) v[e] = load1<T>(kbase + i * D + lane * DPL + e);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] += v[e];
     }
-    float v[DPL];
-    load_dims<T, DPL>(knew + lane * DPL, v);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) cur[e] = (acc[e] + v[e]) / cnt;
-    put_row(a.geo.level_off[1] + j, cur);
-  }
-  // 3. ancestors: node j >> (l-1) of level l is the mean of its existing children
-  const int32_t L1 = num_levels(n1, a.C);
-  int64_t node = j;
-  for (int32_t l = 2; l <= L1; ++l) {
-    const int64_t sib = node ^ 1;
-    const int64_t m_child = level_rows(n1, a.C, l - 1);
-    const float* child_level = pbase + a.geo.level_off[l - 1] * D;
-    if (sib < m_child) {
+    for (int e = 0; e < DPL; ++e) s_mean[w * D + lane * DPL + e] = acc[e];
+    // sibling of the path node at level l - 1, for l = 2 .. L1
+    for (int32_t l = 2 + w; l <= L1; l += NW) {
+      const int64_t node = j_leaf >> (l - 2);
+      const int64_t sib = node ^ 1;
+      if (sib < level_rows(n1, C, l - 1)) {
+        const float* row = pbase + (a.geo.level_off[l - 1] + sib) * D;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const float o = child_level[sib * D + lane * DPL + e];
-        cur[e] = (node & 1) ? (o + cur[e]) * 0.5f : (cur[e] + o) * 0.5f;
+        for (int e = 0; e < DPL; ++e) s_sib[l * D + lane * DPL + e] = row[lane * DPL + e];
       }
     }
-    node >>= 1;
-    put_row(a.geo.level_off[l] + node, cur);
   }
-  __threadfence();  // the path rows are read back below by this wave
+  __syncthreads();
+  if (w == 0) {
+    // writes summary row `row` (this lane's DPL dims in v) and its fp16 copy
+    auto put_row = [&](int64_t row, const float* v) {
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        pbase[row * D + lane * DPL + e] = v[e];
+        mx = fmaxf(mx, fabsf(v[e]));
+      }
+      const int ex = row_exponent(wave_max(mx));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) hbase[row * D + lane * DPL + e] = to_f16_scaled(v[e], ex);
+      if (lane == 0) xbase[row] = ex;
+    };
+    const float cnt = (float)(n1 - lo_leaf);
+    float cur[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      float acc = 0.f;
+      for (int ww = 0; ww < NW; ++ww) acc += s_mean[ww * D + lane * DPL + e];
+      cur[e] = (acc + load1<T>(knew + lane * DPL + e)) / cnt;
+    }
+    put_row(a.geo.level_off[1] + j_leaf, cur);
+    int64_t node = j_leaf;
+    for (int32_t l = 2; l <= L1; ++l) {
+      if ((node ^ 1) < level_rows(n1, C, l - 1)) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) cur[e] = (cur[e] + s_sib[l * D + lane * DPL + e]) * 0.5f;
+      }
+      node >>= 1;
+      put_row(a.geo.level_off[l] + node, cur);
+    }
+  }
+  __threadfence();  // the path rows are read below by every wave
+  __syncthreads();
 
-  // 4. fused selection for the new query at t = n (every block is valid)
-  const T* qn = static_cast<const T*>(a.q_new) + ((int64_t)s * a.Hq + h * G) * D;
-  for (int i = lane; i < G * D; i += kWave) s_q[i] = load1<T>(qn + i);
-  wave_sync();
-  int32_t out_idx;
-  float out_score;
-  route_query<T, D, G>(s_r, s_q, kbase, pbase, a.geo, n1, n, true, a.C, a.K, L1, 1, a.scale, knew, n, out_idx,
-                       out_score);
-  if (lane < a.K) {
-    if (a.idx) a.idx[sh * a.K + lane] = out_idx;
-    if (a.score) a.score[sh * a.K + lane] = out_score;
-    s_a.sel[lane] = out_idx;
+  // ---- 2. descent, levels L1 .. 2 ----------------------------------------
+  // wave 0: drop candidates beyond the level's rows (every block starts at or
+  // before t = n), compacting the list; returns the new count
+  auto compact = [&](int nA, int64_t ml) -> int {
+    const int32_t j = lane < nA ? s_cand[lane] : -1;
+    const bool valid = j >= 0 && j < ml;
+    const uint64_t mask = __ballot(valid);
+    const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+    wave_sync();
+    if (valid) s_cand[pos] = j;
+    wave_sync();
+    return __popcll(mask);
+  };
+  // wave 0: replace the first nI candidates (in lanes' `kept`) by their children
+  auto expand = [&](int32_t kept, int nI) {
+    wave_sync();
+    if (lane < nI) {
+      s_cand[2 * lane] = 2 * kept;
+      s_cand[2 * lane + 1] = 2 * kept + 1;
+    }
+    wave_sync();
+  };
+  if (w == 0) {
+    int l = L1, nA = 1;
+    if (lane == 0) s_cand[0] = 0;
+    wave_sync();
+    // levels with at most K candidates keep them all unscored
+    while (l >= 2 && nA <= K) {
+      const int32_t kept = lane < nA ? s_cand[lane] : -1;
+      expand(kept, nA);
+      --l;
+      nA = compact(2 * nA, level_rows(n1, C, l));
+    }
+    if (lane == 0) {
+      s_state[0] = l;
+      s_state[1] = nA;
+    }
   }
-  wave_sync();
-  // 5. attention of the G query heads over the kept leaves
+  __syncthreads();
+  for (;;) {
+    const int l = s_state[0], nA = s_state[1];
+    if (l < 2) break;
+    // score the nA > K candidates of level l by their children at level l - 1
+    {
+      const int64_t m_child = level_rows(n1, C, l - 1);
+      const float* child_level = pbase + a.geo.level_off[l - 1] * D;
+      constexpr int DL = D / 8;  // dims per lane, 8 lanes per row
+      const int sub = lane & 7;
+      for (int base = 0; base < 2 * nA; base += NW * 8) {
+        const int rr = base + w * 8 + (lane >> 3);
+        const int i = rr >> 1;
+        const int64_t r = (i < nA) ? 2 * (int64_t)s_cand[i] + (rr & 1) : -1;
+        const bool valid = i < nA && r < m_child;
+        float dot[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) dot[g] = 0.f;
+        if (valid) {
+          const float* row = child_level + r * D + sub * DL;
+          float rv[DL];
+#pragma unroll
+          for (int e = 0; e < DL; e += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(row + e);
+            rv[e] = x.x;
+            rv[e + 1] = x.y;
+            rv[e + 2] = x.z;
+            rv[e + 3] = x.w;
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < DL; e += 4) {
+              const float4 qv = *reinterpret_cast<const float4*>(s_q + g * D + sub * DL + e);
+              dot[g] = fmaf(rv[e], qv.x, dot[g]);
+              dot[g] = fmaf(rv[e + 1], qv.y, dot[g]);
+              dot[g] = fmaf(rv[e + 2], qv.z, dot[g]);
+              dot[g] = fmaf(rv[e + 3], qv.w, dot[g]);
+            }
+        }
+        float u = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float x = valid ? group_sum<8>(dot[g]) * a.scale : -INFINITY;
+          u += lse2(x, __shfl_xor(x, 8));  // the sibling child sits 8 lanes away
+        }
+        if ((lane & 15) == 0 && i < nA) s_score[i] = u;
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      uint64_t key = (lane < nA) ? score_key(s_score[lane], s_cand[lane]) : 0ull;
+      key = wave_sort_desc(key);
+      int nI = nA < K ? nA : K;
+      int32_t kept = (lane < nI) ? key_index(key) : -1;
+      int ll = l, na = nI;
+      expand(kept, na);
+      --ll;
+      na = compact(2 * na, level_rows(n1, C, ll));
+      while (ll >= 2 && na <= K) {
+        kept = lane < na ? s_cand[lane] : -1;
+        expand(kept, na);
+        --ll;
+        na = compact(2 * na, level_rows(n1, C, ll));
+      }
+      if (lane == 0) {
+        s_state[0] = ll;
+        s_state[1] = na;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- 3. leaf level: raw-key log-sum-exp per candidate leaf ----------------
+  const int nA = s_state[1];
+  const int g4 = lane >> 4, col = lane & 15;
+  Frag<T> fq[NS];  // B operand: column col = query head col of the group
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (col < G) fq[st].load(qn + col * D + g4 * (D / 4) + 8 * st);
+    else fq[st].zero();
+  }
+  const float sl2 = a.scale * kLog2e;
+  for (int i = w; i < nA; i += NW) {
+    const int64_t lo = (int64_t)s_cand[i] * C;
+    const int64_t hi = lo + C < n1 ? lo + C : n1;
+    floatx4 acc[NKB];
+    leaf_dots<T, D, NKB>(fq, kbase, knew, n, lo, hi, acc);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = lo + kb * 16 + 4 * g4 + e < hi;
+        acc[kb][e] = ok ? acc[kb][e] : -INFINITY;
+        mx = fmaxf(mx, acc[kb][e]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum += exp2f((acc[kb][e] - mx) * sl2);  // exp2(-inf) = 0
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    const float m_nat = mx * a.scale;
+    const float lse = m_nat + __logf(sum);
+    if (g4 == 0 && col < G) {
+      s_lm[i][col] = m_nat;
+      s_ll[i][col] = lse;
+    }
+    const float u = group_sum<16>((g4 == 0 && col < G) ? lse : 0.f);
+    if (lane == 0) s_score[i] = u;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint64_t key = (lane < nA) ? score_key(s_score[lane], s_cand[lane]) : 0ull;
+    key = wave_sort_desc(key);
+    const int nI = nA < K ? nA : K;
+    const int32_t kept = (lane < nI) ? key_index(key) : -1;
+    const float kept_score = (lane < nI) ? key_score(key) : -INFINITY;
+    uint64_t k2 = (lane < nI) ? index_key(kept, kept_score) : 0ull;
+    k2 = wave_sort_desc(k2);
+    const int32_t out_idx = (lane < nI) ? index_key_index(k2) : -1;
+    const float out_score = (lane < nI) ? index_key_score(k2) : -INFINITY;
+    if (lane < K) {
+      if (a.idx) a.idx[sh * K + lane] = out_idx;
+      if (a.score) a.score[sh * K + lane] = out_score;
+    }
+    if (lane < nI) {
+      int slot = 0;
+      for (int c = 0; c < nA; ++c)
+        if (s_cand[c] == out_idx) slot = c;
+      s_sel[lane] = out_idx;
+      s_slot[lane] = slot;
+    }
+    wave_sync();
+    if (lane < G) {
+      float M = -INFINITY;
+      for (int c = 0; c < nI; ++c) M = fmaxf(M, s_lm[s_slot[c]][lane]);
+      float L = 0.f;
+      for (int c = 0; c < nI; ++c) L += __expf(s_ll[s_slot[c]][lane] - M);
+      s_M[lane] = M;
+      s_L[lane] = L;
+    }
+    if (lane == 0) s_state[1] = nI;
+  }
+  __syncthreads();
+
+  // ---- 4. attention over the kept leaves -----------------------------------
+  const int nI = s_state[1];
+  const float mcol = col < G ? s_M[col] * kLog2e : 0.f;
+  const int rg = lane / LPR, dl = (lane % LPR) * 8;
+  float acc_o[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc_o[g][e] = 0.f;
+  for (int c = w; c < nI; c += NW) {
+    const int64_t lo = (int64_t)s_sel[c] * C;
+    const int64_t hi = lo + C < n1 ? lo + C : n1;
+    floatx4 acc[NKB];
+    leaf_dots<T, D, NKB>(fq, kbase, knew, n, lo, hi, acc);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kb * 16 + 4 * g4 + e;
+        const float p = (lo + key < hi) ? exp2f(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
+        if (col < G) s_p[w][key][col] = p;
+      }
+    wave_sync();
+    const int nk = (int)(hi - lo);
+#pragma unroll 4
+    for (int kk = rg; kk < nk; kk += RPI) {
+      const int64_t r = lo + kk;
+      float v8[8];
+      load8<T>((r == n ? vnew : vbase + r * D) + dl, v8);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pg = s_p[w][kk][g];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc_o[g][e] = fmaf(pg, v8[e], acc_o[g][e]);
+      }
+    }
+    wave_sync();
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int o = LPR; o < kWave; o <<= 1) acc_o[g][e] += __shfl_xor(acc_o[g][e], o);
+  if (rg == 0)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[(w * G + g) * D + dl + e] = acc_o[g][e];
+  __syncthreads();
   T* out = static_cast<T*>(a.o) + ((int64_t)s * a.Hq + h * G) * D;
-  attend_query<T, D, G>(s_a, a.K, s_q, kbase, vbase, n1, n, true, a.C, a.scale, knew, vnew, n, out, D, nullptr, 0);
+  for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+    const int g = i / D;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += s_o[ww * G * D + i];
+    store1<T>(out + i, s_L[g] > 0.f ? v / s_L[g] : 0.f);
+  }
 }
 
 __global__ void decode_bump_kernel(int32_t* len, int32_t S, int64_t cap) {
@@ -145,16 +442,23 @@ __global__ void decode_bump_kernel(int32_t* len, int32_t S, int64_t cap) {
 hipError_t launch_decode(const DecodeArgs& d, void* k_cache, void* v_cache, float* pyr, int32_t* len,
                          const void* q_new, const void* k_new, const void* v_new, void* o, int32_t* idx,
                          float* score, int32_t* err, hipStream_t stream) {
+  if (d.K > 32 || d.C > 128) return hipErrorInvalidValue;
   const int64_t plane = (int64_t)d.S * d.Hkv * d.geo.rows * d.D;
   _Float16* f16 = reinterpret_cast<_Float16*>(pyr + plane);
-  DecodeKArgs a{k_cache, v_cache, pyr, f16, reinterpret_cast<int32_t*>(f16 + plane), len, q_new, k_new, v_new, o, idx, score, err,
-                d.S, d.Hq, d.Hkv, d.C, d.K, d.cap, d.scale, d.geo};
+  DecodeKArgs a{k_cache, v_cache, pyr, f16, reinterpret_cast<int32_t*>(f16 + plane), len, q_new, k_new, v_new, o, idx,
+                score, err, d.S, d.Hq, d.Hkv, d.C, d.K, d.cap, d.scale, d.geo};
+  const dim3 grid((unsigned)((int64_t)d.S * d.Hkv));
   hipError_t e = dispatch_tdg(d.dtype, d.D, d.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
-    PISA_LAUNCH("decode", stream, (decode_kernel<T, D, G>), dim3((unsigned)((int64_t)d.S * d.Hkv)), dim3(kWave), 0,
-                a);
+    constexpr int NW = G >= 8 ? 4 : 8;
+    if (d.C <= 32)
+      PISA_LAUNCH("decode", stream, (decode_kernel<T, D, G, NW, 2>), grid, dim3(NW * kWave), 0, a);
+    else if (d.C <= 64)
+      PISA_LAUNCH("decode", stream, (decode_kernel<T, D, G, NW, 4>), grid, dim3(NW * kWave), 0, a);
+    else
+      PISA_LAUNCH("decode", stream, (decode_kernel<T, D, G, NW, 8>), grid, dim3(NW * kWave), 0, a);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
