@@ -45,6 +45,26 @@ struct DecodeKArgs {
 
 constexpr int kDecMaxCand = 64;  // 2K, K <= 32
 
+// N consecutive elements (N = 4 or 8) as fp32
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const T* p, float* out) {
+  if constexpr (N == 8) {
+    load8<T>(p, out);
+  } else if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    out[0] = __uint_as_float(u.x << 16);
+    out[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(u.y << 16);
+    out[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    out[0] = f.x;
+    out[1] = f.y;
+    out[2] = f.z;
+    out[3] = f.w;
+  }
+}
+
 // Raw dot products of the keys [lo, hi) of one leaf with the G query heads:
 // S^T tile kb holds keys lo + 16kb + 4(lane/16) + i (i = 0..3) in column
 // lane % 16 = head.  Row newpos is read from knew (the appended token).
@@ -54,28 +74,34 @@ __device__ __forceinline__ void leaf_dots(const Frag<T>* fq, const T* kbase, con
   constexpr int NS = D / 32;
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
+  const int nk = (int)(hi - lo), knew_off = (int)(newpos - lo);  // keys of the leaf; the new key's offset
+  const T* leaf = kbase + lo * D;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    const int64_t r = lo + kb * 16 + col;
-    const T* row = (r == newpos) ? knew : kbase + r * D;
+    const int r = kb * 16 + col;
+    const T* row = (r == knew_off) ? knew : leaf + r * D;
     Frag<T> fk[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (r < hi) fk[s].load(row + g * (D / 4) + 8 * s);
+      if (r < nk) fk[s].load(row + g * (D / 4) + 8 * s);
       else fk[s].zero();
     }
     acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[kb] = mma(fk[s], fq[s], acc[kb]);
+    // at most two key blocks of fragments in flight (register budget)
+    if (kb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <typename T, int D, int G, int NW, int NKB>
-__global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
+// two workgroups per CU where the registers allow it (bf16, C <= 64)
+__global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : NW / 4) void decode_kernel(DecodeKArgs a) {
   constexpr int DPL = D / kWave;  // dims per lane in whole-row work
   constexpr int NS = D / 32;
   constexpr int CP = NKB * 16;    // keys per leaf tile
-  constexpr int LPR = D / 8;      // lanes per V row in the PV product
+  constexpr int DPV = G >= 8 ? 4 : 8;  // dims per lane in the PV product
+  constexpr int LPR = D / DPV;         // lanes per V row there
   constexpr int RPI = kWave / LPR;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ __align__(16) float s_q[G * D];
@@ -126,18 +152,28 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
     }
   for (int i = threadIdx.x; i < G * D; i += NW * kWave) s_q[i] = load1<T>(qn + i);
   {
-    float acc[DPL];
+    // cached rows of the current leaf: 8 lanes per row, 8 rows per wave
+    constexpr int DL = D / 8;
+    const int sub = lane & 7;
+    float acc[DL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    for (int64_t i = lo_leaf + w; i < n; i += NW) {
-      float v[DPL];
+    for (int e = 0; e < DL; ++e) acc[e] = 0.f;
+    for (int64_t i = lo_leaf + w * 8 + (lane >> 3); i < n; i += NW * 8) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) v[e] = load1<T>(kbase + i * D + lane * DPL + e);
+      for (int e = 0; e < DL; e += 8) {
+        float v[8];
+        load8<T>(kbase + i * D + sub * DL + e, v);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += v[e];
+        for (int x = 0; x < 8; ++x) acc[e + x] += v[x];
+      }
     }
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) s_mean[w * D + lane * DPL + e] = acc[e];
+    for (int e = 0; e < DL; ++e)
+#pragma unroll
+      for (int o = 8; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+    if (lane < 8)
+#pragma unroll
+      for (int e = 0; e < DL; ++e) s_mean[w * D + sub * DL + e] = acc[e];
     // sibling of the path node at level l - 1, for l = 2 .. L1
     for (int32_t l = 2 + w; l <= L1; l += NW) {
       const int64_t node = j_leaf >> (l - 2);
@@ -183,7 +219,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
       put_row(a.geo.level_off[l] + node, cur);
     }
   }
-  __threadfence();  // the path rows are read below by every wave
+  // the path rows are read below by every wave of this workgroup, which all
+  // run on one CU: a workgroup-scope fence suffices (no L2 write-back)
+  __threadfence_block();
   __syncthreads();
 
   // ---- 2. descent, levels L1 .. 2 ----------------------------------------
@@ -310,6 +348,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
   for (int i = w; i < nA; i += NW) {
     const int64_t lo = (int64_t)s_cand[i] * C;
     const int64_t hi = lo + C < n1 ? lo + C : n1;
+    const int nk = (int)(hi - lo);
     floatx4 acc[NKB];
     leaf_dots<T, D, NKB>(fq, kbase, knew, n, lo, hi, acc);
     float mx = -INFINITY;
@@ -317,7 +356,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool ok = lo + kb * 16 + 4 * g4 + e < hi;
+        const bool ok = kb * 16 + 4 * g4 + e < nk;
         acc[kb][e] = ok ? acc[kb][e] : -INFINITY;
         mx = fmaxf(mx, acc[kb][e]);
       }
@@ -377,15 +416,15 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
   // ---- 4. attention over the kept leaves -----------------------------------
   const int nI = s_state[1];
   const float mcol = col < G ? s_M[col] * kLog2e : 0.f;
-  const int rg = lane / LPR, dl = (lane % LPR) * 8;
-  float acc_o[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc_o[g][e] = 0.f;
+  const int rg = lane / LPR, dl = (lane % LPR) * DPV;
+  // this wave's partial output accumulates in its own LDS slice, so the
+  // accumulators are not live while the next leaf's keys are in flight
+  for (int i = lane; i < G * D; i += kWave) s_o[w * G * D + i] = 0.f;
+  wave_sync();
   for (int c = w; c < nI; c += NW) {
     const int64_t lo = (int64_t)s_sel[c] * C;
     const int64_t hi = lo + C < n1 ? lo + C : n1;
+    const int nk = (int)(hi - lo);
     floatx4 acc[NKB];
     leaf_dots<T, D, NKB>(fq, kbase, knew, n, lo, hi, acc);
 #pragma unroll
@@ -393,36 +432,40 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(DecodeKArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = kb * 16 + 4 * g4 + e;
-        const float p = (lo + key < hi) ? exp2f(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
+        const float p = key < nk ? exp2f(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
         if (col < G) s_p[w][key][col] = p;
       }
     wave_sync();
-    const int nk = (int)(hi - lo);
+    float acc_o[G][DPV];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < DPV; ++e) acc_o[g][e] = 0.f;
 #pragma unroll 4
     for (int kk = rg; kk < nk; kk += RPI) {
       const int64_t r = lo + kk;
-      float v8[8];
-      load8<T>((r == n ? vnew : vbase + r * D) + dl, v8);
+      float vv[DPV];
+      load_vec<T, DPV>((r == n ? vnew : vbase + r * D) + dl, vv);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float pg = s_p[w][kk][g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc_o[g][e] = fmaf(pg, v8[e], acc_o[g][e]);
+        for (int e = 0; e < DPV; ++e) acc_o[g][e] = fmaf(pg, vv[e], acc_o[g][e]);
       }
     }
-    wave_sync();
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int o = LPR; o < kWave; o <<= 1) acc_o[g][e] += __shfl_xor(acc_o[g][e], o);
-  if (rg == 0)
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[(w * G + g) * D + dl + e] = acc_o[g][e];
+      for (int e = 0; e < DPV; ++e)
+#pragma unroll
+        for (int o = LPR; o < kWave; o <<= 1) acc_o[g][e] += __shfl_xor(acc_o[g][e], o);
+    if (rg == 0)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < DPV; ++e) s_o[(w * G + g) * D + dl + e] += acc_o[g][e];
+    wave_sync();
+  }
   __syncthreads();
   T* out = static_cast<T*>(a.o) + ((int64_t)s * a.Hq + h * G) * D;
   for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
