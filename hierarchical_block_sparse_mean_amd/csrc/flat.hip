@@ -77,12 +77,15 @@ __global__ __launch_bounds__(kFlatWaves* kWave) void flat_kernel(FlatArgs a) {
 }
 
 // ---- MFMA flat selector (bf16 inputs) -------------------------------------------
-// One wave per 16 / G_Q consecutive queries of one KV head: every valid leaf
-// summary is scored by (16 leaves) x d x (16 query-head columns) fp16 MFMA
-// tiles from the pyramid's block-floating-point copy (as in stage 1), the
-// group sum is a shuffle over the G_Q columns of a query, and each query keeps
-// its top K in an LDS buffer: a score enters only if it beats the current
-// K-th key, and the buffer is compacted (wave sort, keep K) when it fills.
+// A workgroup takes 64 consecutive queries of one KV head, 16 per wave; one
+// MFMA column per query holds the group's summed query (the group sum applied
+// to q first).  Leaf summaries stream through LDS in tiles of 64 rows from the
+// pyramid's block-floating-point fp16 copy (as in stage 1) and are shared by
+// the four waves: (16 leaves) x d x (16 queries) fp16 tiles.  Each query keeps
+// its candidates in an LDS buffer: a score enters only if it beats the
+// current K-th key, and the buffer is compacted (wave sort, keep K) before it
+// can overflow.  The kept leaves' scores are then recomputed in fp32 from the
+// fp32 summaries and the bf16 queries.
 struct FlatMArgs {
   const uint16_t* q;
   const float* pyr;
@@ -96,42 +99,51 @@ struct FlatMArgs {
   PyrGeom geo;
 };
 
+constexpr int kFlatTile = 64;  // leaf rows per LDS tile
+constexpr int kFlatCap = 64;   // candidate buffer per query
+
 template <int D, int G>
 __global__ __launch_bounds__(kFlatWaves* kWave) void flat_mfma_kernel(FlatMArgs a) {
   constexpr int NS = D / 32;
-  constexpr int TQ = 16 / G;
-  constexpr int CAP = kWave;  // candidate buffer per query
-  __shared__ uint64_t s_buf[kFlatWaves][TQ][CAP];
-  __shared__ int32_t s_cnt[kFlatWaves][TQ];
-  __shared__ uint64_t s_thr[kFlatWaves][TQ];
+  constexpr int RP = D + 8;  // fp16 row pitch in LDS
+  __shared__ __align__(16) _Float16 s_tile[kFlatTile * RP];
+  __shared__ int32_t s_ex[kFlatTile];
+  __shared__ uint64_t s_buf[kFlatWaves][16][kFlatCap];
+  __shared__ int32_t s_cnt[kFlatWaves][16];
+  __shared__ uint64_t s_thr[kFlatWaves][16];
+  __shared__ __align__(16) float s_qs[kFlatWaves][D];
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
-  const int qi = col / G, hh = col % G;
-  const int64_t bid = blockIdx.x;
-  const int h = (int)(bid % a.Hkv);
-  const int64_t r = bid / a.Hkv;
-  const int b = (int)(r % a.B);
-  const int64_t t0 = ((r / a.B) * kFlatWaves + w) * TQ;
-  if (t0 >= a.N) return;  // wave-uniform
-  const int64_t tq = t0 + qi;
+  const int64_t bh = blockIdx.y;
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  const int64_t t0 = (int64_t)blockIdx.x * (kFlatWaves * 16);
+  const int64_t tw = t0 + w * 16;  // first query of this wave
+  const int64_t tq = tw + col;
   const bool qlive = tq < a.N;
-  // B operand: this column's query head, scaled into fp16 by 2^-eq
+  // summed query of column col, contraction elements g*(D/4) + 8st + e
   float qv[NS][8];
-  float mx = 0.f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[st][e] = 0.f;
   if (qlive) {
-    const uint16_t* qrow = a.q + (((int64_t)b * a.Hq + h * G + hh) * a.N + tq) * D;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      load8<uint16_t>(qrow + g * (D / 4) + 8 * st, qv[st]);
+    for (int gg = 0; gg < G; ++gg) {
+      const uint16_t* qrow = a.q + (((int64_t)b * a.Hq + h * G + gg) * a.N + tq) * D;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[st][e]));
+      for (int st = 0; st < NS; ++st) {
+        float x[8];
+        load8<uint16_t>(qrow + g * (D / 4) + 8 * st, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[st][e] += x[e];
+      }
     }
-  } else {
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[st][e] = 0.f;
   }
+  float mx = 0.f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[st][e]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const int eq = row_exponent(mx);
@@ -140,109 +152,120 @@ __global__ __launch_bounds__(kFlatWaves* kWave) void flat_mfma_kernel(FlatMArgs 
   for (int st = 0; st < NS; ++st)
 #pragma unroll
     for (int e = 0; e < 8; ++e) fq[st][e] = to_f16_scaled(qv[st][e], eq);
-  const int64_t bh = (int64_t)b * a.Hkv + h;
+
   const _Float16* hb = a.f16 + (bh * a.geo.rows + a.geo.level_off[1]) * D;
   const int32_t* xb = a.ex + bh * a.geo.rows + a.geo.level_off[1];
   const int32_t M1 = (int32_t)level_rows(a.N, a.C, 1);
-  // leaves valid for the last query of the tile (the others mask theirs)
-  const int64_t tlast = (t0 + TQ - 1 < a.N) ? t0 + TQ - 1 : a.N - 1;
-  const int32_t nl = a.causal ? (int32_t)((tlast / a.C + 1) < M1 ? (tlast / a.C + 1) : M1) : M1;
-  const int32_t lq = qlive ? (a.causal ? (int32_t)((tq / a.C + 1) < M1 ? (tq / a.C + 1) : M1) : M1) : 0;
-  if (lane < TQ) {
+  auto limit = [&](int64_t t) -> int32_t {  // valid leaves of query t
+    if (!a.causal) return M1;
+    const int64_t l = t / a.C + 1;
+    return (int32_t)(l < M1 ? l : M1);
+  };
+  const int64_t tlast_b = (t0 + kFlatWaves * 16 - 1 < a.N) ? t0 + kFlatWaves * 16 - 1 : a.N - 1;
+  const int32_t nl = limit(tlast_b);                                           // rows the workgroup needs
+  const int32_t nlw = tw < a.N ? limit(tw + 15 < a.N ? tw + 15 : a.N - 1) : 0;  // rows this wave needs
+  const int32_t lq = qlive ? limit(tq) : 0;
+  if (lane < 16) {
     s_cnt[w][lane] = 0;
     s_thr[w][lane] = 0ull;
   }
-  wave_sync();
-  for (int32_t base = 0; base < nl; base += 16) {
-    const int32_t row = base + col;
-    const bool vrow = row < nl;
-    const int32_t er = vrow ? xb[row] : 0;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      halfx8 fa;
-      if (vrow) fa = *reinterpret_cast<const halfx8*>(hb + (int64_t)row * D + g * (D / 4) + 8 * st);
-      else fa = halfx8{0, 0, 0, 0, 0, 0, 0, 0};
-      acc = mma16x16x32(fa, fq[st], acc);
+  const float scale = a.scale;
+  for (int32_t base = 0; base < nl; base += kFlatTile) {
+    __syncthreads();  // the previous tile is consumed
+    constexpr int CH = D / 8;  // 16-byte pieces per row
+    for (int i = threadIdx.x; i < kFlatTile * CH; i += kFlatWaves * kWave) {
+      const int r = i / CH, piece = i % CH;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (base + r < nl) v = *reinterpret_cast<const uint4*>(hb + (int64_t)(base + r) * D + piece * 8);
+      *reinterpret_cast<uint4*>(s_tile + r * RP + piece * 8) = v;
     }
-    uint64_t key[4];
+    if (threadIdx.x < kFlatTile) s_ex[threadIdx.x] = base + (int)threadIdx.x < nl ? xb[base + threadIdx.x] : 0;
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t leaf = base + 4 * g + i;
-      const int32_t eri = __shfl(er, 4 * g + i);
-      float u = ldexpf(acc[i], eri + eq) * a.scale;
+    for (int rb = 0; rb < kFlatTile / 16; ++rb) {
+      const int32_t row0 = base + rb * 16;
+      if (row0 >= nlw) break;  // wave-uniform
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int o = 1; o < G; o <<= 1) u += __shfl_xor(u, o);
-      key[i] = (leaf < lq) ? score_key(u, leaf) : 0ull;
-    }
-    // append the candidates that beat the query's current K-th key
-    if (hh == 0) {
-      const uint64_t thr = s_thr[w][qi];
+      for (int st = 0; st < NS; ++st) {
+        const halfx8 fa = *reinterpret_cast<const halfx8*>(s_tile + (rb * 16 + col) * RP + g * (D / 4) + 8 * st);
+        acc = mma16x16x32(fa, fq[st], acc);
+      }
+      // lane (g, col): leaves row0 + 4g + i for query col
+      const uint64_t thr = s_thr[w][col];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (key[i] > thr) {
-          const int pos = atomicAdd(&s_cnt[w][qi], 1);
-          s_buf[w][qi][pos] = key[i];
+      for (int i = 0; i < 4; ++i) {
+        const int32_t leaf = row0 + 4 * g + i;
+        const float u = ldexpf(acc[i], s_ex[rb * 16 + 4 * g + i] + eq) * scale;
+        const uint64_t key = leaf < lq ? score_key(u, leaf) : 0ull;
+        if (key > thr) {
+          const int pos = atomicAdd(&s_cnt[w][col], 1);
+          s_buf[w][col][pos] = key;
         }
-    }
-    wave_sync();
-    // compact a buffer that could overflow on the next tile
-#pragma unroll
-    for (int qq = 0; qq < TQ; ++qq) {
-      const int cnt = s_cnt[w][qq];
-      if (cnt > CAP - 16) {
+      }
+      wave_sync();
+      // compact the buffers that could overflow on the next 16 leaves
+      uint64_t full = __ballot(lane < 16 && s_cnt[w][lane] > kFlatCap - 16);
+      while (full) {
+        const int qq = __ffsll((long long)full) - 1;
+        full &= full - 1;
+        const int cnt = s_cnt[w][qq];
         uint64_t k2 = lane < cnt ? s_buf[w][qq][lane] : 0ull;
         k2 = wave_sort_desc(k2);
-        // the K-th largest key becomes the entry threshold
-        const uint64_t thr = (uint64_t)(uint32_t)__shfl((int)(uint32_t)k2, a.K - 1) |
+        const uint64_t kth = (uint64_t)(uint32_t)__shfl((int)(uint32_t)k2, a.K - 1) |
                              ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(k2 >> 32), a.K - 1) << 32);
         wave_sync();
         s_buf[w][qq][lane] = lane < a.K ? k2 : 0ull;
         if (lane == 0) {
           s_cnt[w][qq] = a.K;
-          s_thr[w][qq] = thr;
+          s_thr[w][qq] = kth;
         }
         wave_sync();
       }
     }
   }
-  // final top K of each query, written in ascending leaf order
-#pragma unroll
-  for (int qq = 0; qq < TQ; ++qq) {
-    const int64_t tt = t0 + qq;
-    if (tt >= a.N) break;
+  // final top K of each query, in ascending leaf order, with exact scores:
+  // lane = (slot, quarter of the dims); the summed query passes through LDS
+  const int64_t base_p = bh * a.geo.rows + a.geo.level_off[1];
+  for (int qq = 0; qq < 16; ++qq) {
+    const int64_t tt = tw + qq;
+    if (tt >= a.N) break;  // wave-uniform
     const int cnt = s_cnt[w][qq];
     uint64_t k2 = lane < cnt ? s_buf[w][qq][lane] : 0ull;
     k2 = wave_sort_desc(k2);
     const bool kept = lane < a.K && k2 != 0ull;
     uint64_t k3 = kept ? index_key(key_index(k2), key_score(k2)) : 0ull;
     k3 = wave_sort_desc(k3);
-    if (lane < a.K) {
-      const bool v = k3 != 0ull;
-      const int32_t leaf = v ? index_key_index(k3) : -1;
-      const int64_t o = (bh * a.N + tt) * a.K + lane;
-      a.idx[o] = leaf;
-      if (a.score) {
-        // report the kept leaves' scores exactly: fp32 summaries x bf16 q
-        float u = -INFINITY;
-        if (v) {
-          const float* prow = a.pyr + (bh * a.geo.rows + a.geo.level_off[1] + leaf) * D;
-          u = 0.f;
-#pragma unroll 1
-          for (int gg = 0; gg < G; ++gg) {
-            const uint16_t* qrow = a.q + (((int64_t)b * a.Hq + h * G + gg) * a.N + tt) * D;
-            float acc_d = 0.f;
-            for (int d = 0; d < D; d += 8) {
-              float qx[8], px[8];
-              load8<uint16_t>(qrow + d, qx);
-              load8<float>(prow + d, px);
+    const int32_t leaf = k3 != 0ull ? index_key_index(k3) : -1;  // lanes < K
+    if (col == qq)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) acc_d = fmaf(qx[e], px[e], acc_d);
-            }
-            u += acc_d * a.scale;
-          }
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_qs[w][g * (D / 4) + 8 * st + e] = qv[st][e];
+    wave_sync();
+    for (int s0 = 0; s0 < a.K; s0 += kWave / 4) {
+      const int slot = s0 + lane / 4, quarter = lane % 4;
+      const int32_t lf = __shfl(leaf, slot < kWave ? slot : 0);
+      float dot = 0.f;
+      if (slot < a.K && lf >= 0) {
+        const float* prow = a.pyr + (base_p + lf) * D + quarter * (D / 4);
+        const float* qs = &s_qs[w][quarter * (D / 4)];
+#pragma unroll
+        for (int d = 0; d < D / 4; d += 4) {
+          const float4 pv = *reinterpret_cast<const float4*>(prow + d);
+          const float4 qv4 = *reinterpret_cast<const float4*>(qs + d);
+          dot = fmaf(pv.x, qv4.x, dot);
+          dot = fmaf(pv.y, qv4.y, dot);
+          dot = fmaf(pv.z, qv4.z, dot);
+          dot = fmaf(pv.w, qv4.w, dot);
         }
-        a.score[o] = u;
+      }
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      if (quarter == 0 && slot < a.K) {
+        const int64_t o = (bh * a.N + tt) * a.K + slot;
+        a.idx[o] = lf;
+        if (a.score) a.score[o] = lf >= 0 ? dot * scale : -INFINITY;
       }
     }
     wave_sync();
@@ -262,10 +285,8 @@ hipError_t launch_flat(const Problem& p, const void* q, const float* pyr, int32_
     constexpr int D = decltype(dc)::value;
     constexpr int G = decltype(gc)::value;
     if (std::is_same<T, uint16_t>::value) {
-      const int64_t tiles = (p.N + 16 / G - 1) / (16 / G);
-      const int64_t mblocks = (int64_t)p.B * p.Hkv * ((tiles + kFlatWaves - 1) / kFlatWaves);
-      PISA_LAUNCH("flat", stream, (flat_mfma_kernel<D, G>), dim3((unsigned)mblocks), dim3(kFlatWaves * kWave), 0,
-                  m);
+      const dim3 grid((unsigned)((p.N + kFlatWaves * 16 - 1) / (kFlatWaves * 16)), (unsigned)((int64_t)p.B * p.Hkv));
+      PISA_LAUNCH("flat", stream, (flat_mfma_kernel<D, G>), grid, dim3(kFlatWaves * kWave), 0, m);
     } else {
       PISA_LAUNCH("flat", stream, (flat_kernel<T, D, G>), dim3((unsigned)blocks), dim3(kFlatWaves * kWave), 0, a);
     }

@@ -138,7 +138,8 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
 }
 
 // KP: K when K is 16 or 32 (top-K by half sorts), else 0 (full wave sort).
-template <int D, int G, int KP>
+// CNT: a separate instance that also accumulates the work counters
+template <int D, int G, int KP, bool CNT>
 __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArgs a) {
   constexpr int NS = D / 32;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
   int32_t kept = (lane == 0) ? 0 : -1;
   int nI = 1;
   int64_t w_rows = 0, w_cands = 0, w_levels = 0;  // diagnostics only
-  int64_t* rows_ptr = a.counts != nullptr ? &w_rows : nullptr;
+  int64_t* rows_ptr = CNT ? &w_rows : nullptr;
   wave_sync();
   for (int32_t l = a.L; l >= 2; --l) {
     // valid blocks of level l: index < M_l and (causal) first token <= t
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
   if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
   else k2 = wave_sort_desc(k2);
   if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
-  if (a.counts != nullptr && lane == 0) {
+  if (CNT && lane == 0) {
     atomicAdd(&a.counts[0], 1ull);
     atomicAdd(&a.counts[1], (unsigned long long)w_cands);
     atomicAdd(&a.counts[2], (unsigned long long)w_rows);
@@ -254,15 +255,15 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
     if (fused)
       PISA_LAUNCH("route_fused", stream, (route_kernel<T, D, G, true>), dim3((unsigned)blocks),
                   dim3(kRouteWaves * kWave), 0, a);
-    else if (std::is_same<T, uint16_t>::value && p.K == 16)
-      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G, 16>), dim3((unsigned)blocks),
-                  dim3(kRouteWaves * kWave), 0, a);
-    else if (std::is_same<T, uint16_t>::value && p.K == 32)
-      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G, 32>), dim3((unsigned)blocks),
-                  dim3(kRouteWaves * kWave), 0, a);
-    else if (std::is_same<T, uint16_t>::value)
-      PISA_LAUNCH("route_stage1", stream, (route_mfma_kernel<D, G, 0>), dim3((unsigned)blocks),
-                  dim3(kRouteWaves * kWave), 0, a);
+    else if (std::is_same<T, uint16_t>::value) {
+      auto run = [&](auto kern) {
+        PISA_LAUNCH(counts ? "route_stage1_counted" : "route_stage1", stream, kern, dim3((unsigned)blocks),
+                    dim3(kRouteWaves * kWave), 0, a);
+      };
+      if (p.K == 16) counts ? run(route_mfma_kernel<D, G, 16, true>) : run(route_mfma_kernel<D, G, 16, false>);
+      else if (p.K == 32) counts ? run(route_mfma_kernel<D, G, 32, true>) : run(route_mfma_kernel<D, G, 32, false>);
+      else counts ? run(route_mfma_kernel<D, G, 0, true>) : run(route_mfma_kernel<D, G, 0, false>);
+    }
     else
       PISA_LAUNCH("route_stage1", stream, (route_kernel<T, D, G, false>), dim3((unsigned)blocks),
                   dim3(kRouteWaves * kWave), 0, a);
