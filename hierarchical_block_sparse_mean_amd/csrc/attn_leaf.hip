@@ -20,7 +20,10 @@
 
 namespace pisa {
 
-constexpr int kAttnWaves = 4;
+// waves per workgroup: 8 when a leaf tile fills most of the LDS (C > 64), so
+// that one resident workgroup still keeps 8 waves in flight; 4 otherwise
+template <int NKB>
+constexpr int attn_waves() { return NKB >= 8 ? 8 : 4; }
 constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
 constexpr size_t kAttnBudget = (size_t)8 << 30;  // partial buffers per head chunk
 
@@ -90,7 +93,8 @@ struct AttnLeafArgs {
 
 // NKB: 16-key blocks covering the leaf (even, C <= 16 NKB).
 template <typename T, int D, int G, int NKB>
-__global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafArgs a) {
+__global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(AttnLeafArgs a) {
+  constexpr int NW = attn_waves<NKB>();
   constexpr int NS = D / 32;                   // contraction steps of S
   constexpr int TQ = 16 / G;                   // queries per 16-column tile
   constexpr int CP = NKB * 16;                 // keys held (zero padded)
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
   T* s_vt = s_k + CP * KP;                   // [D][VP]
   // a tile's 16 output columns x D, staged so each lane stores 16-byte pieces
-  __shared__ __align__(16) T s_o[kAttnWaves][16][D + 16 / sizeof(T)];
+  __shared__ __align__(16) T s_o[NW][16][D + 16 / sizeof(T)];
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_leaf_kernel(AttnLeafAr
       for (int s = 0; s < NS; ++s) f[s].zero();
     }
   };
-  const int64_t stride = (int64_t)kAttnWaves * TQ;
+  const int64_t stride = (int64_t)NW * TQ;
   for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += stride) {
     const int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
     Frag<T> fq[NS];
@@ -365,7 +369,7 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value;
       constexpr int G = decltype(gc)::value;
-      auto run = [&](auto kern, int nkb) -> hipError_t {
+      auto run = [&](auto kern, int nkb, int nw) -> hipError_t {
         const size_t lds = ((size_t)nkb * 16 * (D + 16 / sizeof(T)) + (size_t)D * (nkb * 16 + 16 / sizeof(T))) *
                            sizeof(T);
         if (lds > 65536) {
@@ -373,16 +377,16 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
           if (e != hipSuccess) return e;
         }
-        PISA_LAUNCH("attn_leaf", stream, kern, dim3((unsigned)max_chunks), dim3(kAttnWaves * kWave), lds, aa);
+        PISA_LAUNCH("attn_leaf", stream, kern, dim3((unsigned)max_chunks), dim3(nw * kWave), lds, aa);
         return hipGetLastError();
       };
       hipError_t e;
       if (p.C <= 32)
-        e = run(attn_leaf_kernel<T, D, G, 2>, 2);
+        e = run(attn_leaf_kernel<T, D, G, 2>, 2, attn_waves<2>());
       else if (p.C <= 64)
-        e = run(attn_leaf_kernel<T, D, G, 4>, 4);
+        e = run(attn_leaf_kernel<T, D, G, 4>, 4, attn_waves<4>());
       else
-        e = run(attn_leaf_kernel<T, D, G, 8>, 8);
+        e = run(attn_leaf_kernel<T, D, G, 8>, 8, attn_waves<8>());
       if (e != hipSuccess) return e;
       const int64_t waves = heads * p.N;
       PISA_LAUNCH("attn_merge", stream, (attn_merge_kernel<T, D, G>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,

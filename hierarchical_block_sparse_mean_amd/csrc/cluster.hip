@@ -6,8 +6,10 @@
 //
 // Counting sort in three passes, no global atomics:
 //   1. per tile of 8192 entries, an LDS histogram over the head's key blocks;
-//   2. per head, bin totals, an exclusive scan over bins, and per-(bin, tile)
-//      base positions; then one scan of the work-chunk counts of all clusters;
+//   2. per (head, bin), a running sum down the tiles gives the bin total and
+//      each tile's base within the bin; per head, an exclusive scan over the
+//      bins gives each bin's first pair; then one scan of the work-chunk
+//      counts of all clusters;
 //   3. per tile, an LDS cursor per bin scatters t*K + slot into the pairs.
 // Heads with more key blocks than the LDS histogram holds use a global-atomic
 // fallback.  Either way: counts[c], offsets[c] (first pair) and
@@ -44,26 +46,41 @@ __global__ void hist_kernel(const int32_t* __restrict__ keys, int64_t NK, int64_
   for (int64_t i = threadIdx.x; i < M; i += blockDim.x) out[i] = s_h[i];
 }
 
-// One workgroup per head: counts, offsets (head * NK + exclusive scan over
-// bins) and, in place of the histogram, the base position of every (tile, bin).
-__global__ __launch_bounds__(1024) void hist_scan_kernel(int32_t* hist, int64_t NK, int64_t M, int64_t tiles,
-                                                         int32_t* counts, int32_t* offsets) {
-  extern __shared__ int32_t s_tot[];  // M
+// Per (head, bin), one thread: a running sum down the tiles turns each
+// histogram entry into the position of that tile's first pair relative to the
+// bin's first pair, and gives the bin total.
+__global__ void col_scan_kernel(int32_t* hist, int64_t M, int64_t tiles, int32_t* counts) {
+  const int64_t head = blockIdx.y;
+  const int64_t bin = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (bin >= M) return;
+  int32_t* hh = hist + head * tiles * M + bin;
+  int32_t run = 0;
+  for (int64_t tl = 0; tl < tiles; tl += 8) {
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = tl + u < tiles ? hh[(tl + u) * M] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (tl + u < tiles) {
+        hh[(tl + u) * M] = run;
+        run += c[u];
+      }
+  }
+  counts[head * M + bin] = run;
+}
+
+// One workgroup per head: offsets = head * NK + exclusive scan of the bin
+// totals.
+__global__ __launch_bounds__(1024) void bin_scan_kernel(const int32_t* __restrict__ counts, int64_t NK, int64_t M,
+                                                        int32_t* offsets) {
   __shared__ int32_t s_part[1024];
   __shared__ int32_t s_carry;
   const int64_t head = blockIdx.x;
-  int32_t* hh = hist + head * tiles * M;
-  for (int64_t bin = threadIdx.x; bin < M; bin += blockDim.x) {
-    int32_t tot = 0;
-    for (int64_t tl = 0; tl < tiles; ++tl) tot += hh[tl * M + bin];
-    s_tot[bin] = tot;
-    counts[head * M + bin] = tot;
-  }
   if (threadIdx.x == 0) s_carry = 0;
   __syncthreads();
   for (int64_t base = 0; base < M; base += 1024) {
     const int64_t bin = base + threadIdx.x;
-    const int32_t v = bin < M ? s_tot[bin] : 0;
+    const int32_t v = bin < M ? counts[head * M + bin] : 0;
     s_part[threadIdx.x] = v;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
@@ -72,28 +89,20 @@ __global__ __launch_bounds__(1024) void hist_scan_kernel(int32_t* hist, int64_t 
       s_part[threadIdx.x] += add;
       __syncthreads();
     }
-    if (bin < M) s_tot[bin] = s_carry + s_part[threadIdx.x] - v;  // exclusive
+    if (bin < M) offsets[head * M + bin] = (int32_t)(head * NK) + s_carry + s_part[threadIdx.x] - v;
     __syncthreads();
     if (threadIdx.x == 1023) s_carry += s_part[1023];
     __syncthreads();
   }
-  for (int64_t bin = threadIdx.x; bin < M; bin += blockDim.x) {
-    int32_t run = (int32_t)(head * NK) + s_tot[bin];
-    offsets[head * M + bin] = run;
-    for (int64_t tl = 0; tl < tiles; ++tl) {
-      const int32_t c = hh[tl * M + bin];
-      hh[tl * M + bin] = run;
-      run += c;
-    }
-  }
 }
 
 __global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int64_t M, int64_t tiles,
-                               const int32_t* __restrict__ base, int32_t* __restrict__ pairs) {
+                               const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+                               int32_t* __restrict__ pairs) {
   extern __shared__ int32_t s_cur[];
   const int64_t head = blockIdx.y, tile = blockIdx.x;
   const int32_t* b = base + (head * tiles + tile) * M;
-  for (int64_t i = threadIdx.x; i < M; i += blockDim.x) s_cur[i] = b[i];
+  for (int64_t i = threadIdx.x; i < M; i += blockDim.x) s_cur[i] = offsets[head * M + i] + b[i];
   __syncthreads();
   const int64_t lo = head * NK + tile * kHistTile;
   const int64_t hi = (tile + 1) * kHistTile < NK ? lo + kHistTile : head * NK + NK;
@@ -191,16 +200,17 @@ hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int64
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
                          : hipSuccess;
     };
-    if (big(hist_kernel) != hipSuccess || big(hist_scan_kernel) != hipSuccess || big(scatter_kernel) != hipSuccess)
-      return hipErrorInvalidValue;
+    if (big(hist_kernel) != hipSuccess || big(scatter_kernel) != hipSuccess) return hipErrorInvalidValue;
     PISA_LAUNCH("cluster_hist", stream, hist_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds, keys, NK,
                 M, tiles, b.hist);
-    PISA_LAUNCH("cluster_scan", stream, hist_scan_kernel, dim3((unsigned)heads), dim3(1024), lds, b.hist, NK, M,
-                tiles, b.counts, b.offsets);
+    PISA_LAUNCH("cluster_scan", stream, col_scan_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)heads),
+                dim3(256), 0, b.hist, M, tiles, b.counts);
+    PISA_LAUNCH("cluster_scan", stream, bin_scan_kernel, dim3((unsigned)heads), dim3(1024), 0, b.counts, NK, M,
+                b.offsets);
     PISA_LAUNCH("cluster_chunks", stream, chunk_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, chunk,
                 b.chunk_off);
     PISA_LAUNCH("cluster_scatter", stream, scatter_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds,
-                keys, NK, M, tiles, b.hist, b.pairs);
+                keys, NK, M, tiles, b.hist, b.offsets, b.pairs);
     return hipGetLastError();
   }
   const int64_t entries = heads * NK;
