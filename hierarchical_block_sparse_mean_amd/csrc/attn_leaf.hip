@@ -185,17 +185,20 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
     }
     // column softmax statistics (keys are rows 4g+i of each 16-key block):
     // max on the raw dot products, then p = exp2((x - max) * scale*log2e)
-    const int64_t lim = live ? (a.causal ? (t - key0 + 1 < nkeys ? t - key0 + 1 : nkeys) : nkeys) : 0;
+    const int lim = live ? (int)(a.causal ? (t - key0 + 1 < nkeys ? t - key0 + 1 : nkeys) : nkeys) : 0;
+    // the mask only where some column of the tile sees fewer keys than held
+    if (__ballot(lim < NKB * 16) != 0ull) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb * 16 + 4 * g + i >= lim) acc[kb][i] = -INFINITY;
+    }
     float mraw = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb * 16 + 4 * g + i;
-        const float x = key < lim ? acc[kb][i] : -INFINITY;
-        acc[kb][i] = x;
-        mraw = fmaxf(mraw, x);
-      }
+      for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, acc[kb][i]);
     mraw = fmaxf(mraw, __shfl_xor(mraw, 16));
     mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
     const float sl2 = a.scale * 1.4426950408889634f;
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = exp2f(fmaf(acc[kb][i], sl2, nb));  // exp2(-inf) = 0
+        const float pv = exp2_nonpos(fmaf(acc[kb][i], sl2, nb));  // exp2(-inf) = 0
         acc[kb][i] = pv;
         l += pv;
       }

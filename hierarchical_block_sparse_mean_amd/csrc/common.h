@@ -113,6 +113,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// 2^x for x <= 0 (or -inf) on the hardware exp unit alone, without the
+// library's denormal-range fix-up: a result that would be denormal flushes to
+// zero, which changes nothing where every use adds it to a term >= 1 (the
+// running maximum's own 2^0) or scales a value by it.
+__device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // log(exp(a) + exp(b)) with -inf handled
 __device__ __forceinline__ float lse2(float a, float b) {
   const float m = fmaxf(a, b);

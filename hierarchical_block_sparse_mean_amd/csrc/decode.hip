@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum += exp2f((acc[kb][e] - mx) * sl2);  // exp2(-inf) = 0
+      for (int e = 0; e < 4; ++e) sum += exp2_nonpos((acc[kb][e] - mx) * sl2);  // exp2(-inf) = 0
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
     const float m_nat = mx * a.scale;
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = kb * 16 + 4 * g4 + e;
-        const float p = key < nk ? exp2f(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
+        const float p = key < nk ? exp2_nonpos(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
         if (col < G) s_p[w][key][col] = p;
       }
     wave_sync();

@@ -122,7 +122,7 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const float m = fmaxf(x[2 * p], x[2 * p + 1]);
-      u[p] = (m == -INFINITY) ? -INFINITY : m + __log2f(exp2f(x[2 * p] - m) + exp2f(x[2 * p + 1] - m));
+      u[p] = (m == -INFINITY) ? -INFINITY : m + __log2f(exp2_nonpos(x[2 * p] - m) + exp2_nonpos(x[2 * p + 1] - m));
     }
 #pragma unroll
     for (int o = 1; o < G; o <<= 1) {

@@ -171,18 +171,25 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
       const int64_t t = pr / a.K;
       lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
     }
-    // masked raw dot products; max per leaf; exp2 of (x - max) * scale*log2e
+    // masked raw dot products (the mask only where some column of the tile
+    // sees fewer keys than the tile holds); max per leaf; exp2 of
+    // (x - max) * scale*log2e
+    if (__ballot(lim < NCB * 16) != 0ull) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (cb * 16 + 4 * g + i >= lim) acc[cb][i] = -INFINITY;
+    }
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kl = cb * 16 + 4 * g + i;
-        const float x = kl < lim ? acc[cb][i] : -INFINITY;
-        acc[cb][i] = x;
         const bool first = CB0 ? (cb < CB0) : (kl < C);
-        if (first) mx0 = fmaxf(mx0, x);
-        else mx1 = fmaxf(mx1, x);
+        if (first) mx0 = fmaxf(mx0, acc[cb][i]);
+        else mx1 = fmaxf(mx1, acc[cb][i]);
       }
     mx0 = fmaxf(mx0, __shfl_xor(mx0, 16));
     mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
@@ -196,8 +203,8 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
       for (int i = 0; i < 4; ++i) {
         const int kl = cb * 16 + 4 * g + i;
         const bool first = CB0 ? (cb < CB0) : (kl < C);
-        if (first) s0 += exp2f(fmaf(acc[cb][i], sl2, nb0));  // exp2(-inf) = 0
-        else s1 += exp2f(fmaf(acc[cb][i], sl2, nb1));
+        if (first) s0 += exp2_nonpos(fmaf(acc[cb][i], sl2, nb0));  // exp2(-inf) = 0
+        else s1 += exp2_nonpos(fmaf(acc[cb][i], sl2, nb1));
       }
     s0 += __shfl_xor(s0, 16);
     s0 += __shfl_xor(s0, 32);
