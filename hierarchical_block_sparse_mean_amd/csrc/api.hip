@@ -80,6 +80,7 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
   const int64_t cap = p->cap ? p->cap : p->N;
   if ((int64_t)p->B * p->Hkv * p->N * p->K > INT32_MAX || (int64_t)p->N * p->K > INT32_MAX)
     return fail(PISA_ERR_UNSUPPORTED, "B*Hkv*N*K exceeds 2^31-1");
+  if (p->N >= (1 << 26)) return fail(PISA_ERR_UNSUPPORTED, "N must be < 2^26 (got %d)", p->N);
   out->B = p->B;
   out->N = p->N;
   out->Hq = p->Hq;

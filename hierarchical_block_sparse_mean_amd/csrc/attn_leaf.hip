@@ -151,7 +151,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
   // S^T = K Q^T is that query head's row
   auto load_q = [&](int32_t pr, Frag<T>* f) {
     if (pr >= 0) {
-      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + pr / a.K) * D;
+      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + (pr >> 5)) * D;
 #pragma unroll
       for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
     } else {
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
     Frag<T> fq[NS];
     load_q(pr, fq);
     const bool live = pr >= 0;
-    const int64_t t = live ? pr / a.K : -1;
+    const int64_t t = live ? (pr >> 5) : -1;
     // K / V^T fragments are re-read from LDS every tile (an offset opaque to
     // the compiler keeps them from being held in registers across tiles)
     int toff = 0;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
 #pragma unroll
       for (int i = 0; i < 4; ++i) store1<T>(&s_o[w][col][db * 16 + 4 * g + i], oacc[db][i]);
     if (live && g == 0) {
-      const int64_t rec = ((hl * a.N + t) * a.K + pr % a.K) * G + hh;
+      const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
       a.pm[rec] = m;
       a.pl[rec] = l;
     }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
         const int cc = i / PER_COL, piece = i % PER_COL;
         const int32_t pc = __shfl(pr, cc);  // pair of column cc (lane cc of group 0)
         if (pc >= 0) {
-          const int64_t rec = ((hl * a.N + pc / a.K) * a.K + pc % a.K) * G + (cc % G);
+          const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (cc % G);
           *reinterpret_cast<uint4*>(static_cast<T*>(a.po) + rec * D + piece * CH) =
               *reinterpret_cast<const uint4*>(&s_o[w][cc][piece * CH]);
         }
@@ -362,7 +362,8 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     const int64_t entries = heads * p.N * p.K;
     const int64_t ncl = heads * L.M1;
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
-    hipError_t err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, L.M1, kAttnChunk, cb, stream);
+    hipError_t err =
+        launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnChunk, cb, stream);
     if (err != hipSuccess) return err;
     AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, head0, p.N, p.Hq, p.Hkv, p.C, p.K,
                     p.causal ? 1 : 0, p.cap, p.scale};

@@ -10,7 +10,7 @@
 //      each tile's base within the bin; per head, an exclusive scan over the
 //      bins gives each bin's first pair; then one scan of the work-chunk
 //      counts of all clusters;
-//   3. per tile, an LDS cursor per bin scatters t*K + slot into the pairs.
+//   3. per tile, an LDS cursor per bin scatters the pair code (t << 5) | slot.
 // Heads with more key blocks than the LDS histogram holds use a global-atomic
 // fallback.  Either way: counts[c], offsets[c] (first pair) and
 // chunk_off[c] (first work chunk, chunk_off[ncl] = total) for c = head*M + j.
@@ -96,7 +96,13 @@ __global__ __launch_bounds__(1024) void bin_scan_kernel(const int32_t* __restric
   }
 }
 
-__global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int64_t M, int64_t tiles,
+// pair code of entry e_loc = t * K + slot of a head: (t << 5) | slot (K <= 32)
+__device__ __forceinline__ int32_t pair_code(int64_t e_loc, int32_t K) {
+  const int32_t t = (int32_t)(e_loc / K);
+  return (t << 5) | (int32_t)(e_loc - (int64_t)t * K);
+}
+
+__global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int64_t tiles,
                                const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
                                int32_t* __restrict__ pairs) {
   extern __shared__ int32_t s_cur[];
@@ -108,7 +114,7 @@ __global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int
   const int64_t hi = (tile + 1) * kHistTile < NK ? lo + kHistTile : head * NK + NK;
   for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) {
     const int32_t j = keys[e];
-    if (j >= 0 && j < M) pairs[atomicAdd(&s_cur[j], 1)] = (int32_t)(e - head * NK);
+    if (j >= 0 && j < M) pairs[atomicAdd(&s_cur[j], 1)] = pair_code(e - head * NK, K);
   }
 }
 
@@ -178,18 +184,19 @@ __global__ __launch_bounds__(1024) void offset_scan_kernel(const int32_t* __rest
   }
 }
 
-__global__ void atomic_fill_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int64_t M,
-                                   const int32_t* __restrict__ offsets, int32_t* cursor, int32_t* pairs) {
+__global__ void atomic_fill_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int32_t K,
+                                   int64_t M, const int32_t* __restrict__ offsets, int32_t* cursor,
+                                   int32_t* pairs) {
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int32_t j = keys[e];
     if (j < 0 || j >= M) continue;
     const int64_t c = (e / NK) * M + j;
-    pairs[offsets[c] + atomicAdd(&cursor[c], 1)] = (int32_t)(e % NK);
+    pairs[offsets[c] + atomicAdd(&cursor[c], 1)] = pair_code(e % NK, K);
   }
 }
 
-hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int64_t M, int32_t chunk,
+hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int32_t chunk,
                            const ClusterBufs& b, hipStream_t stream) {
   const int64_t ncl = heads * M;
   if (M <= kMaxBins) {
@@ -210,7 +217,7 @@ hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int64
     PISA_LAUNCH("cluster_chunks", stream, chunk_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, chunk,
                 b.chunk_off);
     PISA_LAUNCH("cluster_scatter", stream, scatter_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds,
-                keys, NK, M, tiles, b.hist, b.offsets, b.pairs);
+                keys, NK, K, M, tiles, b.hist, b.offsets, b.pairs);
     return hipGetLastError();
   }
   const int64_t entries = heads * NK;
@@ -222,7 +229,7 @@ hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int64
   PISA_LAUNCH("cluster_scan", stream, offset_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, b.offsets);
   PISA_LAUNCH("cluster_chunks", stream, chunk_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, chunk,
               b.chunk_off);
-  PISA_LAUNCH("cluster_fill", stream, atomic_fill_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, M, b.offsets,
+  PISA_LAUNCH("cluster_fill", stream, atomic_fill_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, b.offsets,
               b.cursor, b.pairs);
   return hipGetLastError();
 }

@@ -88,7 +88,9 @@ struct ClusterBufs {
   int32_t* hist;
 };
 size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t M);
-hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int64_t M, int32_t chunk,
+// keys: [heads][N][K] block indices (-1 = none), NK = N * K.  pairs holds,
+// per cluster (head * M + block), the codes (t << 5) | slot of its entries.
+hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int32_t chunk,
                            const ClusterBufs& b, hipStream_t stream);
 
 // attn_leaf.hip: leaf-major MFMA attention with a merge pass

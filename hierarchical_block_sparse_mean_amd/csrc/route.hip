@@ -190,10 +190,14 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
   int64_t w_rows = 0, w_cands = 0, w_levels = 0;  // diagnostics only
   int64_t* rows_ptr = CNT ? &w_rows : nullptr;
   wave_sync();
+  // level sizes and the last valid block by shifts: M_l = ceil(M_1 / 2^(l-1))
+  // and block j of level l starts at j C 2^(l-1) <= t iff j <= (t / C) >> (l-1)
+  const int32_t M1 = (int32_t)level_rows(a.N, a.C, 1);
+  const int32_t tc = (int32_t)t / a.C;
   for (int32_t l = a.L; l >= 2; --l) {
     // valid blocks of level l: index < M_l and (causal) first token <= t
-    const int32_t ml = (int32_t)level_rows(a.N, a.C, l);
-    const int32_t tl_blk = causal ? (int32_t)(t / ((int64_t)a.C << (l - 1))) : 0x7fffffff;
+    const int32_t ml = ((M1 - 1) >> (l - 1)) + 1;
+    const int32_t tl_blk = causal ? (tc >> (l - 1)) : 0x7fffffff;
     const int32_t j = (lane < nA) ? s.cand[lane] : 0x7fffffff;
     const bool valid = j < ml && j <= tl_blk;
     const uint64_t mask = __ballot(valid);
@@ -203,8 +207,8 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
     if (valid) s.cand[pos] = j;
     wave_sync();
     if (nA > a.K) {
-      const int32_t m_child = (int32_t)level_rows(a.N, a.C, l - 1);
-      const int32_t tl = causal ? (int32_t)(t / ((int64_t)a.C << (l - 2))) : 0x7fffffff;
+      const int32_t m_child = ((M1 - 1) >> (l - 2)) + 1;
+      const int32_t tl = causal ? (tc >> (l - 2)) : 0x7fffffff;
       score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, m_child, tl, l, sl2, rows_ptr);
       w_cands += nA;
       w_levels += 1;

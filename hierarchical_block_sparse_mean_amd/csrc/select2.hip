@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
   float* out_base = a.scores + bh * (int64_t)a.N * a.K * 2;
   auto load_q = [&](int32_t prq, Frag<T>* f) {
     if (prq >= 0) {
-      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + prq / a.K) * D;
+      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + (prq >> 5)) * D;
 #pragma unroll
       for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
     } else {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
     // keys key_local < lim count for this column's query (t >= key0 + key_local)
     int lim = 0;
     if (pr >= 0) {
-      const int64_t t = pr / a.K;
+      const int64_t t = pr >> 5;
       lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
     }
     // masked raw dot products (the mask only where some column of the tile
@@ -220,8 +220,9 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
       u1 += __shfl_xor(u1, o);
     }
     if (g == 0 && hh == 0 && pr >= 0) {
-      out_base[(int64_t)pr * 2] = u0;
-      out_base[(int64_t)pr * 2 + 1] = u1;
+      const int64_t e = (int64_t)(pr >> 5) * a.K + (pr & 31);  // (t, slot) entry
+      out_base[e * 2] = u0;
+      out_base[e * 2 + 1] = u1;
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) fq[s] = fn[s];
@@ -276,7 +277,7 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
   const int64_t entries = (int64_t)p.B * p.Hkv * p.N * p.K;
   const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
-  hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, M2, kS2Chunk, cb, stream);
+  hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, p.K, M2, kS2Chunk, cb, stream);
   if (err != hipSuccess) return err;
   S2Args a{q, k, counts, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, p.B, p.N, p.Hq, p.Hkv, p.C, p.K,
            p.causal ? 1 : 0, p.cap, p.scale};

@@ -33,7 +33,8 @@
  *     PISA_ERR_HIP.  Outputs are undefined unless PISA_OK is returned.
  *     pisa_last_error() then describes the problem (thread-local string).
  *   - Supported in this version: g == 2 (the page's merge factor), D in
- *     {64, 128}, G_Q in {1, 2, 4, 8, 16}, 1 <= K <= 32, 1 <= C <= 128.
+ *     {64, 128}, G_Q in {1, 2, 4, 8, 16}, 1 <= K <= 32, 1 <= C <= 128,
+ *     N < 2^26, B * Hkv * N * K < 2^31.
  */
 #ifndef PISA_H_
 #define PISA_H_

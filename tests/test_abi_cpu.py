@@ -69,6 +69,7 @@ FAKE = 4096  # a non-NULL address; validation must reject before using it
     (dict(Hq=12, Hkv=4), pisa.PISA_ERR_UNSUPPORTED),
     (dict(K=33), pisa.PISA_ERR_UNSUPPORTED),
     (dict(C=256), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(N=1 << 26, K=1), pisa.PISA_ERR_UNSUPPORTED),
     (dict(cap=100), pisa.PISA_ERR_INVALID_ARG),
     (dict(q_tile=3), pisa.PISA_ERR_UNSUPPORTED),
     (dict(select_algo=7), pisa.PISA_ERR_INVALID_ARG),
