@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (reference for HBM counter scaling)")
+    ap.add_argument("--scaling", action="store_true",
+                    help="selection-time scaling and PISA-vs-flat crossover at C=64, K=16 over --scaling-n")
+    ap.add_argument("--scaling-n", default="32768,65536,131072,262144,524288,1048576")
     return ap.parse_args()
 
 
@@ -135,6 +138,8 @@ def main() -> int:
     from hierarchical_block_sparse_mean_amd import pisa
 
     torch.cuda.set_device(0)
+    if args.scaling:
+        return scaling_main(args)
     w = I.workload(args.workload)
     if w.steps:
         return decode_main(args, w)
@@ -366,6 +371,100 @@ def main() -> int:
         "route_work": rc,
         "cpu_baseline": cpu,
         "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def scaling_main(args) -> int:
+    """Selection time against N at fixed C = 64, K = 16 (Hq = 32, Hkv = 8,
+    d = 128, bf16, causal, planted needle leaves as in the 32K/128K workloads):
+    pyramid + two-stage select, the flat selector, and attention, each timed
+    with HIP events over --steps repetitions after one warm-up.  Prints one
+    JSON line with the table, log-log slopes and the interpolated N where the
+    flat selector becomes slower than PISA's."""
+    import numpy as np
+    import torch
+
+    from hierarchical_block_sparse_mean_amd import inputs as I
+    from hierarchical_block_sparse_mean_amd import pisa
+
+    rows = []
+    for N in [int(x) for x in args.scaling_n.split(",")]:
+        w = I.Workload(f"scaling_{N // 1024}k", 1, N, 32, 8, 128, 64, 16, "bf16", True, "leaf_per_query", seed=5000)
+        t0 = time.perf_counter()
+        data = I.generate(w)
+        q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
+        del data
+        log(f"N={N}: inputs ready in {time.perf_counter() - t0:.1f}s")
+        p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True, dtype="bf16")
+        pyr = pisa.alloc_pyramid(p)
+        ws = pisa.workspace(pisa.select_workspace_bytes(p))
+        aws = pisa.workspace(pisa.attn_workspace_bytes(p))
+        idx = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device="cuda")
+        score = torch.empty_like(idx, dtype=torch.float32)
+        fidx = torch.empty_like(idx)
+        fscore = torch.empty_like(score)
+        fws = pisa.workspace(pisa.flat_workspace_bytes(p))
+        o = torch.empty_like(q)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        def sel():
+            pisa.build_pyramid(p, k, pyr)
+            pisa.select(p, q, k, pyr, idx=idx, score=score, ws=ws)
+
+        def flat():
+            pisa.build_pyramid(p, k, pyr)
+            pisa.flat_select(p, q, pyr, idx=fidx, score=fscore, ws=fws)
+
+        sel_ms = timed(sel)
+        flat_ms = timed(flat)
+        attn_ms = timed(lambda: pisa.sparse_attn(p, q, k, v, idx, o=o, lse=None, ws=aws, with_lse=False))
+        rc = pisa.route_counts(p, q, k, pyr)
+        rows.append({"N": N, "levels": pisa.levels(N, w.C), "select_ms": round(sel_ms, 4),
+                     "flat_select_ms": round(flat_ms, 4), "attention_ms": round(attn_ms, 4),
+                     "step_ms": round(sel_ms + attn_ms, 4),
+                     "child_rows_per_query": round(rc["child_rows"] / max(1, rc["queries"]), 2),
+                     "flat_leaves_per_query": round((pisa.level_rows(N, w.C, 1) + 1) / 2, 1)})
+        log(f"N={N}: select {sel_ms:.3f} ms, flat {flat_ms:.3f} ms, attention {attn_ms:.3f} ms")
+        del q, k, v, pyr, ws, aws, idx, score, fidx, fscore, fws, o
+        torch.cuda.empty_cache()
+    ln = np.log([r["N"] for r in rows])
+    slope = lambda key: float(np.polyfit(ln, np.log([r[key] for r in rows]), 1)[0]) if len(rows) > 1 else None
+    # first N where flat is slower, interpolated in log N between neighbours
+    cross = None
+    ratio = [r["flat_select_ms"] / r["select_ms"] for r in rows]
+    for i in range(1, len(rows)):
+        if ratio[i - 1] < 1.0 <= ratio[i]:
+            a, b = math.log(ratio[i - 1]), math.log(ratio[i])
+            f = -a / (b - a)
+            cross = round(math.exp(ln[i - 1] + f * (ln[i] - ln[i - 1])))
+    line = {
+        "metric": "PISA select vs flat select scaling (C=64, K=16), 1 GPU",
+        "value": cross,
+        "unit": "tokens (crossover N; null if not reached)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "scaling", "B": 1, "Hq": 32, "Hkv": 8, "d": 128, "C": 64, "g": 2, "K": 16,
+                   "causal": True, "needles": "leaf_per_query"},
+        "rows": rows,
+        "loglog_slope": {"select_ms": slope("select_ms"), "flat_select_ms": slope("flat_select_ms"),
+                         "attention_ms": slope("attention_ms")},
+        "flat_over_select": [round(x, 4) for x in ratio],
     }
     print(json.dumps(line), flush=True)
     return 0
