@@ -77,6 +77,8 @@ def load(path: str = _LIB_PATH):
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_flat_select.argtypes = [P, vp, vp, vp, i64, vp, vp]
     lib.oracle_flat_select.restype = ctypes.c_int
+    lib.oracle_exact_topk.argtypes = [P, vp, vp, vp, i64, vp, vp]
+    lib.oracle_exact_topk.restype = ctypes.c_int
     lib.oracle_counter_len.argtypes, lib.oracle_counter_len.restype = [], ctypes.c_int
     lib.oracle_threads.argtypes, lib.oracle_threads.restype = [], ctypes.c_int
     if path == _LIB_PATH:
@@ -209,6 +211,23 @@ def flat_select(p: Problem, q, k, ts=None, lib=None, q_sampled: bool = False):
                                 ts.ctypes.data, nt, idx.ctypes.data, score.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_flat_select failed ({rc})")
+    return idx, score
+
+
+def exact_topk(p: Problem, q, k, ts=None, lib=None, q_sampled: bool = False):
+    """Top-K over every valid leaf by the exact level-1 block score (raw-key
+    LSE summed over the group): what the descent returns when every leaf is a
+    candidate.  Returns (idx, score) shaped like select()'s."""
+    lib = lib or load()
+    q, k, ts = _c(q), _c(k), _ts(p, ts)
+    nt = len(ts)
+    _check_q(p, q, nt, q_sampled)
+    idx = np.empty((p.B, p.Hkv, nt, p.K), np.int32)
+    score = np.empty((p.B, p.Hkv, nt, p.K), np.float64)
+    rc = lib.oracle_exact_topk(ctypes.byref(p.c_struct(_dtype_code(q, k), q_sampled)), q.ctypes.data, k.ctypes.data,
+                               ts.ctypes.data, nt, idx.ctypes.data, score.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_exact_topk failed ({rc})")
     return idx, score
 
 

@@ -503,6 +503,55 @@ int oracle_flat_select(const oracle_problem* p, const void* q, const void* k, co
   return 0;
 }
 
+/* ---- public: exact leaf top-K (quality reference) --------------------- *
+ * Every valid leaf j is scored by the level-1 block score of [SEL] (the
+ * exact raw-key LSE, causally masked, summed over the GQA group) and the top
+ * K by (score desc, index asc) are kept: what the descent would return if
+ * every leaf were a candidate.  idx, score: [B][Hkv][nt][K], ascending,
+ * -1 / -inf padded.                                                          */
+int oracle_exact_topk(const oracle_problem* p, const void* q, const void* k, const int32_t* ts, int64_t nt,
+                      int32_t* idx, double* score) {
+  if (p->Hq % p->Hkv != 0) return 1;
+  const int32_t G = p->Hq / p->Hkv;
+  const int64_t M1 = oracle_level_rows(p->N, p->C, 1);
+  for (int32_t b = 0; b < p->B; ++b)
+    for (int32_t h = 0; h < p->Hkv; ++h) {
+      const int64_t kbase = ((int64_t)b * p->Hkv + h) * (int64_t)p->N * p->D;
+#pragma omp parallel
+      {
+        scored* all = (scored*)malloc(sizeof(scored) * M1);
+        double* buf = (double*)malloc(sizeof(double) * p->C);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t s = 0; s < nt; ++s) {
+          const int64_t t = ts[s];
+          int64_t n = 0;
+          for (int64_t j = 0; j < M1; ++j) {
+            if (p->causal && j * p->C > t) break;
+            double u = 0.0;
+            for (int32_t g = 0; g < G; ++g) {
+              int64_t nk = 0;
+              u += score_leaf(p, q, k, query_offset(p, b, h * G + g, t, s, nt), kbase, j, t, buf, &nk);
+            }
+            all[n].u = u;
+            all[n].j = j;
+            ++n;
+          }
+          qsort(all, (size_t)n, sizeof(scored), by_score_then_index);
+          const int64_t keep = n < p->K ? n : p->K;
+          qsort(all, (size_t)keep, sizeof(scored), by_index);
+          const int64_t o = ((int64_t)b * p->Hkv + h) * nt + s;
+          for (int32_t a = 0; a < p->K; ++a) {
+            idx[o * p->K + a] = (a < keep) ? (int32_t)all[a].j : -1;
+            score[o * p->K + a] = (a < keep) ? all[a].u : -INFINITY;
+          }
+        }
+        free(buf);
+        free(all);
+      }
+    }
+  return 0;
+}
+
 /* ---- public: pyramid of every (b, h) head, stacked [B][Hkv][rows][D] --- */
 int oracle_build_pyramid(const oracle_problem* p, const void* k, double* pyr) {
   const int64_t rows = oracle_pyramid_rows(p->N, p->C);

@@ -291,6 +291,37 @@ def check_bruteforce_leaf_topk(lib, causal: bool) -> None:
 
 
 # --------------------------------------------------------------------------
+# Exact leaf top-K (quality reference): the top K over every valid leaf of the
+# raw-key LSE summed over the group, against numpy/scipy brute force, with K
+# small enough that the descent prunes (so it cannot stand in for it)
+# --------------------------------------------------------------------------
+def check_exact_topk(lib, causal: bool) -> None:
+    N, G, D, C, K = 1000, 4, 32, 64, 3
+    q, k, _ = tiny_inputs(N=N, Hq=G, Hkv=1, D=D, seed=53)
+    p = oracle.Problem(1, N, G, 1, D, C, K, causal=causal)
+    ts = np.arange(0, N, 13)
+    idx, score = oracle.exact_topk(p, q, k, ts=ts, lib=lib)
+    qq, kk = q[0].astype(np.float64), k[0, 0].astype(np.float64)
+    z = np.einsum("gtd,nd->gtn", qq, kk) / math.sqrt(D)
+    M1 = -(-N // C)
+    pruned = 0
+    d_idx, _, _, _ = oracle.select(p, q, k, ts=ts, lib=lib)
+    for s_, t in enumerate(ts):
+        nleaf = min(t // C + 1, M1) if causal else M1
+        u = []
+        for j in range(nleaf):
+            hi = min(j * C + C, N, t + 1) if causal else min(j * C + C, N)
+            u.append(sum(logsumexp(z[g, t, j * C:hi]) for g in range(G)))
+        order = sorted(range(nleaf), key=lambda j: (-u[j], j))[:K]
+        got = idx[0, 0, s_]
+        assert got[: len(order)].tolist() == sorted(order), (t, got, sorted(order))
+        assert (got[len(order):] == -1).all()
+        np.testing.assert_allclose(score[0, 0, s_][: len(order)], [u[j] for j in sorted(order)], rtol=1e-12)
+        pruned += int(d_idx[0, 0, s_].tolist() != got.tolist())
+    assert pruned > 0  # the descent really differs somewhere: two independent paths
+
+
+# --------------------------------------------------------------------------
 # Shift invariance: k -> k + b shifts every LSE of a query head by q.b*scale
 # ([SEL] LSE score; [BSA] softmax), so idx and o are unchanged
 # --------------------------------------------------------------------------
@@ -460,6 +491,8 @@ ALL_CHECKS = [
     ("dense_causal", lambda lib: check_dense_equivalence(lib, True)),
     ("bruteforce_leaf_topk_noncausal", lambda lib: check_bruteforce_leaf_topk(lib, False)),
     ("bruteforce_leaf_topk_causal", lambda lib: check_bruteforce_leaf_topk(lib, True)),
+    ("exact_topk_noncausal", lambda lib: check_exact_topk(lib, False)),
+    ("exact_topk_causal", lambda lib: check_exact_topk(lib, True)),
     ("shift_noncausal", lambda lib: check_shift_invariance(lib, False)),
     ("shift_causal", lambda lib: check_shift_invariance(lib, True)),
     ("gqa", lambda lib: check_gqa(lib)),
