@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--scaling", action="store_true",
                     help="selection-time scaling and PISA-vs-flat crossover at C=64, K=16 over --scaling-n")
     ap.add_argument("--scaling-n", default="32768,65536,131072,262144,524288,1048576")
+    ap.add_argument("--io", action="store_true",
+                    help="one-stage vs two-stage selection at G_Q = 4 and 16 (N = 131072, C = 64, K = 16)")
     return ap.parse_args()
 
 
@@ -140,6 +142,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.scaling:
         return scaling_main(args)
+    if args.io:
+        return io_main(args)
     w = I.workload(args.workload)
     if w.steps:
         return decode_main(args, w)
@@ -465,6 +469,81 @@ def scaling_main(args) -> int:
         "loglog_slope": {"select_ms": slope("select_ms"), "flat_select_ms": slope("flat_select_ms"),
                          "attention_ms": slope("attention_ms")},
         "flat_over_select": [round(x, 4) for x in ratio],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def io_main(args) -> int:
+    """One-stage (fused descent to raw-key leaves, one program per query and
+    KV head) against two-stage selection (stage-1 routing, clusters, MFMA leaf
+    scoring over shared key tiles, final top-K) at G_Q = 4 (Hkv = 8) and
+    G_Q = 16 (Hkv = 2), Hq = 32, N = 131072, C = 64, K = 16, bf16, causal,
+    planted needle leaves.  Times each schedule with HIP events (pyramid
+    included), compares their selections, and gives the leaf-level bytes per
+    (query, candidate leaf) of the pages' IO comparison (one-stage: C key rows;
+    two-stage: G_Q query rows + C / Q_tile key rows, Q_tile = 4) next to this
+    design's (G_Q query rows + 2C key rows shared by the queries of a cluster
+    chunk)."""
+    import numpy as np
+    import torch
+
+    from hierarchical_block_sparse_mean_amd import inputs as I
+    from hierarchical_block_sparse_mean_amd import pisa
+
+    rows = []
+    for hkv in (8, 2):
+        G = 32 // hkv
+        w = I.Workload(f"io_g{G}", 1, 131072, 32, hkv, 128, 64, 16, "bf16", True, "leaf_per_query", seed=2000)
+        data = I.generate(w, with_v=False)
+        q, k = dev(data["q"]), dev(data["k"])
+        del data
+        out = {}
+        for algo, name in ((pisa.SELECT_TWO_STAGE, "two_stage"), (pisa.SELECT_FUSED, "one_stage")):
+            p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True, dtype="bf16", select_algo=algo)
+            pyr = pisa.alloc_pyramid(p)
+            ws = pisa.workspace(pisa.select_workspace_bytes(p))
+            idx = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device="cuda")
+            score = torch.empty_like(idx, dtype=torch.float32)
+
+            def run():
+                pisa.build_pyramid(p, k, pyr)
+                pisa.select(p, q, k, pyr, idx=idx, score=score, ws=ws)
+
+            run()
+            torch.cuda.synchronize()
+            pisa.timer_enable(True)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            kern = pisa.timer_report()
+            pisa.timer_enable(False)
+            out[name] = {"ms": e0.elapsed_time(e1) / args.steps, "idx": idx.cpu().numpy(),
+                         "kernels": {kk: round(vv[1] / max(1, vv[0]), 4) for kk, vv in kern.items()}}
+            log(f"G_Q={G} {name}: {out[name]['ms']:.3f} ms {out[name]['kernels']}")
+            del pyr, ws, idx, score
+        same = float((out["two_stage"]["idx"] == out["one_stage"]["idx"]).all(-1).mean())
+        d, C, qt, chunk = w.D, w.C, 4, 256
+        rows.append({
+            "G_Q": G, "Hkv": hkv,
+            "two_stage_ms": round(out["two_stage"]["ms"], 4), "one_stage_ms": round(out["one_stage"]["ms"], 4),
+            "two_stage_kernels_ms": out["two_stage"]["kernels"], "one_stage_kernels_ms": out["one_stage"]["kernels"],
+            "same_selection_rate": round(same, 5),
+            "leaf_bytes_per_pair": {"one_stage": C * d * 2, "two_stage_pages": (G + C // qt) * d * 2,
+                                    "two_stage_here": round(G * d * 2 + 2 * C * d * 2 / chunk, 1)},
+        })
+        del q, k
+        torch.cuda.empty_cache()
+    line = {
+        "metric": "PISA one-stage vs two-stage selection ms at N=131072, G_Q in {4, 16}, 1 GPU",
+        "value": rows[-1]["two_stage_ms"], "unit": "ms (two-stage, G_Q = 16)", "n_gpus": 1, "steps": args.steps,
+        "higher_is_better": False, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "io", "B": 1, "N": 131072, "Hq": 32, "d": 128, "C": 64, "g": 2, "K": 16,
+                   "causal": True, "needles": "leaf_per_query"},
+        "rows": rows,
     }
     print(json.dumps(line), flush=True)
     return 0
