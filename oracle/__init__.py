@@ -79,6 +79,8 @@ def load(path: str = _LIB_PATH):
     lib.oracle_flat_select.restype = ctypes.c_int
     lib.oracle_exact_topk.argtypes = [P, vp, vp, vp, i64, vp, vp]
     lib.oracle_exact_topk.restype = ctypes.c_int
+    lib.oracle_attention_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_attention_backward.restype = ctypes.c_int
     lib.oracle_counter_len.argtypes, lib.oracle_counter_len.restype = [], ctypes.c_int
     lib.oracle_threads.argtypes, lib.oracle_threads.restype = [], ctypes.c_int
     if path == _LIB_PATH:
@@ -212,6 +214,28 @@ def flat_select(p: Problem, q, k, ts=None, lib=None, q_sampled: bool = False):
     if rc != 0:
         raise ValueError(f"oracle_flat_select failed ({rc})")
     return idx, score
+
+
+def attention_backward(p: Problem, q, k, v, idx, dout, lib=None):
+    """Gradients of L = sum_t dout_t . o_t for attention over the fixed
+    selection idx [B][Hkv][N][K] (every position).  Returns (dq, dk, dv) in
+    float64, shaped like q, k, v."""
+    lib = lib or load()
+    q, k, v, dout = _c(q), _c(k), _c(v), _c(dout)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    if q.shape != (p.B, p.Hq, p.N, p.D) or dout.shape != q.shape:
+        raise ValueError(f"q / dout shape {q.shape} / {dout.shape} != {(p.B, p.Hq, p.N, p.D)}")
+    if idx.shape != (p.B, p.Hkv, p.N, p.K):
+        raise ValueError(f"idx shape {idx.shape} != {(p.B, p.Hkv, p.N, p.K)}")
+    dq = np.empty(q.shape, np.float64)
+    dk = np.empty(k.shape, np.float64)
+    dv = np.empty(v.shape, np.float64)
+    rc = lib.oracle_attention_backward(ctypes.byref(p.c_struct(_dtype_code(q, k, v, dout))), q.ctypes.data,
+                                       k.ctypes.data, v.ctypes.data, idx.ctypes.data, dout.ctypes.data,
+                                       dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attention_backward failed ({rc})")
+    return dq, dk, dv
 
 
 def exact_topk(p: Problem, q, k, ts=None, lib=None, q_sampled: bool = False):

@@ -453,6 +453,89 @@ int oracle_attention(const oracle_problem* p, const void* q, const void* k, cons
   return 0;
 }
 
+/* ---- public: gradients of [BSA] attention over a fixed selection ------- *
+ * o_t = sum_i p_i v_i with p = softmax(z), z_i = q_t . k_i * scale over the
+ * keys i of the kept leaves (i <= t when causal).  For L = sum_t dO_t . o_t:
+ *   dv_i += p_i dO_t,   dp_i = dO_t . v_i,   D_t = dO_t . o_t,
+ *   ds_i = p_i (dp_i - D_t),   dq_t = scale sum_i ds_i k_i,
+ *   dk_i += scale ds_i q_t.
+ * The selection is index-valued, so no gradient flows through it.  Every
+ * position t in [0, N): idx [B][Hkv][N][K]; q, dout [B][Hq][N][D] (dtype of
+ * the problem); k, v [B][Hkv][N][D].  dq [B][Hq][N][D], dk, dv [B][Hkv][N][D]
+ * in fp64.                                                                   */
+int oracle_attention_backward(const oracle_problem* p, const void* q, const void* k, const void* v,
+                              const int32_t* idx, const void* dout, double* dq, double* dk, double* dv) {
+  if (p->Hq % p->Hkv != 0 || p->q_sampled) return 1;
+  const int32_t G = p->Hq / p->Hkv;
+  const int64_t N = p->N;
+  const int32_t D = p->D;
+  memset(dq, 0, sizeof(double) * (size_t)p->B * p->Hq * N * D);
+  memset(dk, 0, sizeof(double) * (size_t)p->B * p->Hkv * N * D);
+  memset(dv, 0, sizeof(double) * (size_t)p->B * p->Hkv * N * D);
+#pragma omp parallel
+  {
+    const int64_t cap = (int64_t)p->K * p->C;
+    double* z = (double*)malloc(sizeof(double) * (cap > 0 ? cap : 1));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (cap > 0 ? cap : 1));
+    double* o = (double*)malloc(sizeof(double) * D);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)p->B * p->Hkv; ++bh) {  /* a head's dk, dv belong to one thread */
+      const int32_t b = (int32_t)(bh / p->Hkv), h = (int32_t)(bh % p->Hkv);
+      const int64_t kvbase = bh * N * D;
+      for (int64_t t = 0; t < N; ++t) {
+        const int32_t* sel = idx + (bh * N + t) * p->K;
+        int64_t n = 0;
+        for (int32_t a = 0; a < p->K; ++a) {
+          const int64_t j = sel[a];
+          if (j < 0) continue;
+          const int64_t lo = j * p->C, hi = lo + p->C < N ? lo + p->C : N;
+          for (int64_t i = lo; i < hi; ++i) {
+            if (p->causal && i > t) break;
+            key[n++] = i;
+          }
+        }
+        if (n == 0) continue;
+        for (int32_t g = 0; g < G; ++g) {
+          const int32_t hq = h * G + g;
+          const int64_t qoff = (((int64_t)b * p->Hq + hq) * N + t) * D;
+          double m = -INFINITY;
+          for (int64_t a = 0; a < n; ++a) {
+            z[a] = dot_qk(q, k, p->dtype, qoff, kvbase + key[a] * D, D) * p->scale;
+            if (z[a] > m) m = z[a];
+          }
+          double den = 0.0;
+          for (int64_t a = 0; a < n; ++a) {
+            z[a] = exp(z[a] - m);
+            den += z[a];
+          }
+          for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+          for (int64_t a = 0; a < n; ++a) {
+            z[a] /= den; /* p_i */
+            for (int32_t d = 0; d < D; ++d) o[d] += z[a] * widen(v, p->dtype, kvbase + key[a] * D + d);
+          }
+          double Dt = 0.0;
+          for (int32_t d = 0; d < D; ++d) Dt += widen(dout, p->dtype, qoff + d) * o[d];
+          for (int64_t a = 0; a < n; ++a) {
+            const int64_t ko = kvbase + key[a] * D;
+            double dp = 0.0;
+            for (int32_t d = 0; d < D; ++d) dp += widen(dout, p->dtype, qoff + d) * widen(v, p->dtype, ko + d);
+            const double ds = z[a] * (dp - Dt);
+            for (int32_t d = 0; d < D; ++d) {
+              dq[qoff + d] += p->scale * ds * widen(k, p->dtype, ko + d);
+              dk[ko + d] += p->scale * ds * widen(q, p->dtype, qoff + d);
+              dv[ko + d] += z[a] * widen(dout, p->dtype, qoff + d);
+            }
+          }
+        }
+      }
+    }
+    free(z);
+    free(key);
+    free(o);
+  }
+  return 0;
+}
+
 /* ---- public: [BSA-flat] single-level selector -------------------------- *
  * Every valid leaf j is scored by sum over the GQA group of
  * q_{h',t} . P_1[j] * scale; the top K by (score desc, index asc) are kept.

@@ -322,6 +322,82 @@ def check_exact_topk(lib, causal: bool) -> None:
 
 
 # --------------------------------------------------------------------------
+# Attention backward: the gradients of L = sum_t dO_t . o_t over a fixed
+# selection ([BSA] o_t equation; no gradient through the index-valued
+# selection).  Pinned by central finite differences of the forward oracle on
+# dyadic-exact perturbations, and by torch fp64 autograd of dense attention
+# when every leaf is kept.
+# --------------------------------------------------------------------------
+def _random_selection(rng, B, Hkv, N, C, K, causal):
+    M1 = -(-N // C)
+    idx = np.full((B, Hkv, N, K), -1, np.int32)
+    for b in range(B):
+        for h in range(Hkv):
+            for t in range(N):
+                nvalid = min(t // C + 1, M1) if causal else M1
+                pick = np.sort(rng.choice(nvalid, size=min(K, nvalid), replace=False))
+                idx[b, h, t, : len(pick)] = pick
+    return idx
+
+
+def check_backward_finite_difference(lib, causal: bool) -> None:
+    B, N, G, Hkv, D, C, K = 1, 150, 2, 2, 16, 32, 2
+    Hq = G * Hkv
+    q = _bf16_valued_f32(71, 1, (B, Hq, N, D))
+    k = _bf16_valued_f32(71, 2, (B, Hkv, N, D))
+    v = _bf16_valued_f32(71, 3, (B, Hkv, N, D))
+    dO = _bf16_valued_f32(71, 4, (B, Hq, N, D))
+    rng = np.random.default_rng(72)
+    idx = _random_selection(rng, B, Hkv, N, C, K, causal)
+    p = oracle.Problem(B, N, Hq, Hkv, D, C, K, causal=causal)
+    dq, dk, dv = oracle.attention_backward(p, q, k, v, idx, dO, lib=lib)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(p, qq, kk, vv, idx, lib=lib)
+        return float((o * dO.astype(np.float64)).sum())
+
+    h = 2.0 ** -9  # x +- h stays exact in float32 for bf16-valued x
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for flat in rng.choice(arr.size, size=12, replace=False):
+            at = np.unravel_index(flat, arr.shape)
+            xp, xm = arr.copy(), arr.copy()
+            xp[at] += h
+            xm[at] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            assert abs(fd - grad[at]) <= 2e-4 * max(1.0, abs(grad[at])), (name, at, fd, grad[at])
+
+
+def check_backward_dense(lib, causal: bool) -> None:
+    import torch
+
+    N, G, D, C = 256, 2, 32, 64
+    q, k, v = tiny_inputs(N=N, Hq=G, Hkv=1, D=D, seed=73)
+    dO = I.normal(73, 4, G * N * D, dtype="f32").reshape(1, G, N, D)
+    M1 = N // C
+    idx = np.broadcast_to(np.arange(M1, dtype=np.int32), (1, 1, N, M1)).copy()
+    if causal:
+        for t in range(N):
+            idx[0, 0, t, t // C + 1:] = -1
+    p = oracle.Problem(1, N, G, 1, D, C, M1, causal=causal)
+    dq, dk, dv = oracle.attention_backward(p, q, k, v, idx, dO, lib=lib)
+    tq = torch.tensor(q[0], dtype=torch.float64, requires_grad=True)
+    tk = torch.tensor(k[0, 0], dtype=torch.float64, requires_grad=True)
+    tv = torch.tensor(v[0, 0], dtype=torch.float64, requires_grad=True)
+    z = torch.einsum("gtd,nd->gtn", tq, tk) / math.sqrt(D)
+    if causal:
+        mask = torch.arange(N)[None, None, :] > torch.arange(N)[None, :, None]
+        z = z.masked_fill(mask, float("-inf"))
+    o = torch.softmax(z, dim=-1) @ tv
+    (o * torch.tensor(dO[0], dtype=torch.float64)).sum().backward()
+    np.testing.assert_allclose(dq[0], tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk[0, 0], tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv[0, 0], tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # Shift invariance: k -> k + b shifts every LSE of a query head by q.b*scale
 # ([SEL] LSE score; [BSA] softmax), so idx and o are unchanged
 # --------------------------------------------------------------------------
@@ -493,6 +569,10 @@ ALL_CHECKS = [
     ("bruteforce_leaf_topk_causal", lambda lib: check_bruteforce_leaf_topk(lib, True)),
     ("exact_topk_noncausal", lambda lib: check_exact_topk(lib, False)),
     ("exact_topk_causal", lambda lib: check_exact_topk(lib, True)),
+    ("backward_fd_noncausal", lambda lib: check_backward_finite_difference(lib, False)),
+    ("backward_fd_causal", lambda lib: check_backward_finite_difference(lib, True)),
+    ("backward_dense_noncausal", lambda lib: check_backward_dense(lib, False)),
+    ("backward_dense_causal", lambda lib: check_backward_dense(lib, True)),
     ("shift_noncausal", lambda lib: check_shift_invariance(lib, False)),
     ("shift_causal", lambda lib: check_shift_invariance(lib, True)),
     ("gqa", lambda lib: check_gqa(lib)),

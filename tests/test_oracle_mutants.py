@@ -37,6 +37,9 @@ MUTANTS = [
     ("keeps_one_block_too_few", "      nI = K;\n", "      nI = K > 1 ? K - 1 : 1;\n"),
     ("flat_uses_first_head_only", "            for (int32_t g = 0; g < G; ++g) {\n              int64_t qoff",
      "            for (int32_t g = 0; g < 1; ++g) {\n              int64_t qoff"),
+    ("backward_drops_row_term", "            const double ds = z[a] * (dp - Dt);", "            const double ds = z[a] * dp;"),
+    ("backward_dk_unscaled", "              dk[ko + d] += p->scale * ds * widen(q, p->dtype, qoff + d);",
+     "              dk[ko + d] += ds * widen(q, p->dtype, qoff + d);"),
 ]
 
 
