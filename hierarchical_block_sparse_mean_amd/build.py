@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpisa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "pyramid.hip", "route.hip", "select2.hip", "cluster.hip", "attn_leaf.hip", "flat.hip", "decode.hip"]
+SOURCES = ["api.hip", "pyramid.hip", "route.hip", "select2.hip", "cluster.hip", "attn_leaf.hip", "attn_bwd.hip",
+           "flat.hip", "decode.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # no packed-fp32 instructions (v_pk_fma_f32 and friends)

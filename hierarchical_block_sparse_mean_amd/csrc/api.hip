@@ -281,6 +281,29 @@ pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k
   return hip_status(pisa::launch_attn_leaf(pr, q, k, v, idx, o, lse, ws, stream), "pisa_sparse_attn (leaf-major)");
 }
 
+size_t pisa_attn_backward_workspace_bytes(const pisa_problem* p) {
+  pisa::Problem q;
+  if (validate(p, &q) != PISA_OK) return 0;
+  return pisa::attn_bwd_workspace_bytes(q);
+}
+
+pisa_status pisa_sparse_attn_backward(const pisa_problem* p, const void* q, const void* k, const void* v,
+                                      const int32_t* idx, const void* o, const float* lse, const void* dout,
+                                      void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  pisa::Problem pr;
+  pisa_status s = validate(p, &pr);
+  if (s != PISA_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || o == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "q, k, v, idx, o, lse, dout, dq, dk and dv must be non-NULL");
+  const size_t need = pisa::attn_bwd_workspace_bytes(pr);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws == nullptr ? 0 : ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(PISA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return hip_status(pisa::launch_attn_bwd(pr, q, k, v, idx, o, lse, dout, dq, dk, dv, ws, stream),
+                    "pisa_sparse_attn_backward");
+}
+
 size_t pisa_flat_workspace_bytes(const pisa_problem* p) {
   pisa::Problem q;
   if (validate(p, &q) != PISA_OK) return 0;

@@ -1,0 +1,462 @@
+// Backward of the block-sparse attention ("Block Sparse Attention with
+// Log-Linear Complexity", hyper.ai page, section "block-sparse attention", the
+// o_t equation; the page names training kernels but gives no backward, so
+// this is the calculus of that equation over a fixed selection: the selection
+// is index-valued and carries no gradient).  With p = softmax(z),
+// z_i = q_t . k_i * scale over the keys of the kept leaves (i <= t causally)
+// and L = sum_t dO_t . o_t:
+//   D_t = dO_t . o_t,  dP_i = dO_t . v_i,  dS_i = p_i (dP_i - D_t),
+//   dq_t = scale sum_i dS_i k_i,  dk_i += scale dS_i q_t,  dv_i += p_i dO_t.
+//
+// Leaf-major, like the forward: the kept (query, leaf) pairs are clustered by
+// leaf; a workgroup holds the leaf's K, V and K^T in LDS and walks its query
+// tiles (16 columns = 16/G_Q queries x G_Q heads), all waves on one tile:
+//   phase A (waves split the 16-key blocks): S^T = K Q^T and dP^T = V dO^T on
+//     MFMA, p = exp(z - lse) from the forward's lse, dS = p (dP - D), both
+//     written to LDS;
+//   phase B (waves split the 16-dim blocks): dV^T += dO^T P and dK^T += Q^T dS
+//     (16x16x16 MFMA over the tile's columns, accumulated in registers across
+//     tiles), and dQ^T = K^T dS^T (16x16x32 MFMA over the keys) written as a
+//     partial per (query, slot, head).
+// At the end of its chunk a workgroup adds its dK, dV sums into fp32
+// accumulators (atomics: a leaf's queries may span several chunks); a merge
+// kernel sums each query's K partial dQ rows, a last pass converts dK, dV.
+#include "kernels.h"
+
+namespace pisa {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdChunk = 256;                   // (query, slot) pairs per workgroup
+constexpr size_t kBwdBudget = (size_t)8 << 30;  // partial dQ rows per head chunk
+
+static size_t b256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  int64_t heads, M1, ncl, slots;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_dq, off_hist, off_rowdot, off_dk, off_dv,
+      total;
+};
+
+static BwdLayout bwd_layout(const Problem& p) {
+  BwdLayout L{};
+  L.M1 = level_rows(p.N, p.C, 1);
+  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * p.D * 4) + (size_t)L.M1 * 16;
+  const int64_t BH = (int64_t)p.B * p.Hkv;
+  int64_t hmax = (int64_t)(kBwdBudget / per_head);
+  if (hmax < 1) hmax = 1;
+  if (hmax > BH) hmax = BH;
+  const int64_t nchunks = (BH + hmax - 1) / hmax;
+  L.heads = (BH + nchunks - 1) / nchunks;
+  L.ncl = L.heads * L.M1;
+  L.slots = L.heads * (int64_t)p.N * p.K;
+  size_t off = 0;
+  L.off_counts = off;
+  off = b256(off + 4 * (size_t)L.ncl);
+  L.off_cursor = off;
+  off = b256(off + 4 * (size_t)L.ncl);
+  L.off_offsets = off;
+  off = b256(off + 4 * (size_t)(L.ncl + 1));
+  L.off_chunks = off;
+  off = b256(off + 4 * (size_t)(L.ncl + 1));
+  L.off_pairs = off;
+  off = b256(off + 4 * (size_t)L.slots);
+  L.off_dq = off;
+  off = b256(off + 4 * (size_t)L.slots * p.G * p.D);
+  L.off_hist = off;
+  off = b256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.M1));
+  L.off_rowdot = off;
+  off = b256(off + 4 * (size_t)p.B * p.Hq * p.N);
+  L.off_dk = off;
+  off = b256(off + 4 * (size_t)BH * p.N * p.D);
+  L.off_dv = off;
+  off = b256(off + 4 * (size_t)BH * p.N * p.D);
+  L.total = off;
+  return L;
+}
+
+size_t attn_bwd_workspace_bytes(const Problem& p) { return bwd_layout(p).total; }
+
+// ---- D_t = dO_t . o_t per (b, query head, t) ----------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ dout, const T* __restrict__ o, int64_t rows,
+                                                     float* __restrict__ rowdot) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LPR;
+  const int sub = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < rows) {
+    float x[8], y[8];
+    load8<T>(dout + row * D + sub * 8, x);
+    load8<T>(o + row * D + sub * 8, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(x[e], y[e], s);
+  }
+  s = group_sum<LPR>(s);
+  if (row < rows && sub == 0) rowdot[row] = s;
+}
+
+// ---- 16x16x16 MFMA: lane group g supplies contraction elements 4g .. 4g+3 ----
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx4 mma16(const float* a4, const float* b4, floatx4 acc, uint16_t) {
+  shortx4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (short)f32_to_bf16(a4[i]);
+    b[i] = (short)f32_to_bf16(b4[i]);
+  }
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma16(const float* a4, const float* b4, floatx4 acc, float) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], b4[i], acc, 0, 0, 0);
+  return acc;
+}
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* rowdot;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* chunk_off;
+  const int32_t* pairs;
+  float* dq_part;  // [heads][N][K][G][D]
+  float* dk_acc;   // [B][Hkv][N][D]
+  float* dv_acc;
+  int64_t ncl, M1, head0;
+  int32_t N, Hq, Hkv, C, K;
+  int32_t causal;
+  int64_t cap;
+  float scale;
+};
+
+template <typename T, int D, int G, int NKB>
+__global__ __launch_bounds__(kBwdWaves* kWave) void attn_bwd_kernel(BwdArgs a) {
+  constexpr int NS = D / 32;
+  constexpr int TQ = 16 / G;
+  constexpr int CP = NKB * 16;
+  constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int KP = D + EPV;               // row pitch of K, V, q, dO tiles
+  constexpr int TP = CP + EPV;              // row pitch of K^T
+  constexpr int NDB = D / 16;
+  constexpr int DBW = NDB / kBwdWaves;  // dim blocks per wave
+  constexpr float kLog2e = 1.4426950408889634f;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
+  T* s_v = s_k + CP * KP;                    // [CP][KP]
+  T* s_kt = s_v + CP * KP;                   // [D][TP]
+  __shared__ __align__(16) T s_q[16][KP];    // the tile's query rows, one per column
+  __shared__ __align__(16) T s_do[16][KP];   // and their output gradients
+  __shared__ __align__(16) float s_p[CP][16];
+  __shared__ __align__(16) float s_ds[CP][16];
+  __shared__ float s_lse[16], s_rd[16];
+  __shared__ int32_t s_pr[16];
+
+  const int64_t chunk = blockIdx.x;
+  if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
+  int64_t lo = 0, hi = a.ncl;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a.chunk_off[mid] <= chunk) lo = mid;
+    else hi = mid;
+  }
+  const int64_t c = lo;
+  const int64_t hl = c / a.M1;
+  const int64_t j = c % a.M1;
+  const int64_t bh = a.head0 + hl;
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kBwdChunk;
+  const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
+  const int64_t p_end = p_begin + kBwdChunk < p_end_c ? p_begin + kBwdChunk : p_end_c;
+
+  const int64_t key0 = j * (int64_t)a.C;
+  const int nkeys = (int)((a.N - key0) < a.C ? (a.N - key0) : a.C);
+  const T* kh = static_cast<const T*>(a.k) + bh * a.cap * D;
+  const T* vh = static_cast<const T*>(a.v) + bh * a.cap * D;
+  for (int i = threadIdx.x; i < CP * (D / EPV); i += blockDim.x) {
+    const int r = i / (D / EPV), d = (i % (D / EPV)) * EPV;
+    uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (r < nkeys) {
+      kv = *reinterpret_cast<const uint4*>(kh + (key0 + r) * D + d);
+      vv = *reinterpret_cast<const uint4*>(vh + (key0 + r) * D + d);
+    }
+    *reinterpret_cast<uint4*>(s_k + r * KP + d) = kv;
+    *reinterpret_cast<uint4*>(s_v + r * KP + d) = vv;
+    const T* ke = reinterpret_cast<const T*>(&kv);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s_kt[(d + e) * TP + r] = ke[e];
+  }
+
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+  const float sl2 = a.scale * kLog2e;
+  const T* qb = static_cast<const T*>(a.q);
+  const T* gb = static_cast<const T*>(a.dout);
+  floatx4 dvt[DBW][NKB], dkt[DBW][NKB];
+#pragma unroll
+  for (int di = 0; di < DBW; ++di)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      dvt[di][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dkt[di][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  for (int64_t tile = p_begin; tile < p_end; tile += TQ) {
+    // stage the tile: column cc = query cc / G (pair tile + cc / G) x head cc % G
+    if (threadIdx.x < 16) {
+      const int cc = threadIdx.x;
+      const int32_t pr = tile + cc / G < p_end ? a.pairs[tile + cc / G] : -1;
+      s_pr[cc] = pr;
+      const int64_t row = ((int64_t)b * a.Hq + h * G + cc % G) * a.N + (pr >> 5);
+      s_lse[cc] = pr >= 0 ? a.lse[row] : 0.f;
+      s_rd[cc] = pr >= 0 ? a.rowdot[row] : 0.f;
+    }
+    for (int i = threadIdx.x; i < 16 * (D / EPV); i += blockDim.x) {
+      const int cc = i / (D / EPV), d = (i % (D / EPV)) * EPV;
+      const int32_t pr = tile + cc / G < p_end ? a.pairs[tile + cc / G] : -1;
+      uint4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+      if (pr >= 0) {
+        const int64_t row = ((int64_t)b * a.Hq + h * G + cc % G) * a.N + (pr >> 5);
+        qv = *reinterpret_cast<const uint4*>(qb + row * D + d);
+        gv = *reinterpret_cast<const uint4*>(gb + row * D + d);
+      }
+      *reinterpret_cast<uint4*>(&s_q[cc][d]) = qv;
+      *reinterpret_cast<uint4*>(&s_do[cc][d]) = gv;
+    }
+    __syncthreads();
+    // phase A: key blocks of this wave
+    {
+      Frag<T> fq[NS], fg[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        fq[s].load(&s_q[col][g * (D / 4) + 8 * s]);
+        fg[s].load(&s_do[col][g * (D / 4) + 8 * s]);
+      }
+      const int32_t prc = s_pr[col];
+      int lim = 0;
+      if (prc >= 0) {
+        const int64_t t = prc >> 5;
+        lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
+      }
+      const float lse2 = s_lse[col] * kLog2e, rd = s_rd[col];
+      for (int kb = w; kb < NKB; kb += kBwdWaves) {
+        floatx4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          Frag<T> fk, fv;
+          fk.load(s_k + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+          fv.load(s_v + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+          st = mma(fk, fq[s], st);
+          dpt = mma(fv, fg[s], dpt);
+        }
+        // lane (g, col): keys kb*16 + 4g + i of column col
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb * 16 + 4 * g + i;
+          const float pv = key < lim ? exp2_nonpos(fminf(fmaf(st[i], sl2, -lse2), 0.f)) : 0.f;
+          s_p[key][col] = pv;
+          s_ds[key][col] = pv * (dpt[i] - rd);
+        }
+      }
+    }
+    __syncthreads();
+    // phase B: dim blocks of this wave
+#pragma unroll
+    for (int di = 0; di < DBW; ++di) {
+      const int db = w * DBW + di;
+      const int dim = db * 16 + col;  // A row of this lane
+      float ag[4], aq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ag[e] = load1<T>(&s_do[4 * g + e][dim]);
+        aq[e] = load1<T>(&s_q[4 * g + e][dim]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float4 pp = *reinterpret_cast<const float4*>(&s_p[kb * 16 + col][4 * g]);
+        const float4 dd = *reinterpret_cast<const float4*>(&s_ds[kb * 16 + col][4 * g]);
+        const float bp[4] = {pp.x, pp.y, pp.z, pp.w};
+        const float bd[4] = {dd.x, dd.y, dd.z, dd.w};
+        dvt[di][kb] = mma16(ag, bp, dvt[di][kb], T{});
+        dkt[di][kb] = mma16(aq, bd, dkt[di][kb], T{});
+      }
+      // dQ^T for these 16 dims: K^T (dims x keys) times dS^T (keys x columns)
+      floatx4 dqt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < CP / 32; ++ks) {
+        Frag<T> fa, fb;
+        fa.load(s_kt + dim * TP + ks * 32 + g * 8);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = s_ds[ks * 32 + g * 8 + e][col];
+        fb.set(x);
+        dqt = mma(fa, fb, dqt);
+      }
+      // lane (g, col): dims db*16 + 4g + i of column col
+      const int32_t pc = s_pr[col];
+      if (pc >= 0) {
+        const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (col % G);
+        *reinterpret_cast<float4*>(a.dq_part + rec * D + db * 16 + 4 * g) =
+            float4{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale, dqt[3] * a.scale};
+      }
+    }
+    __syncthreads();  // the next tile restages s_q, s_do, s_p, s_ds
+  }
+  // this chunk's share of dK, dV: lane (g, col) holds dims db*16 + 4g + i of key kb*16 + col
+#pragma unroll
+  for (int di = 0; di < DBW; ++di) {
+    const int db = w * DBW + di;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int key = kb * 16 + col;
+      if (key < nkeys) {
+        float* dkr = a.dk_acc + (bh * a.N + key0 + key) * D + db * 16 + 4 * g;
+        float* dvr = a.dv_acc + (bh * a.N + key0 + key) * D + db * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          atomicAdd(dkr + i, dkt[di][kb][i] * a.scale);
+          atomicAdd(dvr + i, dvt[di][kb][i]);
+        }
+      }
+    }
+  }
+}
+
+// ---- dq = sum of the K partial rows of every (query, head) -----------------------
+struct BwdMergeArgs {
+  const int32_t* idx;
+  const float* dq_part;
+  void* dq;
+  int64_t head0, heads, M1;
+  int32_t N, Hq, Hkv, K;
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void bwd_merge_kernel(BwdMergeArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (wid >= a.heads * a.N) return;
+  const int lane = lane_id();
+  const int64_t hl = wid / a.N, t = wid % a.N;
+  const int64_t bh = a.head0 + hl;
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  const int32_t* sel = a.idx + (bh * a.N + t) * a.K;
+  const int64_t rec0 = (hl * a.N + t) * a.K * G;
+  for (int e0 = lane * 4; e0 < G * D; e0 += kWave * 4) {
+    const int hh = e0 / D, d = e0 % D;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.K; ++s) {
+      const int32_t jl = sel[s];
+      if (jl < 0 || jl >= a.M1) continue;
+      const float4 v = *reinterpret_cast<const float4*>(a.dq_part + (rec0 + s * G + hh) * D + d);
+      acc[0] += v.x;
+      acc[1] += v.y;
+      acc[2] += v.z;
+      acc[3] += v.w;
+    }
+    T* out = static_cast<T*>(a.dq) + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D + d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store1<T>(out + i, acc[i]);
+  }
+}
+
+__global__ void zero_f32_kernel(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+// dk, dv [B][Hkv][cap][D] rows < N from the fp32 accumulators [B][Hkv][N][D]
+template <typename T>
+__global__ void bwd_store_kernel(const float* __restrict__ acc, T* out, int64_t BH, int64_t N, int64_t cap,
+                                 int32_t D) {
+  const int64_t n = BH * N * D;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / D, d = i % D;
+    const int64_t bh = row / N, r = row % N;
+    store1<T>(out + (bh * cap + r) * D + d, acc[i]);
+  }
+}
+
+hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                           hipStream_t stream) {
+  const BwdLayout L = bwd_layout(p);
+  char* base = static_cast<char*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
+  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
+  int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
+  float* dq_part = reinterpret_cast<float*>(base + L.off_dq);
+  float* rowdot = reinterpret_cast<float*>(base + L.off_rowdot);
+  float* dk_acc = reinterpret_cast<float*>(base + L.off_dk);
+  float* dv_acc = reinterpret_cast<float*>(base + L.off_dv);
+  const int64_t BH = (int64_t)p.B * p.Hkv;
+  const int64_t acc_n = BH * p.N * p.D;
+  const unsigned zb = (unsigned)((acc_n + 255) / 256 < 65536 ? (acc_n + 255) / 256 : 65536);
+  PISA_LAUNCH("bwd_zero", stream, zero_f32_kernel, dim3(zb), dim3(256), 0, dk_acc, acc_n);
+  PISA_LAUNCH("bwd_zero", stream, zero_f32_kernel, dim3(zb), dim3(256), 0, dv_acc, acc_n);
+  hipError_t err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto) -> hipError_t {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    constexpr int D = decltype(dc)::value;
+    const int64_t rows = (int64_t)p.B * p.Hq * p.N;
+    const int64_t threads = rows * (D / 8);
+    PISA_LAUNCH("bwd_rowdot", stream, (rowdot_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                static_cast<const T*>(dout), static_cast<const T*>(o), rows, rowdot);
+    return hipGetLastError();
+  });
+  if (err != hipSuccess) return err;
+  for (int64_t head0 = 0; head0 < BH; head0 += L.heads) {
+    const int64_t heads = (BH - head0) < L.heads ? (BH - head0) : L.heads;
+    const int64_t entries = heads * p.N * p.K;
+    const int64_t ncl = heads * L.M1;
+    const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
+    err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kBwdChunk, cb, stream);
+    if (err != hipSuccess) return err;
+    BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1,
+               head0, p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
+    BwdMergeArgs ma{idx, dq_part, dq, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
+    const int64_t max_chunks = (entries + kBwdChunk - 1) / kBwdChunk + ncl;
+    err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
+      using T = std::remove_pointer_t<decltype(tp)>;
+      constexpr int D = decltype(dc)::value;
+      constexpr int G = decltype(gc)::value;
+      auto run = [&](auto kern, int nkb) -> hipError_t {
+        const int cp = nkb * 16, epv = 16 / (int)sizeof(T);
+        const size_t lds = (2 * (size_t)cp * (D + epv) + (size_t)D * (cp + epv)) * sizeof(T);
+        if (lds > 65536) {
+          hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (e != hipSuccess) return e;
+        }
+        PISA_LAUNCH("attn_bwd", stream, kern, dim3((unsigned)max_chunks), dim3(kBwdWaves * kWave), lds, ba);
+        return hipGetLastError();
+      };
+      hipError_t e;
+      if (p.C <= 32)
+        e = run(attn_bwd_kernel<T, D, G, 2>, 2);
+      else if (p.C <= 64)
+        e = run(attn_bwd_kernel<T, D, G, 4>, 4);
+      else
+        e = run(attn_bwd_kernel<T, D, G, 8>, 8);
+      if (e != hipSuccess) return e;
+      const int64_t waves = heads * p.N;
+      PISA_LAUNCH("bwd_merge", stream, (bwd_merge_kernel<T, D, G>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                  ma);
+      return hipGetLastError();
+    });
+    if (err != hipSuccess) return err;
+  }
+  return dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto, auto) -> hipError_t {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    PISA_LAUNCH("bwd_store", stream, bwd_store_kernel<T>, dim3(zb), dim3(256), 0, dk_acc, static_cast<T*>(dk), BH,
+                (int64_t)p.N, p.cap, p.D);
+    PISA_LAUNCH("bwd_store", stream, bwd_store_kernel<T>, dim3(zb), dim3(256), 0, dv_acc, static_cast<T*>(dv), BH,
+                (int64_t)p.N, p.cap, p.D);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace pisa

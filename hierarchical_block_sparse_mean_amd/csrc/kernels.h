@@ -98,6 +98,12 @@ size_t attn_leaf_workspace_bytes(const Problem& p);
 hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
                             void* o, float* lse, void* ws, hipStream_t stream);
 
+// attn_bwd.hip: leaf-major backward of the sparse attention
+size_t attn_bwd_workspace_bytes(const Problem& p);
+hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                           hipStream_t stream);
+
 // flat.hip
 hipError_t launch_flat(const Problem& p, const void* q, const float* pyr, int32_t* idx, float* score,
                        hipStream_t stream);

@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "PISA_OK", 1: "PISA_ERR_INVALID_ARG", 2: "PISA_ERR_UNSUPPORTE
 EXPORTS = [
     "pisa_pyramid_bytes", "pisa_levels", "pisa_level_rows", "pisa_level_offset", "pisa_build_pyramid",
     "pisa_select_workspace_bytes", "pisa_select", "pisa_attn_workspace_bytes", "pisa_sparse_attn",
-    "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
+    "pisa_attn_backward_workspace_bytes", "pisa_sparse_attn_backward", "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
     "pisa_route_counts",
     "pisa_last_error", "pisa_version",
 ]
@@ -82,6 +82,8 @@ def load(path: str = LIB_PATH):
         "pisa_select": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_attn_workspace_bytes": ([P], sz),
         "pisa_sparse_attn": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "pisa_attn_backward_workspace_bytes": ([P], sz),
+        "pisa_sparse_attn_backward": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_flat_workspace_bytes": ([P], sz),
         "pisa_flat_select": ([P, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_decode_step": ([DP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -270,6 +272,36 @@ def sparse_attn(p: Problem, q, k, v, idx, o=None, lse=None, ws=None, with_lse: b
 
 def flat_workspace_bytes(p: Problem) -> int:
     return load().pisa_flat_workspace_bytes(ctypes.byref(p.c()))
+
+
+def attn_backward_workspace_bytes(p: Problem) -> int:
+    return load().pisa_attn_backward_workspace_bytes(ctypes.byref(p.c()))
+
+
+def sparse_attn_backward(p: Problem, q, k, v, idx, o, lse, dout, dq=None, dk=None, dv=None, ws=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * o) for the attention over the fixed
+    selection idx; o and lse are the forward's outputs."""
+    _need(q, "q", (p.B, p.Hq, p.N, p.D), p.torch_dtype)
+    _need(k, "k", (p.B, p.Hkv, p.cap_tokens, p.D), p.torch_dtype)
+    _need(v, "v", (p.B, p.Hkv, p.cap_tokens, p.D), p.torch_dtype)
+    _need(idx, "idx", (p.B, p.Hkv, p.N, p.K), torch.int32)
+    _need(o, "o", (p.B, p.Hq, p.N, p.D), p.torch_dtype)
+    _need(lse, "lse", (p.B, p.Hq, p.N), torch.float32)
+    _need(dout, "dout", (p.B, p.Hq, p.N, p.D), p.torch_dtype)
+    dev = q.device
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.zeros_like(k)
+    if dv is None:
+        dv = torch.zeros_like(v)
+    if ws is None:
+        ws = workspace(attn_backward_workspace_bytes(p), dev)
+    _check(load().pisa_sparse_attn_backward(ctypes.byref(p.c()), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            idx.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                                            _stream(stream)))
+    return dq, dk, dv
 
 
 def flat_select(p: Problem, q, pyr, idx=None, score=None, ws=None, with_score: bool = True, stream=None):

@@ -142,6 +142,25 @@ pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k
                              const int32_t* idx, void* o, float* lse, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ---- backward of the sparse attention [BSA] o_t equation ----------------- *
+ * Gradients of L = sum_t dout_t . o_t for the attention of pisa_sparse_attn
+ * over the FIXED selection idx (index-valued: no gradient flows through the
+ * selection).  With p = softmax(z), z_i = q_t . k_i * scale over the keys of
+ * the kept leaves (i <= t when causal) and D_t = dout_t . o_t:
+ *   dq_t = scale sum_i p_i (dout_t . v_i - D_t) k_i,
+ *   dk_i = scale sum_t p_i (dout_t . v_i - D_t) q_t,   dv_i = sum_t p_i dout_t.
+ * q, dout, dq: [B][Hq][N][D]; k, v, dk, dv: [B][Hkv][cap][D] (rows >= N of dk,
+ * dv are not written); idx: [B][Hkv][N][K] as from pisa_select; o and lse:
+ * the outputs of pisa_sparse_attn for the same inputs (lse fp32 [B][Hq][N],
+ * required).  Element types follow dtype; accumulation is fp32 (bf16 inputs:
+ * p and dS are rounded to bf16 for the matrix products).  ws: at least
+ * pisa_attn_backward_workspace_bytes(p) bytes, 256-byte aligned.            */
+size_t pisa_attn_backward_workspace_bytes(const pisa_problem* p);
+pisa_status pisa_sparse_attn_backward(const pisa_problem* p, const void* q, const void* k, const void* v,
+                                      const int32_t* idx, const void* o, const float* lse, const void* dout,
+                                      void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* ---- flat single-level selector (measurement baseline) [BSA] ------------ *
  * Scores every valid leaf j by sum over the G_Q query heads of
  * q_{h',t} . P_1[j] * scale and keeps the top K (same order and output

@@ -1,0 +1,79 @@
+"""GPU parity of the sparse-attention backward (pisa_sparse_attn_backward)
+against the oracle's fp64 gradients, on the selection pisa_select returns
+(the oracle is given the same idx, so the comparison does not depend on
+near-ties), with the forward's o and lse from the GPU as a caller would pass
+them.  Bar: max |GPU - oracle| <= tol * max(1, max |oracle|) per tensor, tol
+1e-4 for fp32 inputs and 2e-2 for bf16 inputs (p and dS are rounded to bf16
+for the matrix products, like the forward's probabilities).  Cases cover
+ragged N, N <= C, C = 48 / 32 / 128, every GQA width, D = 64, B = 2, causal
+and not, and leaves whose queries span several workgroup chunks."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import log, to_dev, to_host_f64
+from hierarchical_block_sparse_mean_amd import inputs as I
+from hierarchical_block_sparse_mean_amd import pisa
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+CASES = {
+    "f32_tiny": I.Workload("bwd_f32_tiny", 1, 1024, 4, 1, 64, 64, 4, "f32", False, seed=81),
+    "f32_c48_causal_ragged": I.Workload("bwd_f32_c48", 1, 1000, 4, 2, 64, 48, 3, "f32", True, seed=82),
+    "f32_one_leaf": I.Workload("bwd_f32_one", 1, 40, 4, 1, 64, 64, 4, "f32", True, seed=83),
+    "bf16_g4_n4133": I.Workload("bwd_bf16_g4", 1, 4133, 32, 8, 128, 64, 16, "bf16", True, "leaf_per_query",
+                                seed=84),
+    "bf16_g16_c32": I.Workload("bwd_bf16_g16", 1, 1500, 16, 1, 128, 32, 4, "bf16", True, seed=85),
+    "bf16_c128": I.Workload("bwd_bf16_c128", 1, 3000, 8, 2, 128, 128, 8, "bf16", True, seed=86),
+    "bf16_d64_b2_g2": I.Workload("bwd_bf16_d64", 2, 1500, 4, 2, 64, 64, 8, "bf16", False, seed=87),
+    "bf16_g1_g8": I.Workload("bwd_bf16_g8", 1, 2100, 16, 2, 128, 64, 8, "bf16", True, seed=88),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward(name):
+    w = CASES[name]
+    log(f"[test_backward {name}]")
+    data = I.generate(w)
+    n = w.B * w.Hq * w.N * w.D
+    dout = I.normal(w.seed, 11, n, dtype=w.dtype).reshape(w.B, w.Hq, w.N, w.D)
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype)
+    q, k, v, g = (to_dev(x) for x in (data["q"], data["k"], data["v"], dout))
+    pyr = pisa.build_pyramid(p, k)
+    idx, _ = pisa.select(p, q, k, pyr)
+    o, lse = pisa.sparse_attn(p, q, k, v, idx)
+    dq, dk, dv = pisa.sparse_attn_backward(p, q, k, v, idx, o, lse, g)
+    torch.cuda.synchronize()
+    op = oracle.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal)
+    r_dq, r_dk, r_dv = oracle.attention_backward(op, data["q"], data["k"], data["v"], idx.cpu().numpy(), dout)
+    for label, got, ref in (("dq", dq, r_dq), ("dk", dk, r_dk), ("dv", dv, r_dv)):
+        err = np.abs(to_host_f64(got) - ref).max()
+        lim = TOL[w.dtype] * max(1.0, np.abs(ref).max())
+        log(f"  {label}: max err {err:.3g} (limit {lim:.3g}, max |ref| {np.abs(ref).max():.3g})")
+        assert err <= lim, f"{name} {label}: {err} > {lim}"
+
+
+def test_backward_rows_beyond_n_untouched():
+    """dk, dv rows >= N of a cache-shaped buffer are not written."""
+    w = I.Workload("bwd_cap", 1, 300, 4, 1, 64, 64, 4, "f32", True, seed=89)
+    cap = 400
+    data = I.generate(w)
+    kc = np.zeros((1, 1, cap, 64), np.float32)
+    vc = np.zeros_like(kc)
+    kc[:, :, :300], vc[:, :, :300] = data["k"], data["v"]
+    p = pisa.Problem(1, 300, 4, 1, 64, 64, 4, causal=True, dtype="f32", cap=cap)
+    q, k, v = to_dev(data["q"]), to_dev(kc), to_dev(vc)
+    g = to_dev(I.normal(89, 11, 4 * 300 * 64, dtype="f32").reshape(1, 4, 300, 64))
+    pyr = pisa.build_pyramid(p, k)
+    idx, _ = pisa.select(p, q, k, pyr)
+    o, lse = pisa.sparse_attn(p, q, k, v, idx)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    pisa.sparse_attn_backward(p, q, k, v, idx, o, lse, g, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert (dk[:, :, 300:] == 7.0).all() and (dv[:, :, 300:] == 7.0).all()
+    assert not (dk[:, :, :300] == 7.0).any()
