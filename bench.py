@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--scaling", action="store_true",
                     help="selection-time scaling and PISA-vs-flat crossover at C=64, K=16 over --scaling-n")
     ap.add_argument("--scaling-n", default="32768,65536,131072,262144,524288,1048576")
+    ap.add_argument("--backward", action="store_true",
+                    help="sparse-attention forward + backward over the workload's selection")
     ap.add_argument("--io", action="store_true",
                     help="one-stage vs two-stage selection at G_Q = 4 and 16 (N = 131072, C = 64, K = 16)")
     return ap.parse_args()
@@ -144,6 +146,8 @@ def main() -> int:
         return scaling_main(args)
     if args.io:
         return io_main(args)
+    if args.backward:
+        return backward_main(args)
     w = I.workload(args.workload)
     if w.steps:
         return decode_main(args, w)
@@ -469,6 +473,77 @@ def scaling_main(args) -> int:
         "loglog_slope": {"select_ms": slope("select_ms"), "flat_select_ms": slope("flat_select_ms"),
                          "attention_ms": slope("attention_ms")},
         "flat_over_select": [round(x, 4) for x in ratio],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def backward_main(args) -> int:
+    """Sparse-attention backward over the selection of the workload's
+    queries: forward (with lse) then backward with a seeded N(0,1) output
+    gradient, each timed with HIP events over --steps repetitions.  Work:
+    attention forward 4 d flop per attended (query head, key); backward
+    10 d (S recomputed, dP, dV, dK, dQ)."""
+    import numpy as np
+    import torch
+
+    from hierarchical_block_sparse_mean_amd import inputs as I
+    from hierarchical_block_sparse_mean_amd import pisa
+
+    w = I.workload(args.workload)
+    data = I.generate(w)
+    q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
+    g = dev(I.normal(w.seed, 11, w.B * w.Hq * w.N * w.D, dtype=w.dtype).reshape(w.B, w.Hq, w.N, w.D))
+    del data
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype)
+    pyr = pisa.build_pyramid(p, k)
+    idx, _ = pisa.select(p, q, k, pyr)
+    aws = pisa.workspace(pisa.attn_workspace_bytes(p))
+    bws = pisa.workspace(pisa.attn_backward_workspace_bytes(p))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.zeros_like(k), torch.zeros_like(v)
+
+    def fwd():
+        pisa.sparse_attn(p, q, k, v, idx, o=o, lse=lse, ws=aws)
+
+    def bwd():
+        pisa.sparse_attn_backward(p, q, k, v, idx, o, lse, g, dq=dq, dk=dk, dv=dv, ws=bws)
+
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    res = {}
+    kern = {}
+    for name, fn in (("forward", fwd), ("backward", bwd)):
+        pisa.timer_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        kern[name] = {kk: {"avg_ms": round(vv[1] / max(1, vv[0]), 4), "launches_per_step": vv[0] / args.steps}
+                      for kk, vv in pisa.timer_report().items()}
+        pisa.timer_enable(False)
+        res[name] = e0.elapsed_time(e1) / args.steps
+        log(f"{name}: {res[name]:.3f} ms")
+    keys = attended_keys(idx, w.N, w.C, w.causal) * (w.Hq // w.Hkv)
+    fwd_tf = 4.0 * w.D * keys / (res["forward"] * 1e-3) / 1e12
+    bwd_tf = 10.0 * w.D * keys / (res["backward"] * 1e-3) / 1e12
+    line = {
+        "metric": "PISA sparse-attention backward ms over the prefill selection, 1 GPU",
+        "value": round(res["backward"], 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "higher_is_better": False, "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.D, "C": w.C, "g": 2,
+                   "K": w.K, "causal": w.causal},
+        "forward_ms": round(res["forward"], 4),
+        "attended_head_keys": int(keys),
+        "roofline": {"forward": {"bound": "mfma", "achieved_TFLOPs": round(fwd_tf, 2),
+                                 "frac": round(fwd_tf / PEAK["mfma_bf16_TFLOPs"], 5)},
+                     "backward": {"bound": "mfma", "achieved_TFLOPs": round(bwd_tf, 2),
+                                  "frac": round(bwd_tf / PEAK["mfma_bf16_TFLOPs"], 5)}},
+        "kernels": kern,
     }
     print(json.dumps(line), flush=True)
     return 0

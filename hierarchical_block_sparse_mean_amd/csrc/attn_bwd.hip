@@ -98,13 +98,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ dout,
 // ---- 16x16x16 MFMA: lane group g supplies contraction elements 4g .. 4g+3 ----
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ floatx4 mma16(const float* a4, const float* b4, floatx4 acc, uint16_t) {
-  shortx4 a, b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = (short)f32_to_bf16(a4[i]);
-    b[i] = (short)f32_to_bf16(b4[i]);
-  }
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+  const uint2 ua = {pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3])};
+  const uint2 ub = {pack_bf16x2(b4[0], b4[1]), pack_bf16x2(b4[2], b4[3])};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, ua), __builtin_bit_cast(shortx4, ub),
+                                                  acc, 0, 0, 0);
 }
 __device__ __forceinline__ floatx4 mma16(const float* a4, const float* b4, floatx4 acc, float) {
 #pragma unroll

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
       uint32_t wv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        wv[i] = (uint32_t)f32_to_bf16(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16(acc[2 * i + 1] * inv) << 16);
+        wv[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
       *reinterpret_cast<uint4*>(out) = uint4{wv[0], wv[1], wv[2], wv[3]};
     } else {
 #pragma unroll

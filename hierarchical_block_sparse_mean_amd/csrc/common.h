@@ -16,12 +16,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
-// round to nearest even (inputs here are finite)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const floatx2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
@@ -258,10 +260,8 @@ struct Frag<uint16_t> {
   }
   // round eight fp32 values to bf16 (nearest even)
   __device__ __forceinline__ void set(const float* x) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
-    const uint4 u = {w[0], w[1], w[2], w[3]};
+    const uint4 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
     v = *reinterpret_cast<const bf16x8*>(&u);
   }
   __device__ __forceinline__ void zero() {
