@@ -95,6 +95,27 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
+// x from lane (lane ^ M): a DPP quad permutation for M = 1, 2 (no LDS
+// traffic), ds_bpermute otherwise
+template <int M>
+__device__ __forceinline__ float shfl_xor_dpp(float x) {
+  if constexpr (M == 1)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  else if constexpr (M == 2)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  else
+    return __shfl_xor(x, M);
+}
+// sum over aligned groups of W consecutive lanes (W a power of two <= 16)
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  if constexpr (W >= 2) x += shfl_xor_dpp<1>(x);
+  if constexpr (W >= 4) x += shfl_xor_dpp<2>(x);
+  if constexpr (W >= 8) x += shfl_xor_dpp<4>(x);
+  if constexpr (W >= 16) x += shfl_xor_dpp<8>(x);
+  return x;
+}
+
 // reductions inside aligned groups of `W` lanes (W a power of two <= 64)
 template <int W>
 __device__ __forceinline__ float group_max(float x) {

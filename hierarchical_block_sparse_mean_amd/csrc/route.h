@@ -16,9 +16,10 @@
 namespace pisa {
 
 // Per-wave LDS scratch used by route_query.
-struct RouteLds {
+struct __align__(16) RouteLds {
   int32_t cand[kWave];  // candidate block indices of the current level
   float score[kWave];   // their GQA-summed scores
+  int32_t ex[16];       // block-floating-point exponents of a 16-row tile
 };
 
 // G dot products of one fp32 pyramid row with the G query vectors in LDS.

@@ -110,25 +110,24 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
       else fa = halfx8{0, 0, 0, 0, 0, 0, 0, 0};
       acc = mma16x16x32(fa, fq[st], acc);
     }
-    // accumulator row 4g+i: its exponent (INT32_MIN = invalid child) sits in
-    // lane 4g+i; logits in log2 units
+    // accumulator row 4g+i: its exponent (INT32_MIN = invalid child) comes
+    // from lane 4g+i through LDS; logits in log2 units
+    if (g == 0) s.ex[col] = er;
+    wave_sync();
+    const int4 er4 = *reinterpret_cast<const int4*>(&s.ex[4 * g]);
+    const int32_t ers[4] = {er4.x, er4.y, er4.z, er4.w};
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t eri = __shfl(er, 4 * g + i);
-      x[i] = (eri == INT32_MIN) ? -INFINITY : ldexpf(acc[i], eri + eq) * sl2;
-    }
+    for (int i = 0; i < 4; ++i) x[i] = (ers[i] == INT32_MIN) ? -INFINITY : ldexpf(acc[i], ers[i] + eq) * sl2;
+    wave_sync();  // s.ex is rewritten by the next row tile
     float u[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const float m = fmaxf(x[2 * p], x[2 * p + 1]);
       u[p] = (m == -INFINITY) ? -INFINITY : m + __log2f(exp2_nonpos(x[2 * p] - m) + exp2_nonpos(x[2 * p + 1] - m));
     }
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) {
-      u[0] += __shfl_xor(u[0], o);
-      u[1] += __shfl_xor(u[1], o);
-    }
+    u[0] = lane_group_sum<G>(u[0]);
+    u[1] = lane_group_sum<G>(u[1]);
     const int c0 = 8 * rt + 2 * g;
     if (col == 0) {
       if (c0 < nA) s.score[c0] = u[0];

@@ -214,11 +214,8 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
     float u0 = (mx0 == -INFINITY) ? -INFINITY : mx0 * a.scale + __log2f(s0) * kLn2;
     float u1 = (mx1 == -INFINITY) ? -INFINITY : mx1 * a.scale + __log2f(s1) * kLn2;
     // GQA sum over the G columns of the query
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) {
-      u0 += __shfl_xor(u0, o);
-      u1 += __shfl_xor(u1, o);
-    }
+    u0 = lane_group_sum<G>(u0);
+    u1 = lane_group_sum<G>(u1);
     if (g == 0 && hh == 0 && pr >= 0) {
       const int64_t e = (int64_t)(pr >> 5) * a.K + (pr & 31);  // (t, slot) entry
       out_base[e * 2] = u0;
@@ -239,6 +236,9 @@ struct TopkArgs {
   int32_t B, N, Hkv, K;
 };
 
+// KP: K when K is 16 or 32 (the 2K candidates sit in lanes [0, 2K): top K by
+// half sorts, then a K-lane index sort), else 0 (full wave sorts).
+template <int KP>
 __global__ __launch_bounds__(kTopkWaves* kWave) void final_topk_kernel(TopkArgs a) {
   const int64_t wid = (int64_t)blockIdx.x * kTopkWaves + threadIdx.x / kWave;
   const int64_t total = (int64_t)a.B * a.Hkv * a.N;
@@ -253,10 +253,12 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void final_topk_kernel(TopkArgs 
       if (sc != -INFINITY) key = score_key(sc, 2 * j2 + l);
     }
   }
-  key = wave_sort_desc(key);
+  if (KP) key = top_half<(KP ? KP : 16)>(key);
+  else key = wave_sort_desc(key);
   const bool kept = lane < a.K && key != 0ull;
   uint64_t k2 = kept ? index_key(key_index(key), key_score(key)) : 0ull;
-  k2 = wave_sort_desc(k2);
+  if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
+  else k2 = wave_sort_desc(k2);
   if (lane < a.K) {
     const bool v = k2 != 0ull;
     a.idx[wid * a.K + lane] = v ? index_key_index(k2) : -1;
@@ -316,8 +318,13 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   if (err != hipSuccess) return err;
   TopkArgs ta{blk2, scores, idx, score, p.B, p.N, p.Hkv, p.K};
   const int64_t waves = (int64_t)p.B * p.Hkv * p.N;
-  PISA_LAUNCH("final_topk", stream, final_topk_kernel, dim3((unsigned)((waves + kTopkWaves - 1) / kTopkWaves)),
-              dim3(kTopkWaves * kWave), 0, ta);
+  const dim3 tgrid((unsigned)((waves + kTopkWaves - 1) / kTopkWaves)), tblock(kTopkWaves * kWave);
+  if (p.K == 16)
+    PISA_LAUNCH("final_topk", stream, final_topk_kernel<16>, tgrid, tblock, 0, ta);
+  else if (p.K == 32)
+    PISA_LAUNCH("final_topk", stream, final_topk_kernel<32>, tgrid, tblock, 0, ta);
+  else
+    PISA_LAUNCH("final_topk", stream, final_topk_kernel<0>, tgrid, tblock, 0, ta);
   return hipGetLastError();
 }
 
