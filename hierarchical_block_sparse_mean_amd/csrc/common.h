@@ -136,6 +136,21 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// 32-bit x from lane (lane ^ m) for a compile-time m after unrolling: DPP for
+// m = 1, 2 (quad permutations) and m = 8 (rotation of a 16-lane row by 8,
+// which is lane ^ 8 in either rotation direction); ds_bpermute otherwise.
+__device__ __forceinline__ int shfl_xor_fast(int x, int m) {
+  if (m == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if (m == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if (m == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  return __shfl_xor(x, m);
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64_fast(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)shfl_xor_fast((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)shfl_xor_fast((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // 2^x for x <= 0 (or -inf) on the hardware exp unit alone, without the
 // library's denormal-range fix-up: a result that would be denormal flushes to
 // zero, which changes nothing where every use adds it to a term >= 1 (the
@@ -203,7 +218,7 @@ __device__ __forceinline__ uint64_t group_sort_desc(uint64_t key) {
   for (int k = 2; k <= N; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t other = shfl_xor_u64(key, j);
+      const uint64_t other = shfl_xor_u64_fast(key, j);
       const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
       key = take_max ? (key > other ? key : other) : (key < other ? key : other);
     }

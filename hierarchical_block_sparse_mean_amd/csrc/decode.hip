@@ -83,7 +83,7 @@ __device__ __forceinline__ void leaf_dots(const Frag<T>* fq, const T* kbase, con
     Frag<T> fk[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (r < nk) fk[s].load(row + g * (D / 4) + 8 * s);
+      if (r < nk) fk[s].load(row + 32 * s + 8 * g);  // contiguous 64-byte spans per row
       else fk[s].zero();
     }
     acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
   Frag<T> fq[NS];  // B operand: column col = query head col of the group
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    if (col < G) fq[st].load(qn + col * D + g4 * (D / 4) + 8 * st);
+    if (col < G) fq[st].load(qn + col * D + 32 * st + 8 * g4);  // element order of leaf_dots
     else fq[st].zero();
   }
   const float sl2 = a.scale * kLog2e;

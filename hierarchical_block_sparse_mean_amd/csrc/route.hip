@@ -101,13 +101,16 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
     const int32_t r = (c < nA) ? 2 * s.cand[c] + (row & 1) : 0x7fffffff;
     const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
     if (rows_out != nullptr) *rows_out += __popcll(__ballot(vrow) & 0xFFFFull);
-    const int32_t er = vrow ? xb[lvl + r] : INT32_MIN;
+    // an invalid row reads row 0 of the level instead (finite data): its
+    // accumulator row is discarded through the INT32_MIN exponent below
+    const int64_t rr = lvl + (vrow ? r : 0);
+    const int32_t er = vrow ? xb[rr] : INT32_MIN;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      halfx8 fa;
-      if (vrow) fa = *reinterpret_cast<const halfx8*>(hb + (lvl + r) * D + g * (D / 4) + 8 * st);
-      else fa = halfx8{0, 0, 0, 0, 0, 0, 0, 0};
+      // step st covers elements [32 st, 32 st + 32): the four lane groups read
+      // one contiguous 64-byte span of the row per load
+      const halfx8 fa = *reinterpret_cast<const halfx8*>(hb + rr * D + 32 * st + 8 * g);
       acc = mma16x16x32(fa, fq[st], acc);
     }
     // accumulator row 4g+i: its exponent (INT32_MIN = invalid child) comes
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArg
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Hq + h * G + col) * a.N + t) * D;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      load8<uint16_t>(qrow + g * (D / 4) + 8 * st, qv[st]);
+      load8<uint16_t>(qrow + 32 * st + 8 * g, qv[st]);  // same element order as the rows
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[st][e]));
     }
