@@ -98,6 +98,36 @@ def traffic_for(kernel: str, workload: str, per_launch_bytes=None):
         return None
 
 
+def measured_ceilings() -> dict:
+    """Ceilings measured on this GPU, next to the vendor peaks: a 1 GiB
+    device-to-device copy (2 GiB of HBM traffic per copy) and a bf16 GEMM
+    (8192^3, the platform BLAS), each timed with HIP events."""
+    import torch
+
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1000.0
+
+    copy_s = timed(lambda: dst.copy_(src), 10)
+    gemm_s = timed(lambda: torch.matmul(a, b), 10)
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * (1 << 30) / copy_s / 1e9, 1),
+            "gemm_bf16_TFLOPs": round(2 * 8192 ** 3 / gemm_s / 1e12, 1)}
+
+
 def attended_keys(idx, N: int, C: int, causal: bool):
     """Sum over (b, h, t, slot) of the keys attention reads for that leaf."""
     import torch
@@ -165,6 +195,8 @@ def main() -> int:
     o = torch.empty_like(q)
     attn_ws = pisa.workspace(pisa.attn_workspace_bytes(p))
 
+    ceilings = measured_ceilings()
+    log(f"measured ceilings: {ceilings}")
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -262,8 +294,10 @@ def main() -> int:
             achieved, peak = per_launch / avg_s / 1e12, mfma_peak
         else:
             achieved, peak = per_launch / avg_s / 1e9, PEAK["hbm_GBps"]
+        measured = ceilings["copy_GBps"] if unit == "GB/s" else ceilings["gemm_bf16_TFLOPs"]
         roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
                     "unit": unit, "frac": round(achieved / peak, 5),
+                    "measured_peak": measured, "frac_of_measured": round(achieved / measured, 5),
                     "traffic": traffic_for(dominant, w.name, per_launch_bytes=None),
                     "avg_launch_ms": round(per_kernel[dominant]["avg_ms"], 4),
                     "work_per_launch": per_launch, "work_note": note}
@@ -275,11 +309,15 @@ def main() -> int:
         avg_s = per_kernel[name]["avg_ms"] / 1000.0
         per_launch = amount / launches
         if unit == "TFLOP/s":
-            kernel_rooflines[name] = {"bound": bound, "achieved_TFLOPs": round(per_launch / avg_s / 1e12, 2),
-                                      "frac": round(per_launch / avg_s / 1e12 / mfma_peak, 4)}
+            ach = per_launch / avg_s / 1e12
+            kernel_rooflines[name] = {"bound": bound, "achieved_TFLOPs": round(ach, 2),
+                                      "frac": round(ach / mfma_peak, 4),
+                                      "frac_of_measured": round(ach / ceilings["gemm_bf16_TFLOPs"], 4)}
         else:
-            kernel_rooflines[name] = {"bound": bound, "achieved_GBps": round(per_launch / avg_s / 1e9, 1),
-                                      "frac": round(per_launch / avg_s / 1e9 / PEAK["hbm_GBps"], 4)}
+            ach = per_launch / avg_s / 1e9
+            kernel_rooflines[name] = {"bound": bound, "achieved_GBps": round(ach, 1),
+                                      "frac": round(ach / PEAK["hbm_GBps"], 4),
+                                      "frac_of_measured": round(ach / ceilings["copy_GBps"], 4)}
 
     # ---- flat single-level selector on the same inputs ------------------------
     flat_ms = None
@@ -376,6 +414,7 @@ def main() -> int:
                     for kk, vv in per_kernel.items()},
         "roofline": roofline,
         "kernel_rooflines": kernel_rooflines,
+        "measured_ceilings": ceilings,
         "route_work": rc,
         "cpu_baseline": cpu,
         "parity": parity,

@@ -105,14 +105,17 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
     // accumulator row is discarded through the INT32_MIN exponent below
     const int64_t rr = lvl + (vrow ? r : 0);
     const int32_t er = vrow ? xb[rr] : INT32_MIN;
+    // step st covers elements [32 st, 32 st + 32): the four lane groups read
+    // one contiguous 64-byte span of the row per load.  All NS loads are
+    // issued before the first product (the barrier keeps the scheduler from
+    // sinking each load next to its use, which serialises the round trips).
+    halfx8 fa[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * D + 32 * st + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      // step st covers elements [32 st, 32 st + 32): the four lane groups read
-      // one contiguous 64-byte span of the row per load
-      const halfx8 fa = *reinterpret_cast<const halfx8*>(hb + rr * D + 32 * st + 8 * g);
-      acc = mma16x16x32(fa, fq[st], acc);
-    }
+    for (int st = 0; st < NS; ++st) acc = mma16x16x32(fa[st], fq[st], acc);
     // accumulator row 4g+i: its exponent (INT32_MIN = invalid child) comes
     // from lane 4g+i through LDS; logits in log2 units
     if (g == 0) s.ex[col] = er;
