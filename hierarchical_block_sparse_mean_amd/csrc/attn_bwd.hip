@@ -32,7 +32,7 @@ constexpr size_t kBwdBudget = (size_t)8 << 30;  // partial dQ rows per head chun
 static size_t b256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  int64_t heads, M1, ncl, slots;
+  int64_t heads, M1, Mb, ncl, slots;  // Mb: cluster bins per head
   size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_dq, off_hist, off_rowdot, off_dk, off_dv,
       total;
 };
@@ -40,14 +40,15 @@ struct BwdLayout {
 static BwdLayout bwd_layout(const Problem& p) {
   BwdLayout L{};
   L.M1 = level_rows(p.N, p.C, 1);
-  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * p.D * 4) + (size_t)L.M1 * 16;
+  L.Mb = cluster_bins(p.N, L.M1, kAttnBins);
+  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * p.D * 4) + (size_t)L.Mb * 16;
   const int64_t BH = (int64_t)p.B * p.Hkv;
   int64_t hmax = (int64_t)(kBwdBudget / per_head);
   if (hmax < 1) hmax = 1;
   if (hmax > BH) hmax = BH;
   const int64_t nchunks = (BH + hmax - 1) / hmax;
   L.heads = (BH + nchunks - 1) / nchunks;
-  L.ncl = L.heads * L.M1;
+  L.ncl = L.heads * L.Mb;
   L.slots = L.heads * (int64_t)p.N * p.K;
   size_t off = 0;
   L.off_counts = off;
@@ -63,7 +64,7 @@ static BwdLayout bwd_layout(const Problem& p) {
   L.off_dq = off;
   off = b256(off + 4 * (size_t)L.slots * p.G * p.D);
   L.off_hist = off;
-  off = b256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.M1));
+  off = b256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.Mb));
   L.off_rowdot = off;
   off = b256(off + 4 * (size_t)p.B * p.Hq * p.N);
   L.off_dk = off;
@@ -123,7 +124,7 @@ struct BwdArgs {
   float* dq_part;  // [heads][N][K][G][D]
   float* dk_acc;   // [B][Hkv][N][D]
   float* dv_acc;
-  int64_t ncl, M1, head0;
+  int64_t ncl, M1, Mb, head0;
   int32_t N, Hq, Hkv, C, K;
   int32_t causal;
   int64_t cap;
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kBwdWaves* kWave) void attn_bwd_kernel(BwdArgs a) {
     else hi = mid;
   }
   const int64_t c = lo;
-  const int64_t hl = c / a.M1;
+  const int64_t hl = c / a.Mb;
   const int64_t j = c % a.M1;
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
@@ -408,11 +409,11 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
   for (int64_t head0 = 0; head0 < BH; head0 += L.heads) {
     const int64_t heads = (BH - head0) < L.heads ? (BH - head0) : L.heads;
     const int64_t entries = heads * p.N * p.K;
-    const int64_t ncl = heads * L.M1;
+    const int64_t ncl = heads * L.Mb;
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
-    err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kBwdChunk, cb, stream);
+    err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, kBwdChunk, cb, stream);
     if (err != hipSuccess) return err;
-    BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1,
+    BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1, L.Mb,
                head0, p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
     BwdMergeArgs ma{idx, dq_part, dq, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
     const int64_t max_chunks = (entries + kBwdChunk - 1) / kBwdChunk + ncl;

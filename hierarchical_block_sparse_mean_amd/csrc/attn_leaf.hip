@@ -31,7 +31,7 @@ static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct AttnLayout {
   int64_t heads;  // (b, h) heads per chunk
-  int64_t M1, ncl, slots;
+  int64_t M1, Mb, ncl, slots;  // Mb: cluster bins per head
   size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_m, off_l, off_o, off_hist, total;
 };
 
@@ -39,14 +39,15 @@ static AttnLayout attn_layout(const Problem& p) {
   AttnLayout L{};
   const size_t osz = p.dtype == 1 ? 2 : 4;
   L.M1 = level_rows(p.N, p.C, 1);
-  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * (8 + p.D * osz)) + (size_t)L.M1 * 16;
+  L.Mb = cluster_bins(p.N, L.M1, kAttnBins);
+  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * (8 + p.D * osz)) + (size_t)L.Mb * 16;
   const int64_t BH = (int64_t)p.B * p.Hkv;
   int64_t hmax = (int64_t)(kAttnBudget / per_head);
   if (hmax < 1) hmax = 1;
   if (hmax > BH) hmax = BH;
   const int64_t nchunks = (BH + hmax - 1) / hmax;
   L.heads = (BH + nchunks - 1) / nchunks;
-  L.ncl = L.heads * L.M1;
+  L.ncl = L.heads * L.Mb;
   L.slots = L.heads * (int64_t)p.N * p.K;
   size_t off = 0;
   L.off_counts = off;
@@ -66,7 +67,7 @@ static AttnLayout attn_layout(const Problem& p) {
   L.off_o = off;
   off = a256(off + osz * (size_t)L.slots * p.G * p.D);
   L.off_hist = off;
-  off = a256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.M1));
+  off = a256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.Mb));
   L.total = off;
   return L;
 }
@@ -84,7 +85,7 @@ struct AttnLeafArgs {
   float* pm;   // [heads][N][K][G]
   float* pl;
   void* po;    // [heads][N][K][G][D] (input dtype)
-  int64_t ncl, M1, head0;
+  int64_t ncl, M1, Mb, head0;
   int32_t N, Hq, Hkv, C, K;
   int32_t causal;
   int64_t cap;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(At
     else hi = mid;
   }
   const int64_t c = lo;
-  const int64_t hl = c / a.M1;  // head within the chunk
+  const int64_t hl = c / a.Mb;  // head within the chunk
   const int64_t j = c % a.M1;   // leaf
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
@@ -360,12 +361,13 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
   for (int64_t head0 = 0; head0 < BH; head0 += L.heads) {
     const int64_t heads = (BH - head0) < L.heads ? (BH - head0) : L.heads;
     const int64_t entries = heads * p.N * p.K;
-    const int64_t ncl = heads * L.M1;
+    const int64_t ncl = heads * L.Mb;
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
     hipError_t err =
-        launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnChunk, cb, stream);
+        launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, kAttnChunk, cb, stream);
     if (err != hipSuccess) return err;
-    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, head0, p.N, p.Hq, p.Hkv, p.C, p.K,
+    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, L.Mb, head0, p.N, p.Hq, p.Hkv, p.C,
+                    p.K,
                     p.causal ? 1 : 0, p.cap, p.scale};
     MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
     const int64_t max_chunks = (entries + kAttnChunk - 1) / kAttnChunk + ncl;

@@ -11,9 +11,15 @@
 //      bins gives each bin's first pair; then one scan of the work-chunk
 //      counts of all clusters;
 //   3. per tile, an LDS cursor per bin scatters the pair code (t << 5) | slot.
-// Heads with more key blocks than the LDS histogram holds use a global-atomic
-// fallback.  Either way: counts[c], offsets[c] (first pair) and
-// chunk_off[c] (first work chunk, chunk_off[ncl] = total) for c = head*M + j.
+// A cluster is the set of entries of one (head, query block, key block): the
+// queries of a head are cut into blocks of 2^s consecutive positions (the
+// smallest s >= 12 whose bins still fit the LDS histogram), so that the work
+// on one block of queries is grouped together and the consumers' re-reads of
+// those queries' rows stay cache-resident.  Bins per head: Mb = blocks * M,
+// bin = (t >> s) * M + key block.  Heads with more key blocks than the LDS
+// histogram holds use one query block and a global-atomic fallback.  Either
+// way: counts[c], offsets[c] (first pair) and chunk_off[c] (first work chunk,
+// chunk_off[ncl] = total) for c = head * Mb + bin.
 #include "kernels.h"
 
 namespace pisa {
@@ -23,27 +29,46 @@ constexpr int64_t kMaxBins = 16384; // LDS bins (64 KB)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t M) {
-  if (M > kMaxBins) return 256;
-  const int64_t tiles = (NK + kHistTile - 1) / kHistTile;
-  return al256(sizeof(int32_t) * (size_t)heads * tiles * M);
+int32_t cluster_query_shift(int64_t N, int64_t M, int64_t max_bins) {
+  if (max_bins > kMaxBins) max_bins = kMaxBins;
+  if (M >= max_bins) return 31;
+  int32_t sh = 12;
+  while (sh < 31 && ((N + ((int64_t)1 << sh) - 1) >> sh) * M > max_bins) ++sh;
+  return sh;
 }
 
-__global__ void hist_kernel(const int32_t* __restrict__ keys, int64_t NK, int64_t M, int64_t tiles,
-                            int32_t* __restrict__ hist) {
+int64_t cluster_bins(int64_t N, int64_t M, int64_t max_bins) {
+  const int32_t sh = cluster_query_shift(N, M, max_bins);
+  return ((N + ((int64_t)1 << sh) - 1) >> sh) * M;
+}
+
+size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t Mb) {
+  if (Mb > kMaxBins) return 256;
+  const int64_t tiles = (NK + kHistTile - 1) / kHistTile;
+  return al256(sizeof(int32_t) * (size_t)heads * tiles * Mb);
+}
+
+// bin of entry e_loc = t * K + slot of a head holding key block j, or -1
+__device__ __forceinline__ int64_t bin_of(int32_t j, int64_t e_loc, int32_t K, int64_t M, int32_t qshift) {
+  if (j < 0 || j >= M) return -1;
+  return ((e_loc / K) >> qshift) * M + j;
+}
+
+__global__ void hist_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int32_t qshift,
+                            int64_t Mb, int64_t tiles, int32_t* __restrict__ hist) {
   extern __shared__ int32_t s_h[];
   const int64_t head = blockIdx.y, tile = blockIdx.x;
-  for (int64_t i = threadIdx.x; i < M; i += blockDim.x) s_h[i] = 0;
+  for (int64_t i = threadIdx.x; i < Mb; i += blockDim.x) s_h[i] = 0;
   __syncthreads();
   const int64_t lo = head * NK + tile * kHistTile;
   const int64_t hi = (tile + 1) * kHistTile < NK ? lo + kHistTile : head * NK + NK;
   for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) {
-    const int32_t j = keys[e];
-    if (j >= 0 && j < M) atomicAdd(&s_h[j], 1);
+    const int64_t bin = bin_of(keys[e], e - head * NK, K, M, qshift);
+    if (bin >= 0) atomicAdd(&s_h[bin], 1);
   }
   __syncthreads();
-  int32_t* out = hist + (head * tiles + tile) * M;
-  for (int64_t i = threadIdx.x; i < M; i += blockDim.x) out[i] = s_h[i];
+  int32_t* out = hist + (head * tiles + tile) * Mb;
+  for (int64_t i = threadIdx.x; i < Mb; i += blockDim.x) out[i] = s_h[i];
 }
 
 // Per (head, bin), one thread: a running sum down the tiles turns each
@@ -102,32 +127,35 @@ __device__ __forceinline__ int32_t pair_code(int64_t e_loc, int32_t K) {
   return (t << 5) | (int32_t)(e_loc - (int64_t)t * K);
 }
 
-__global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int64_t tiles,
-                               const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
-                               int32_t* __restrict__ pairs) {
+__global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int32_t qshift,
+                               int64_t Mb, int64_t tiles, const int32_t* __restrict__ base,
+                               const int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
   extern __shared__ int32_t s_cur[];
   const int64_t head = blockIdx.y, tile = blockIdx.x;
-  const int32_t* b = base + (head * tiles + tile) * M;
-  for (int64_t i = threadIdx.x; i < M; i += blockDim.x) s_cur[i] = offsets[head * M + i] + b[i];
+  const int32_t* b = base + (head * tiles + tile) * Mb;
+  for (int64_t i = threadIdx.x; i < Mb; i += blockDim.x) s_cur[i] = offsets[head * Mb + i] + b[i];
   __syncthreads();
   const int64_t lo = head * NK + tile * kHistTile;
   const int64_t hi = (tile + 1) * kHistTile < NK ? lo + kHistTile : head * NK + NK;
   for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) {
-    const int32_t j = keys[e];
-    if (j >= 0 && j < M) pairs[atomicAdd(&s_cur[j], 1)] = pair_code(e - head * NK, K);
+    const int64_t bin = bin_of(keys[e], e - head * NK, K, M, qshift);
+    if (bin >= 0) pairs[atomicAdd(&s_cur[bin], 1)] = pair_code(e - head * NK, K);
   }
 }
 
-// Single-workgroup exclusive scan of the work-chunk counts of all clusters.
-__global__ __launch_bounds__(1024) void chunk_scan_kernel(const int32_t* __restrict__ counts, int64_t ncl,
-                                                          int32_t chunk, int32_t* chunk_off) {
+// Exclusive scan of the work-chunk counts of all clusters, in three steps:
+// per head (one workgroup each) over its Mb bins, over the head totals, and
+// the head bases added back.  head_tot: one int per head (scratch).
+__global__ __launch_bounds__(1024) void chunk_scan_kernel(const int32_t* __restrict__ counts, int64_t Mb,
+                                                          int32_t chunk, int32_t* chunk_off, int32_t* head_tot) {
   __shared__ int32_t s_part[1024];
   __shared__ int32_t s_carry;
+  const int64_t head = blockIdx.x;
   if (threadIdx.x == 0) s_carry = 0;
   __syncthreads();
-  for (int64_t base = 0; base < ncl; base += 1024) {
+  for (int64_t base = 0; base < Mb; base += 1024) {
     const int64_t i = base + threadIdx.x;
-    const int32_t v = i < ncl ? (counts[i] + chunk - 1) / chunk : 0;
+    const int32_t v = i < Mb ? (counts[head * Mb + i] + chunk - 1) / chunk : 0;
     s_part[threadIdx.x] = v;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
@@ -136,12 +164,43 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(const int32_t* __restr
       s_part[threadIdx.x] += add;
       __syncthreads();
     }
-    if (i < ncl) chunk_off[i] = s_carry + s_part[threadIdx.x] - v;
+    if (i < Mb) chunk_off[head * Mb + i] = s_carry + s_part[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) s_carry += s_part[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) head_tot[head] = s_carry;
+}
+
+// Exclusive scan of the head totals (in place), total into chunk_off[ncl].
+__global__ __launch_bounds__(1024) void head_scan_kernel(int32_t* head_tot, int64_t heads, int32_t* chunk_off,
+                                                         int64_t ncl) {
+  __shared__ int32_t s_part[1024];
+  __shared__ int32_t s_carry;
+  if (threadIdx.x == 0) s_carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < heads; base += 1024) {
+    const int64_t i = base + threadIdx.x;
+    const int32_t v = i < heads ? head_tot[i] : 0;
+    s_part[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int32_t add = threadIdx.x >= (unsigned)o ? s_part[threadIdx.x - o] : 0;
+      __syncthreads();
+      s_part[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (i < heads) head_tot[i] = s_carry + s_part[threadIdx.x] - v;
     __syncthreads();
     if (threadIdx.x == 1023) s_carry += s_part[1023];
     __syncthreads();
   }
   if (threadIdx.x == 0) chunk_off[ncl] = s_carry;
+}
+
+__global__ void head_base_kernel(int32_t* chunk_off, const int32_t* __restrict__ head_base, int64_t Mb, int64_t ncl) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < ncl; i += (int64_t)gridDim.x * blockDim.x)
+    chunk_off[i] += head_base[i / Mb];
 }
 
 // ---- fallback for heads with more than kMaxBins key blocks ----------------------
@@ -150,12 +209,12 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-__global__ void atomic_count_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int64_t M,
-                                    int32_t* counts) {
+__global__ void atomic_count_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int32_t K,
+                                    int64_t M, int32_t qshift, int64_t Mb, int32_t* counts) {
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t j = keys[e];
-    if (j >= 0 && j < M) atomicAdd(&counts[(e / NK) * M + j], 1);
+    const int64_t bin = bin_of(keys[e], e % NK, K, M, qshift);
+    if (bin >= 0) atomicAdd(&counts[(e / NK) * Mb + bin], 1);
   }
 }
 
@@ -185,23 +244,38 @@ __global__ __launch_bounds__(1024) void offset_scan_kernel(const int32_t* __rest
 }
 
 __global__ void atomic_fill_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int32_t K,
-                                   int64_t M, const int32_t* __restrict__ offsets, int32_t* cursor,
-                                   int32_t* pairs) {
+                                   int64_t M, int32_t qshift, int64_t Mb, const int32_t* __restrict__ offsets,
+                                   int32_t* cursor, int32_t* pairs) {
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t j = keys[e];
-    if (j < 0 || j >= M) continue;
-    const int64_t c = (e / NK) * M + j;
+    const int64_t bin = bin_of(keys[e], e % NK, K, M, qshift);
+    if (bin < 0) continue;
+    const int64_t c = (e / NK) * Mb + bin;
     pairs[offsets[c] + atomicAdd(&cursor[c], 1)] = pair_code(e % NK, K);
   }
 }
 
-hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int32_t chunk,
-                           const ClusterBufs& b, hipStream_t stream) {
-  const int64_t ncl = heads * M;
-  if (M <= kMaxBins) {
+// chunk_off[c] for every cluster (counts known): see chunk_scan_kernel
+static hipError_t launch_chunk_scan(const ClusterBufs& b, int64_t heads, int64_t Mb, int32_t chunk,
+                                    hipStream_t stream) {
+  const int64_t ncl = heads * Mb;
+  PISA_LAUNCH("cluster_chunks", stream, chunk_scan_kernel, dim3((unsigned)heads), dim3(1024), 0, b.counts, Mb, chunk,
+              b.chunk_off, b.cursor);
+  PISA_LAUNCH("cluster_chunks", stream, head_scan_kernel, dim3(1), dim3(1024), 0, b.cursor, heads, b.chunk_off, ncl);
+  const unsigned blocks = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
+  PISA_LAUNCH("cluster_chunks", stream, head_base_kernel, dim3(blocks), dim3(256), 0, b.chunk_off, b.cursor, Mb, ncl);
+  return hipGetLastError();
+}
+
+hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int64_t max_bins,
+                           int32_t chunk, const ClusterBufs& b, hipStream_t stream) {
+  const int64_t N = NK / K;
+  const int32_t qs = cluster_query_shift(N, M, max_bins);
+  const int64_t Mb = cluster_bins(N, M, max_bins);
+  const int64_t ncl = heads * Mb;
+  if (Mb <= kMaxBins) {
     const int64_t tiles = (NK + kHistTile - 1) / kHistTile;
-    const size_t lds = sizeof(int32_t) * (size_t)M;
+    const size_t lds = sizeof(int32_t) * (size_t)Mb;
     auto big = [&](auto kern) -> hipError_t {
       return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
@@ -209,28 +283,27 @@ hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32
     };
     if (big(hist_kernel) != hipSuccess || big(scatter_kernel) != hipSuccess) return hipErrorInvalidValue;
     PISA_LAUNCH("cluster_hist", stream, hist_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds, keys, NK,
-                M, tiles, b.hist);
-    PISA_LAUNCH("cluster_scan", stream, col_scan_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)heads),
-                dim3(256), 0, b.hist, M, tiles, b.counts);
-    PISA_LAUNCH("cluster_scan", stream, bin_scan_kernel, dim3((unsigned)heads), dim3(1024), 0, b.counts, NK, M,
+                K, M, qs, Mb, tiles, b.hist);
+    PISA_LAUNCH("cluster_scan", stream, col_scan_kernel, dim3((unsigned)((Mb + 255) / 256), (unsigned)heads),
+                dim3(256), 0, b.hist, Mb, tiles, b.counts);
+    PISA_LAUNCH("cluster_scan", stream, bin_scan_kernel, dim3((unsigned)heads), dim3(1024), 0, b.counts, NK, Mb,
                 b.offsets);
-    PISA_LAUNCH("cluster_chunks", stream, chunk_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, chunk,
-                b.chunk_off);
+    if (launch_chunk_scan(b, heads, Mb, chunk, stream) != hipSuccess) return hipGetLastError();
     PISA_LAUNCH("cluster_scatter", stream, scatter_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds,
-                keys, NK, K, M, tiles, b.hist, b.offsets, b.pairs);
+                keys, NK, K, M, qs, Mb, tiles, b.hist, b.offsets, b.pairs);
     return hipGetLastError();
   }
   const int64_t entries = heads * NK;
   const unsigned ew = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
   const unsigned cw = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
   PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cw), dim3(256), 0, b.counts, ncl, 0);
-  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cw), dim3(256), 0, b.cursor, ncl, 0);
-  PISA_LAUNCH("cluster_count", stream, atomic_count_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, M, b.counts);
+  PISA_LAUNCH("cluster_count", stream, atomic_count_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, qs, Mb,
+              b.counts);
   PISA_LAUNCH("cluster_scan", stream, offset_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, b.offsets);
-  PISA_LAUNCH("cluster_chunks", stream, chunk_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, chunk,
-              b.chunk_off);
-  PISA_LAUNCH("cluster_fill", stream, atomic_fill_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, b.offsets,
-              b.cursor, b.pairs);
+  if (launch_chunk_scan(b, heads, Mb, chunk, stream) != hipSuccess) return hipGetLastError();  // cursor as scratch
+  PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cw), dim3(256), 0, b.cursor, ncl, 0);
+  PISA_LAUNCH("cluster_fill", stream, atomic_fill_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, qs, Mb,
+              b.offsets, b.cursor, b.pairs);
   return hipGetLastError();
 }
 

@@ -87,11 +87,23 @@ struct ClusterBufs {
   int32_t* pairs;
   int32_t* hist;
 };
-size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t M);
+// Bins per head of a clustering of N queries over M key blocks: query blocks
+// of 2^cluster_query_shift(N, M) positions times M (see cluster.hip).
+// max_bins: the clustering's bin budget per head (query blocks are added
+// while bins stay within it; M >= max_bins gives one query block).
+int32_t cluster_query_shift(int64_t N, int64_t M, int64_t max_bins);
+int64_t cluster_bins(int64_t N, int64_t M, int64_t max_bins);
+size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t Mb);
 // keys: [heads][N][K] block indices (-1 = none), NK = N * K.  pairs holds,
-// per cluster (head * M + block), the codes (t << 5) | slot of its entries.
-hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int32_t chunk,
-                           const ClusterBufs& b, hipStream_t stream);
+// per cluster c = head * Mb + (t >> shift) * M + block, the codes
+// (t << 5) | slot of its entries; the key block of cluster c is c % M.
+hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int64_t max_bins,
+                           int32_t chunk, const ClusterBufs& b, hipStream_t stream);
+
+// Attention clusters (forward and backward): (query block, leaf) bins per
+// head, so one block of queries is attended together and its query rows are
+// re-read from cache.
+constexpr int64_t kAttnBins = 8192;
 
 // attn_leaf.hip: leaf-major MFMA attention with a merge pass
 size_t attn_leaf_workspace_bytes(const Problem& p);

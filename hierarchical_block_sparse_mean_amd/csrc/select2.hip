@@ -26,7 +26,7 @@ constexpr int kTopkWaves = 4;
 
 // ---- workspace layout -------------------------------------------------------
 struct S2Layout {
-  int64_t ncl;      // clusters = B * Hkv * M2
+  int64_t ncl;      // clusters = B * Hkv * bins per head
   int64_t max_pairs;
   size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_scores, off_hist, total;
 };
@@ -36,7 +36,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static S2Layout s2_layout(const Problem& p) {
   S2Layout s{};
   const int64_t M2 = level_rows(p.N, p.C, 2);
-  s.ncl = (int64_t)p.B * p.Hkv * M2;
+  const int64_t Mb = cluster_bins(p.N, M2, M2);  // (query block, level-2 block) bins per head
+  s.ncl = (int64_t)p.B * p.Hkv * Mb;
   s.max_pairs = (int64_t)p.B * p.Hkv * p.N * p.K;
   size_t off = 0;
   s.off_counts = off;
@@ -52,7 +53,7 @@ static S2Layout s2_layout(const Problem& p) {
   s.off_scores = off;
   off = align256(off + sizeof(float) * 2 * s.max_pairs);
   s.off_hist = off;
-  off = align256(off + cluster_scratch_bytes((int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, M2));
+  off = align256(off + cluster_scratch_bytes((int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, Mb));
   s.total = off;
   return s;
 }
@@ -67,7 +68,7 @@ struct S2Args {
   const int32_t* chunk_off;
   const int32_t* pairs;
   float* scores;  // [B][Hkv][N][K][2]
-  int64_t ncl, M1, M2;
+  int64_t ncl, M1, M2, Mb;  // Mb: cluster bins per head
   int32_t B, N, Hq, Hkv, C, K;
   int32_t causal;
   int64_t cap;
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
     else hi = mid;
   }
   const int64_t c = lo;
-  const int64_t bh = c / a.M2;
+  const int64_t bh = c / a.Mb;
   const int64_t j2 = c % a.M2;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kS2Chunk;
@@ -279,9 +280,10 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
   const int64_t entries = (int64_t)p.B * p.Hkv * p.N * p.K;
   const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
-  hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, p.K, M2, kS2Chunk, cb, stream);
+  hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, p.K, M2, M2, kS2Chunk, cb, stream);
   if (err != hipSuccess) return err;
-  S2Args a{q, k, counts, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, p.B, p.N, p.Hq, p.Hkv, p.C, p.K,
+  S2Args a{q, k, counts, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, cluster_bins(p.N, M2, M2), p.B, p.N, p.Hq, p.Hkv,
+           p.C, p.K,
            p.causal ? 1 : 0, p.cap, p.scale};
   const int64_t max_chunks = (entries + kS2Chunk - 1) / kS2Chunk + L.ncl;
   err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
