@@ -132,7 +132,7 @@ struct BwdArgs {
 };
 
 template <typename T, int D, int G, int NKB>
-__global__ __launch_bounds__(kBwdWaves* kWave) void attn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kernel(BwdArgs a) {
   constexpr int NS = D / 32;
   constexpr int TQ = 16 / G;
   constexpr int CP = NKB * 16;

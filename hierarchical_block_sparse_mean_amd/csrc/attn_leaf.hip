@@ -94,7 +94,7 @@ struct AttnLeafArgs {
 
 // NKB: 16-key blocks covering the leaf (even, C <= 16 NKB).
 template <typename T, int D, int G, int NKB>
-__global__ __launch_bounds__(attn_waves<NKB>() * kWave) void attn_leaf_kernel(AttnLeafArgs a) {
+__global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn_leaf_kernel(AttnLeafArgs a) {
   constexpr int NW = attn_waves<NKB>();
   constexpr int NS = D / 32;                   // contraction steps of S
   constexpr int TQ = 16 / G;                   // queries per 16-column tile

@@ -8,6 +8,12 @@
 namespace pisa {
 
 constexpr int kWave = 64;
+
+// For MFMA kernels: at least two waves per SIMD, so at most 256 registers per
+// lane.  Within that budget the compiler keeps MFMA accumulators in ordinary
+// VGPRs; with the 512-register budget of one wave per SIMD it places them in
+// AGPRs and copies every result out with v_accvgpr_read.
+#define PISA_MFMA_REGS __attribute__((amdgpu_waves_per_eu(2)))
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -139,6 +145,38 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 // 32-bit x from lane (lane ^ m) for a compile-time m after unrolling: DPP for
 // m = 1, 2 (quad permutations) and m = 8 (rotation of a 16-lane row by 8,
 // which is lane ^ 8 in either rotation direction); ds_bpermute otherwise.
+// Lane l's value and lane (l ^ M)'s (M = 16 or 32), in a lane-dependent
+// order (for commutative reductions), by the gfx950 permlane swaps: a VALU
+// exchange between rows with no LDS round trip.
+template <int M>
+__device__ __forceinline__ void xor_pair(float x, float& a, float& b) {
+  static_assert(M == 16 || M == 32, "rows of 16 or halves of 32 lanes");
+  const unsigned u = __float_as_uint(x);
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per row)
+__device__ __forceinline__ float rows_max(float x) {
+  float a, b;
+  xor_pair<16>(x, a, b);
+  xor_pair<32>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float a, b;
+  xor_pair<16>(x, a, b);
+  xor_pair<32>(a + b, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ int shfl_xor_fast(int x, int m) {
   if (m == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
   if (m == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]

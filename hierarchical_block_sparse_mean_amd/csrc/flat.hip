@@ -103,7 +103,7 @@ constexpr int kFlatTile = 64;  // leaf rows per LDS tile
 constexpr int kFlatCap = 64;   // candidate buffer per query
 
 template <int D, int G>
-__global__ __launch_bounds__(kFlatWaves* kWave) void flat_mfma_kernel(FlatMArgs a) {
+__global__ __launch_bounds__(kFlatWaves* kWave) PISA_MFMA_REGS void flat_mfma_kernel(FlatMArgs a) {
   constexpr int NS = D / 32;
   constexpr int RP = D + 8;  // fp16 row pitch in LDS
   __shared__ __align__(16) _Float16 s_tile[kFlatTile * RP];

@@ -145,7 +145,7 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
 // KP: K when K is 16 or 32 (top-K by half sorts), else 0 (full wave sort).
 // CNT: a separate instance that also accumulates the work counters
 template <int D, int G, int KP, bool CNT>
-__global__ __launch_bounds__(kRouteWaves* kWave) void route_mfma_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kRouteWaves* kWave) PISA_MFMA_REGS void route_mfma_kernel(RouteArgs a) {
   constexpr int NS = D / 32;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ RouteLds s_r[kRouteWaves];

@@ -76,20 +76,25 @@ struct S2Args {
 };
 
 // NCB: 16-key blocks covering the 2C keys of a tile (2C <= 16 NCB).
-// CB0: blocks of the first leaf when C is a multiple of 16 (C = 16 CB0), so
-// the leaf of a block is known at compile time; 0 for other C.
+// CB0: blocks of the first leaf when C is a multiple of 16 (C = 16 CB0): the
+// two leaves are then scored one after the other, CB0 blocks each; 0 for
+// other C (one pass over all NCB blocks, the leaf of a key by its index).
+// TT: query tiles scored together, so that each key fragment read from LDS
+// feeds TT products (the LDS traffic per pair falls by TT).
 // Transposed tiles: S^T = K Q^T with the keys as MFMA rows (A from LDS) and
 // 16 columns = 16 / G_Q queries x G_Q heads (B = q rows), so the LSE over a
 // leaf's keys is an in-lane reduction plus two cross-group shuffles, and the
 // GQA sum is a shuffle over the G_Q columns of a query.
-template <typename T, int D, int G, int NCB, int CB0>
-__global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
+template <typename T, int D, int G, int NCB, int CB0, int TT>
+__global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_kernel(S2Args a) {
   constexpr int NS = D / 32;                  // 32-wide contraction steps
   constexpr int TQ = 16 / G;                  // queries per 16-column tile
   constexpr int PITCH = D + 16 / sizeof(T);   // LDS row pitch (elements)
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [NCB*16][PITCH]
+  __shared__ int32_t s_pr[kS2Chunk];        // the chunk's pair codes
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -121,6 +126,8 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
     if (r < nkeys) v = *reinterpret_cast<const uint4*>(kh + (key0 + r) * D + d);
     *reinterpret_cast<uint4*>(s_k + r * PITCH + d) = v;
   }
+  for (int i = threadIdx.x; i < kS2Chunk; i += blockDim.x)
+    s_pr[i] = p_begin + i < p_end ? a.pairs[p_begin + i] : -1;
   __syncthreads();
 
   const int w = threadIdx.x / kWave, lane = lane_id();
@@ -129,102 +136,188 @@ __global__ __launch_bounds__(kS2Waves* kWave) void leaf_score_kernel(S2Args a) {
   const T* qb = static_cast<const T*>(a.q);
   const float sl2 = a.scale * kLog2e;  // logits in log2 units
   float* out_base = a.scores + bh * (int64_t)a.N * a.K * 2;
+  // q rows of the column's query; an empty column (prq < 0) reads query 0's
+  // rows, finite data whose results are masked and never stored
   auto load_q = [&](int32_t prq, Frag<T>* f) {
-    if (prq >= 0) {
-      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + (prq >> 5)) * D;
+    const int64_t tq = prq >= 0 ? (prq >> 5) : 0;
+    const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + tq) * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) f[s].zero();
-    }
+    for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
   };
-  const int64_t stride = (int64_t)kS2Waves * TQ;
-  int64_t tile = p_begin + (int64_t)w * TQ;
-  int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
-  Frag<T> fq[NS];
-  load_q(pr, fq);
-  for (; tile < p_end; tile += stride) {
-    // prefetch the next tile's pair and query rows
-    const int32_t pr_n = (tile + stride + qi < p_end) ? a.pairs[tile + stride + qi] : -1;
-    Frag<T> fn[NS];
-    load_q(pr_n, fn);
-    // re-read the key fragments from LDS every tile rather than keeping all
+  // keys key_local < limit count for the column's query (t >= key0 + key_local)
+  auto limit = [&](int32_t pr) -> int {
+    if (pr < 0) return 0;
+    const int64_t t = pr >> 5;
+    return a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
+  };
+  // LSE of one leaf from this lane's (masked) logits: max and sum of exp2 of
+  // (x - max) * scale*log2e, each over the lane's values and then the four
+  // lane groups (rows of the accumulator tiles)
+  auto leaf_lse = [&](float mx, auto&& sum_exp) -> float {
+    mx = rows_max(mx);
+    const float sm = rows_sum(sum_exp(-mx * sl2));  // exp2(-inf) = 0
+    return (mx == -INFINITY) ? -INFINITY : mx * a.scale + __log2f(sm) * kLn2;
+  };
+  // the two leaf scores of TT tiles of 16 / G_Q pairs each (column query qi)
+  auto score_tiles = [&](Frag<T> (&fq)[TT][NS], const int32_t (&pr)[TT], auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    // re-read the key fragments from LDS every step rather than keeping all
     // of them live in registers (which would cap occupancy at one wave): the
     // offset is opaque to the compiler, the pointer stays an LDS pointer
     int koff = 0;
     asm volatile("" : "+v"(koff));
     const T* sk = s_k + koff;
-    floatx4 acc[NCB];
+    int lim[TT];
+    float u[TT][2];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TT; ++tt) lim[tt] = limit(pr[tt]);
+    if constexpr (CB0 > 0) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        Frag<T> fk;
-        fk.load(sk + (cb * 16 + col) * PITCH + g * (D / 4) + 8 * s);
-        acc[cb] = mma(fk, fq[s], acc[cb]);
+      for (int leaf = 0; leaf < 2; ++leaf) {
+        floatx4 acc[TT][CB0];
+#pragma unroll
+        for (int cb = 0; cb < CB0; ++cb) {
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) acc[tt][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            Frag<T> fk;
+            fk.load(sk + ((leaf * CB0 + cb) * 16 + col) * PITCH + g * (D / 4) + 8 * s);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) acc[tt][cb] = mma(fk, fq[tt][s], acc[tt][cb]);
+          }
+        }
+        // masked chunks: keys at or beyond the column's limit drop out
+        if constexpr (MASK) {
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int cb = 0; cb < CB0; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[tt][cb][i] = (leaf * CB0 + cb) * 16 + 4 * g + i >= lim[tt] ? -INFINITY : acc[tt][cb][i];
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int cb = 0; cb < CB0; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[tt][cb][i]);
+          u[tt][leaf] = leaf_lse(mx, [&](float nb) {
+            float sm = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < CB0; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sm += exp2_nonpos(fmaf(acc[tt][cb][i], sl2, nb));
+            return sm;
+          });
+        }
+      }
+    } else {
+      floatx4 acc[TT][NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc[tt][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          Frag<T> fk;
+          fk.load(sk + (cb * 16 + col) * PITCH + g * (D / 4) + 8 * s);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) acc[tt][cb] = mma(fk, fq[tt][s], acc[tt][cb]);
+        }
+      }
+      // (all-zero key rows beyond 2C are masked too)
+      bool part = false;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) part |= lim[tt] < NCB * 16;
+      if (__ballot(part) != 0ull) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (cb * 16 + 4 * g + i >= lim[tt]) acc[tt][cb][i] = -INFINITY;
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+        for (int leaf = 0; leaf < 2; ++leaf) {
+          // key kl belongs to leaf (kl >= C)
+          float mx = -INFINITY;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if ((cb * 16 + 4 * g + i >= C) == (leaf == 1)) mx = fmaxf(mx, acc[tt][cb][i]);
+          u[tt][leaf] = leaf_lse(mx, [&](float nb) {
+            float sm = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if ((cb * 16 + 4 * g + i >= C) == (leaf == 1)) sm += exp2_nonpos(fmaf(acc[tt][cb][i], sl2, nb));
+            return sm;
+          });
+        }
       }
     }
-    // keys key_local < lim count for this column's query (t >= key0 + key_local)
-    int lim = 0;
-    if (pr >= 0) {
-      const int64_t t = pr >> 5;
-      lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
-    }
-    // masked raw dot products (the mask only where some column of the tile
-    // sees fewer keys than the tile holds); max per leaf; exp2 of
-    // (x - max) * scale*log2e
-    if (__ballot(lim < NCB * 16) != 0ull) {
+    // GQA sum over the G columns of each query
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (cb * 16 + 4 * g + i >= lim) acc[cb][i] = -INFINITY;
-    }
-    float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kl = cb * 16 + 4 * g + i;
-        const bool first = CB0 ? (cb < CB0) : (kl < C);
-        if (first) mx0 = fmaxf(mx0, acc[cb][i]);
-        else mx1 = fmaxf(mx1, acc[cb][i]);
+    for (int tt = 0; tt < TT; ++tt) {
+      const float u0 = lane_group_sum<G>(u[tt][0]);
+      const float u1 = lane_group_sum<G>(u[tt][1]);
+      if (g == 0 && hh == 0 && pr[tt] >= 0) {
+        const int64_t e = (int64_t)(pr[tt] >> 5) * a.K + (pr[tt] & 31);  // (t, slot) entry
+        out_base[e * 2] = u0;
+        out_base[e * 2 + 1] = u1;
       }
-    mx0 = fmaxf(mx0, __shfl_xor(mx0, 16));
-    mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
-    mx1 = fmaxf(mx1, __shfl_xor(mx1, 16));
-    mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
-    const float nb0 = -mx0 * sl2, nb1 = -mx1 * sl2;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kl = cb * 16 + 4 * g + i;
-        const bool first = CB0 ? (cb < CB0) : (kl < C);
-        if (first) s0 += exp2_nonpos(fmaf(acc[cb][i], sl2, nb0));  // exp2(-inf) = 0
-        else s1 += exp2_nonpos(fmaf(acc[cb][i], sl2, nb1));
-      }
-    s0 += __shfl_xor(s0, 16);
-    s0 += __shfl_xor(s0, 32);
-    s1 += __shfl_xor(s1, 16);
-    s1 += __shfl_xor(s1, 32);
-    constexpr float kLn2 = 0.6931471805599453f;
-    float u0 = (mx0 == -INFINITY) ? -INFINITY : mx0 * a.scale + __log2f(s0) * kLn2;
-    float u1 = (mx1 == -INFINITY) ? -INFINITY : mx1 * a.scale + __log2f(s1) * kLn2;
-    // GQA sum over the G columns of the query
-    u0 = lane_group_sum<G>(u0);
-    u1 = lane_group_sum<G>(u1);
-    if (g == 0 && hh == 0 && pr >= 0) {
-      const int64_t e = (int64_t)(pr >> 5) * a.K + (pr & 31);  // (t, slot) entry
-      out_base[e * 2] = u0;
-      out_base[e * 2 + 1] = u1;
     }
+  };
+  // steps of TT tiles: wave w takes steps w, w + W, w + 2W, ... (W = waves)
+  // of the chunk, with two query-row buffers: the next step's rows load
+  // while the current step is scored
+  constexpr int SP = TT * TQ;  // pairs per step
+  const int n = (int)(p_end - p_begin);
+  const int stride = kS2Waves * SP;
+  auto fetch = [&](int i, int32_t (&pr)[TT], Frag<T> (&f)[TT][NS]) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) fq[s] = fn[s];
-    pr = pr_n;
+    for (int tt = 0; tt < TT; ++tt) {
+      const int j = i + tt * TQ + qi;
+      pr[tt] = j < n ? s_pr[j] : -1;
+      load_q(pr[tt], f[tt]);
+    }
+  };
+  auto run = [&](auto mask_c) {
+    Frag<T> fa[TT][NS], fb[TT][NS];
+    int32_t pa[TT], pb[TT];
+    int i = w * SP;
+    if (i >= n) return;
+    fetch(i, pa, fa);
+    while (true) {
+      fetch(i + stride, pb, fb);
+      score_tiles(fa, pa, mask_c);
+      i += stride;
+      if (i >= n) break;
+      fetch(i + stride, pa, fa);
+      score_tiles(fb, pb, mask_c);
+      i += stride;
+      if (i >= n) break;
+    }
+  };
+  // With whole leaves (CB0 > 0) the mask is only needed in chunks where some
+  // query sees fewer than the 2C keys (its own block under the causal rule,
+  // or the last block of the sequence); the rest run without it.
+  // Columns without a pair (-1) need no mask: their results are not stored.
+  if constexpr (CB0 > 0) {
+    bool part = false;
+    for (int j = threadIdx.x; j < n; j += blockDim.x) part |= limit(s_pr[j]) < 2 * C;
+    if (__syncthreads_or(part)) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
+    run(std::false_type{});
   }
 }
 
@@ -301,19 +394,22 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
       PISA_LAUNCH("leaf_score", stream, kern, dim3((unsigned)max_chunks), dim3(kS2Waves * kWave), lds, a);
       return hipSuccess;
     };
+    // two tiles per step for 16-bit inputs (fp32 query rows take twice the
+    // registers)
+    constexpr int TT2 = sizeof(T) == 2 ? 2 : 1;
     hipError_t e;
     if (p.C == 32)
-      e = run(leaf_score_kernel<T, D, G, 4, 2>);
+      e = run(leaf_score_kernel<T, D, G, 4, 2, TT2>);
     else if (p.C == 64)
-      e = run(leaf_score_kernel<T, D, G, 8, 4>);
+      e = run(leaf_score_kernel<T, D, G, 8, 4, TT2>);
     else if (p.C == 128)
-      e = run(leaf_score_kernel<T, D, G, 16, 8>);
+      e = run(leaf_score_kernel<T, D, G, 16, 8, TT2>);
     else if (p.C <= 32)
-      e = run(leaf_score_kernel<T, D, G, 4, 0>);
+      e = run(leaf_score_kernel<T, D, G, 4, 0, 1>);
     else if (p.C <= 64)
-      e = run(leaf_score_kernel<T, D, G, 8, 0>);
+      e = run(leaf_score_kernel<T, D, G, 8, 0, 1>);
     else
-      e = run(leaf_score_kernel<T, D, G, 16, 0>);
+      e = run(leaf_score_kernel<T, D, G, 16, 0, 1>);
     if (e != hipSuccess) return e;
     return hipGetLastError();
   });
