@@ -241,7 +241,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
       const bool lower = (lane & j) == 0;
       const bool desc = (lane & k) == 0;
       const bool take_max = (lower == desc);
-      key = take_max ? (key > other ? key : other) : (key < other ? key : other);
+      key = ((key > other) == take_max) ? key : other;
     }
   }
   return key;
@@ -258,7 +258,9 @@ __device__ __forceinline__ uint64_t group_sort_desc(uint64_t key) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       const uint64_t other = shfl_xor_u64_fast(key, j);
       const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      key = take_max ? (key > other ? key : other) : (key < other ? key : other);
+      // keep the own key where (key > other) agrees with take_max: one
+      // 64-bit compare, a mask operation and two selects
+      key = ((key > other) == take_max) ? key : other;
     }
   }
   return key;
@@ -271,7 +273,7 @@ template <int K>
 __device__ __forceinline__ uint64_t top_half(uint64_t key) {
   key = group_sort_desc<K>(key);
   const uint64_t other = shfl_xor_u64(key, K);
-  return ((lane_id() & K) == 0) ? (key > other ? key : other) : key;
+  return ((lane_id() & K) == 0 && other > key) ? other : key;
 }
 
 // ---- pyramid geometry (capacity layout, see pisa.h) -----------------------

@@ -19,7 +19,7 @@ namespace pisa {
 struct __align__(16) RouteLds {
   int32_t cand[kWave];  // candidate block indices of the current level
   float score[kWave];   // their GQA-summed scores
-  int32_t ex[16];       // block-floating-point exponents of a 16-row tile
+  float2 fb[16];        // (scale, bias) of the 16 rows of a tile
 };
 
 // G dot products of one fp32 pyramid row with the G query vectors in LDS.

@@ -84,16 +84,17 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
 // child rows r, as (16 child rows) x d x (16 columns = the G_Q query heads)
 // v_mfma_f32_16x16x32_f16 tiles.  Rows come from the pyramid's fp16
 // block-floating-point copy (row * 2^-ex[row]); q is bf16, so q * 2^-eq is
-// exact in fp16; the logit is rescaled by 2^(ex + eq) in fp32.  A row costs
-// d * 2 bytes of gather (half the fp32 row).  The sibling LSE is in-lane
-// (accumulator rows 2c, 2c+1) and the GQA sum a shuffle over the G_Q columns.
+// exact in fp16; the logit in log2 units is acc * 2^(ex + eq) * scale*log2e.
+// A row costs d * 2 bytes of gather (half the fp32 row).  The sibling LSE is
+// in-lane (accumulator rows 2c, 2c+1) and the GQA sum a shuffle over the G_Q
+// columns.
 template <int D, int G>
 __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq, const _Float16* hb,
                                                  const int32_t* xb, const PyrGeom& geo, int32_t m_child, int32_t tl,
                                                  int32_t l, float sl2, int64_t* rows_out) {
   constexpr int NS = D / 32;
   const int lane = lane_id(), g = lane >> 4, col = lane & 15;
-  const int64_t lvl = geo.level_off[l - 1];
+  const int32_t lvl = (int32_t)geo.level_off[l - 1];
   for (int rt = 0; rt * 16 < 2 * nA; ++rt) {
     // A row `col` of the tile: child (row & 1) of candidate row >> 1
     const int row = 16 * rt + col;
@@ -102,36 +103,37 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
     const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
     if (rows_out != nullptr) *rows_out += __popcll(__ballot(vrow) & 0xFFFFull);
     // an invalid row reads row 0 of the level instead (finite data): its
-    // accumulator row is discarded through the INT32_MIN exponent below
-    const int64_t rr = lvl + (vrow ? r : 0);
-    const int32_t er = vrow ? xb[rr] : INT32_MIN;
+    // accumulator row gets scale 0 and bias -inf below.  Offsets within a
+    // head fit 32 bits.
+    const uint32_t rr = (uint32_t)(lvl + (vrow ? r : 0));
+    const int32_t er = xb[rr];
     // step st covers elements [32 st, 32 st + 32): the four lane groups read
     // one contiguous 64-byte span of the row per load.  All NS loads are
     // issued before the first product (the barrier keeps the scheduler from
     // sinking each load next to its use, which serialises the round trips).
     halfx8 fa[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * D + 32 * st + 8 * g);
+    for (int st = 0; st < NS; ++st) fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)D + 32 * st + 8 * g);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS; ++st) acc = mma16x16x32(fa[st], fq[st], acc);
-    // accumulator row 4g+i: its exponent (INT32_MIN = invalid child) comes
-    // from lane 4g+i through LDS; logits in log2 units
-    if (g == 0) s.ex[col] = er;
+    // accumulator row 4g+i: its (scale, bias) = (2^ex * scale*log2e, 0), or
+    // (0, -inf) for a missing child, comes from lane 4g+i through LDS; the
+    // column's own 2^eq (one per query head) is applied by each lane.  Both
+    // factors are exact powers of two times scale*log2e: one rounding.
+    if (g == 0) s.fb[col] = vrow ? float2{ldexpf(sl2, er), 0.f} : float2{0.f, -INFINITY};
     wave_sync();
-    const int4 er4 = *reinterpret_cast<const int4*>(&s.ex[4 * g]);
-    const int32_t ers[4] = {er4.x, er4.y, er4.z, er4.w};
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (ers[i] == INT32_MIN) ? -INFINITY : ldexpf(acc[i], ers[i] + eq) * sl2;
-    wave_sync();  // s.ex is rewritten by the next row tile
+    const float4 fb01 = *reinterpret_cast<const float4*>(&s.fb[4 * g]);
+    const float4 fb23 = *reinterpret_cast<const float4*>(&s.fb[4 * g + 2]);
+    wave_sync();  // s.fb is rewritten by the next row tile
+    const float x0 = fmaf(ldexpf(acc[0], eq), fb01.x, fb01.y), x1 = fmaf(ldexpf(acc[1], eq), fb01.z, fb01.w);
+    const float x2 = fmaf(ldexpf(acc[2], eq), fb23.x, fb23.y), x3 = fmaf(ldexpf(acc[3], eq), fb23.z, fb23.w);
+    // sibling LSE: max + log2(1 + 2^-|a - b|).  Child 0 of a candidate always
+    // exists, so a stored score is finite; a missing child 1 (-inf) adds 0.
     float u[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float m = fmaxf(x[2 * p], x[2 * p + 1]);
-      u[p] = (m == -INFINITY) ? -INFINITY : m + __log2f(exp2_nonpos(x[2 * p] - m) + exp2_nonpos(x[2 * p + 1] - m));
-    }
+    u[0] = fmaxf(x0, x1) + __log2f(1.f + exp2_nonpos(-fabsf(x0 - x1)));
+    u[1] = fmaxf(x2, x3) + __log2f(1.f + exp2_nonpos(-fabsf(x2 - x3)));
     u[0] = lane_group_sum<G>(u[0]);
     u[1] = lane_group_sum<G>(u[1]);
     const int c0 = 8 * rt + 2 * g;
