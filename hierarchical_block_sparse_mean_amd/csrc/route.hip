@@ -25,6 +25,11 @@ struct RouteArgs {
   int64_t cap;
   float scale;
   PyrGeom geo;
+  // stage 1: levels >= stage_level of the fp16 summaries (stage_rows rows from
+  // row stage_off of a head) sit in LDS; chunks workgroups per (b, h)
+  int32_t stage_level, stage_rows;
+  int64_t stage_off;
+  int32_t chunks;
 };
 
 // Workgroup -> (b, h, first query).  Consecutive workgroups go to consecutive
@@ -88,13 +93,14 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
 // A row costs d * 2 bytes of gather (half the fp32 row).  The sibling LSE is
 // in-lane (accumulator rows 2c, 2c+1) and the GQA sum a shuffle over the G_Q
 // columns.
-template <int D, int G>
+// hb / xb: the rows (pitch PITCH elements) and exponents of a head, in LDS
+// or in global memory; lvl: the child level's first row there.
+template <int D, int G, int PITCH>
 __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq, const _Float16* hb,
-                                                 const int32_t* xb, const PyrGeom& geo, int32_t m_child, int32_t tl,
-                                                 int32_t l, float sl2, int64_t* rows_out) {
+                                                 const int32_t* xb, int32_t lvl, int32_t m_child, int32_t tl,
+                                                 float sl2, int64_t* rows_out) {
   constexpr int NS = D / 32;
   const int lane = lane_id(), g = lane >> 4, col = lane & 15;
-  const int32_t lvl = (int32_t)geo.level_off[l - 1];
   for (int rt = 0; rt * 16 < 2 * nA; ++rt) {
     // A row `col` of the tile: child (row & 1) of candidate row >> 1
     const int row = 16 * rt + col;
@@ -113,7 +119,8 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
     // sinking each load next to its use, which serialises the round trips).
     halfx8 fa[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)D + 32 * st + 8 * g);
+    for (int st = 0; st < NS; ++st)
+      fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)PITCH + 32 * st + 8 * g);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -145,111 +152,171 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
 }
 
 // KP: K when K is 16 or 32 (top-K by half sorts), else 0 (full wave sort).
-// CNT: a separate instance that also accumulates the work counters
+// CNT: a separate instance that also accumulates the work counters.
+// Persistent workgroups of kRouteWgWaves waves, chunks of them per (b, h):
+// the workgroup first copies the coarse levels of its head's fp16 summaries
+// (every level from stage_level up, rows padded by 16 bytes so that the 16
+// rows of a fragment read fall in different LDS banks) into LDS, where every
+// query of the head finds them; each wave then routes the queries
+// t = chunk W + w, + chunks W, ... (W = waves).  Levels whose children are
+// staged read them from LDS, the finer levels gather from global memory.
+constexpr int kRouteWgWaves = 16;
+
+template <int D>
+constexpr int stage_pitch() { return D + 8; }  // fp16 elements per staged row
+
 template <int D, int G, int KP, bool CNT>
-__global__ __launch_bounds__(kRouteWaves* kWave) PISA_MFMA_REGS void route_mfma_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfma_kernel(RouteArgs a) {
   constexpr int NS = D / 32;
+  constexpr int SP = stage_pitch<D>();
   constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ RouteLds s_r[kRouteWaves];
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ RouteLds s_r[kRouteWgWaves];
+  _Float16* s_rows = reinterpret_cast<_Float16*>(smem_raw);                             // [stage_rows][SP]
+  int32_t* s_exs = reinterpret_cast<int32_t*>(smem_raw + (size_t)a.stage_rows * SP * 2);  // [stage_rows]
   const int w = threadIdx.x / kWave, lane = lane_id();
-  int b, h;
-  int64_t t0;
-  map_query_block(a.Hkv, a.B, b, h, t0);
-  const int64_t t = t0 + w;
-  if (t >= a.N) return;  // wave-uniform; the kernel has no workgroup barrier
-  const int g = lane >> 4, col = lane & 15;
-  // B operand: column col = query head col of the group (zero beyond G_Q),
-  // scaled by 2^-eq into fp16 (exact for bf16 values)
-  float qv[NS][8];
-  float mx = 0.f;
-  if (col < G) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Hq + h * G + col) * a.N + t) * D;
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      load8<uint16_t>(qrow + 32 * st + 8 * g, qv[st]);  // same element order as the rows
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[st][e]));
-    }
-  } else {
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[st][e] = 0.f;
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const int eq = row_exponent(mx);
-  halfx8 fq[NS];
-#pragma unroll
-  for (int st = 0; st < NS; ++st)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) fq[st][e] = to_f16_scaled(qv[st][e], eq);
+  const int64_t bid = blockIdx.x;
+  const int h = (int)(bid % a.Hkv);
+  const int64_t rb = bid / a.Hkv;
+  const int b = (int)(rb % a.B);
+  const int chunk = (int)(rb / a.B);
   const int64_t bh = (int64_t)b * a.Hkv + h;
   const _Float16* hb = a.f16 + bh * a.geo.rows * D;
   const int32_t* xb = a.ex + bh * a.geo.rows;
+  for (int i = threadIdx.x; i < a.stage_rows * (D / 8); i += blockDim.x) {
+    const int r = i / (D / 8), d = (i % (D / 8)) * 8;
+    *reinterpret_cast<uint4*>(s_rows + r * SP + d) = *reinterpret_cast<const uint4*>(hb + (a.stage_off + r) * D + d);
+  }
+  for (int i = threadIdx.x; i < a.stage_rows; i += blockDim.x) s_exs[i] = xb[a.stage_off + i];
+  __syncthreads();  // the only workgroup barrier: the query loop below is per wave
+
+  const int g = lane >> 4, col = lane & 15;
   RouteLds& s = s_r[w];
   const bool causal = a.causal != 0;
   const float sl2 = a.scale * kLog2e;
-  int nA = 1;
-  if (lane == 0) s.cand[0] = 0;
-  int32_t kept = (lane == 0) ? 0 : -1;
-  int nI = 1;
-  int64_t w_rows = 0, w_cands = 0, w_levels = 0;  // diagnostics only
-  int64_t* rows_ptr = CNT ? &w_rows : nullptr;
-  wave_sync();
   // level sizes and the last valid block by shifts: M_l = ceil(M_1 / 2^(l-1))
   // and block j of level l starts at j C 2^(l-1) <= t iff j <= (t / C) >> (l-1)
   const int32_t M1 = (int32_t)level_rows(a.N, a.C, 1);
-  const int32_t tc = (int32_t)t / a.C;
-  for (int32_t l = a.L; l >= 2; --l) {
-    // valid blocks of level l: index < M_l and (causal) first token <= t
-    const int32_t ml = ((M1 - 1) >> (l - 1)) + 1;
-    const int32_t tl_blk = causal ? (tc >> (l - 1)) : 0x7fffffff;
-    const int32_t j = (lane < nA) ? s.cand[lane] : 0x7fffffff;
-    const bool valid = j < ml && j <= tl_blk;
-    const uint64_t mask = __ballot(valid);
-    const int pos = __popcll(mask & ((1ull << lane) - 1ull));
-    nA = __popcll(mask);
-    wave_sync();
-    if (valid) s.cand[pos] = j;
-    wave_sync();
-    if (nA > a.K) {
-      const int32_t m_child = ((M1 - 1) >> (l - 2)) + 1;
-      const int32_t tl = causal ? (tc >> (l - 2)) : 0x7fffffff;
-      score_level_mfma<D, G>(s, nA, fq, eq, hb, xb, a.geo, m_child, tl, l, sl2, rows_ptr);
-      w_cands += nA;
-      w_levels += 1;
-      wave_sync();
-      uint64_t key = (lane < nA) ? score_key(s.score[lane], s.cand[lane]) : 0ull;
-      if (KP) key = top_half<(KP ? KP : 16)>(key);
-      else key = wave_sort_desc(key);
-      nI = a.K;
-      kept = (lane < nI) ? key_index(key) : -1;
-    } else {
-      nI = nA;
-      kept = (lane < nA) ? s.cand[lane] : -1;
-    }
-    if (l > 2) {
-      wave_sync();
-      if (lane < nI) {
-        s.cand[2 * lane] = 2 * kept;
-        s.cand[2 * lane + 1] = 2 * kept + 1;
+  const int64_t tstep = (int64_t)a.chunks * kRouteWgWaves;
+  for (int64_t t = (int64_t)chunk * kRouteWgWaves + w; t < a.N; t += tstep) {
+    // B operand: column col = query head col of the group (zero beyond G_Q),
+    // scaled by 2^-eq into fp16 (exact for bf16 values)
+    float qv[NS][8];
+    float mx = 0.f;
+    if (col < G) {
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Hq + h * G + col) * a.N + t) * D;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        load8<uint16_t>(qrow + 32 * st + 8 * g, qv[st]);  // same element order as the rows
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[st][e]));
       }
-      nA = 2 * nI;
+    } else {
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[st][e] = 0.f;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const int eq = row_exponent(mx);
+    halfx8 fq[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fq[st][e] = to_f16_scaled(qv[st][e], eq);
+    int nA = 1;
+    wave_sync();  // the previous query's last reads of s are done
+    if (lane == 0) s.cand[0] = 0;
+    int32_t kept = (lane == 0) ? 0 : -1;
+    int nI = 1;
+    int64_t w_rows = 0, w_cands = 0, w_levels = 0;  // diagnostics only
+    int64_t* rows_ptr = CNT ? &w_rows : nullptr;
+    wave_sync();
+    const int32_t tc = (int32_t)t / a.C;
+    for (int32_t l = a.L; l >= 2; --l) {
+      // valid blocks of level l: index < M_l and (causal) first token <= t
+      const int32_t ml = ((M1 - 1) >> (l - 1)) + 1;
+      const int32_t tl_blk = causal ? (tc >> (l - 1)) : 0x7fffffff;
+      const int32_t j = (lane < nA) ? s.cand[lane] : 0x7fffffff;
+      const bool valid = j < ml && j <= tl_blk;
+      const uint64_t mask = __ballot(valid);
+      const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+      nA = __popcll(mask);
       wave_sync();
+      if (valid) s.cand[pos] = j;
+      wave_sync();
+      if (nA > a.K) {
+        const int32_t m_child = ((M1 - 1) >> (l - 2)) + 1;
+        const int32_t tl = causal ? (tc >> (l - 2)) : 0x7fffffff;
+        const int32_t lvl = (int32_t)a.geo.level_off[l - 1];
+        if (l - 1 >= a.stage_level)
+          score_level_mfma<D, G, SP>(s, nA, fq, eq, s_rows, s_exs, lvl - (int32_t)a.stage_off, m_child, tl, sl2,
+                                     rows_ptr);
+        else
+          score_level_mfma<D, G, D>(s, nA, fq, eq, hb, xb, lvl, m_child, tl, sl2, rows_ptr);
+        w_cands += nA;
+        w_levels += 1;
+        wave_sync();
+        uint64_t key = (lane < nA) ? score_key(s.score[lane], s.cand[lane]) : 0ull;
+        if (KP) key = top_half<(KP ? KP : 16)>(key);
+        else key = wave_sort_desc(key);
+        nI = a.K;
+        kept = (lane < nI) ? key_index(key) : -1;
+      } else {
+        nI = nA;
+        kept = (lane < nA) ? s.cand[lane] : -1;
+      }
+      if (l > 2) {
+        wave_sync();
+        if (lane < nI) {
+          s.cand[2 * lane] = 2 * kept;
+          s.cand[2 * lane + 1] = 2 * kept + 1;
+        }
+        nA = 2 * nI;
+        wave_sync();
+      }
+    }
+    uint64_t k2 = (lane < nI) ? index_key(kept, 0.f) : 0ull;
+    if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
+    else k2 = wave_sort_desc(k2);
+    if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
+    if (CNT && lane == 0) {
+      atomicAdd(&a.counts[0], 1ull);
+      atomicAdd(&a.counts[1], (unsigned long long)w_cands);
+      atomicAdd(&a.counts[2], (unsigned long long)w_rows);
+      atomicAdd(&a.counts[3], (unsigned long long)w_levels);
+      atomicAdd(&a.counts[4], (unsigned long long)nI);
     }
   }
-  uint64_t k2 = (lane < nI) ? index_key(kept, 0.f) : 0ull;
-  if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
-  else k2 = wave_sort_desc(k2);
-  if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
-  if (CNT && lane == 0) {
-    atomicAdd(&a.counts[0], 1ull);
-    atomicAdd(&a.counts[1], (unsigned long long)w_cands);
-    atomicAdd(&a.counts[2], (unsigned long long)w_rows);
-    atomicAdd(&a.counts[3], (unsigned long long)w_levels);
-    atomicAdd(&a.counts[4], (unsigned long long)nI);
+}
+
+// Staged levels for stage 1: the coarsest levels of a head whose rows fit a
+// 144 KB LDS budget (the whole pyramid for short sequences), one workgroup
+// per compute unit (two with half the budget each were slower: the finer
+// levels gathered from memory cost more than the extra waves gain).
+static void route_stage_plan(const Problem& p, RouteArgs& a, size_t& lds) {
+  constexpr int wg_per_cu = 1;
+  const size_t pitch_bytes = (size_t)(p.D + 8) * 2 + 4;  // padded fp16 row + exponent
+  const size_t budget = (size_t)144 * 1024;
+  a.stage_level = p.geo.levels_cap + 1;
+  a.stage_rows = 0;
+  a.stage_off = p.geo.rows;
+  for (int32_t l = 1; l <= p.geo.levels_cap; ++l) {
+    const int64_t rows = p.geo.rows - p.geo.level_off[l];
+    if ((size_t)rows * pitch_bytes <= budget) {
+      a.stage_level = l;
+      a.stage_rows = (int32_t)rows;
+      a.stage_off = p.geo.level_off[l];
+      break;
+    }
   }
+  lds = (size_t)a.stage_rows * pitch_bytes;
+  // workgroups: about wg_per_cu per compute unit over all (b, h)
+  const int64_t heads = (int64_t)p.B * p.Hkv;
+  const int64_t want = (256 * (int64_t)wg_per_cu + heads - 1) / heads;
+  const int64_t most = (p.N + kRouteWgWaves - 1) / kRouteWgWaves;
+  a.chunks = (int32_t)(want < 1 ? 1 : (want > most ? most : want));
 }
 
 hipError_t launch_route(const Problem& p, const void* q, const void* k, const float* pyr, int32_t* idx,
@@ -257,7 +324,7 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
   const int64_t plane = (int64_t)p.B * p.Hkv * p.geo.rows * p.D;
   const _Float16* f16 = reinterpret_cast<const _Float16*>(pyr + plane);
   RouteArgs a{counts, q, k, pyr, f16, reinterpret_cast<const int32_t*>(f16 + plane), idx, score, p.B, p.N, p.Hq, p.Hkv, p.C, p.K, p.L, p.causal ? 1 : 0,
-              p.cap, p.scale, p.geo};
+              p.cap, p.scale, p.geo, 0, 0, 0, 1};
   const int64_t blocks = (int64_t)p.B * p.Hkv * ((p.N + kRouteWaves - 1) / kRouteWaves);
   return dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
     using T = std::remove_pointer_t<decltype(tp)>;
@@ -267,13 +334,24 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
       PISA_LAUNCH("route_fused", stream, (route_kernel<T, D, G, true>), dim3((unsigned)blocks),
                   dim3(kRouteWaves * kWave), 0, a);
     else if (std::is_same<T, uint16_t>::value) {
-      auto run = [&](auto kern) {
-        PISA_LAUNCH(counts ? "route_stage1_counted" : "route_stage1", stream, kern, dim3((unsigned)blocks),
-                    dim3(kRouteWaves * kWave), 0, a);
+      RouteArgs ra = a;
+      size_t lds = 0;
+      route_stage_plan(p, ra, lds);
+      const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * ra.chunks)), block(kRouteWgWaves * kWave);
+      auto run = [&](auto kern) -> hipError_t {
+        if (lds > 65536) {
+          hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (e != hipSuccess) return e;
+        }
+        PISA_LAUNCH(counts ? "route_stage1_counted" : "route_stage1", stream, kern, grid, block, lds, ra);
+        return hipSuccess;
       };
-      if (p.K == 16) counts ? run(route_mfma_kernel<D, G, 16, true>) : run(route_mfma_kernel<D, G, 16, false>);
-      else if (p.K == 32) counts ? run(route_mfma_kernel<D, G, 32, true>) : run(route_mfma_kernel<D, G, 32, false>);
-      else counts ? run(route_mfma_kernel<D, G, 0, true>) : run(route_mfma_kernel<D, G, 0, false>);
+      hipError_t e;
+      if (p.K == 16) e = counts ? run(route_mfma_kernel<D, G, 16, true>) : run(route_mfma_kernel<D, G, 16, false>);
+      else if (p.K == 32) e = counts ? run(route_mfma_kernel<D, G, 32, true>) : run(route_mfma_kernel<D, G, 32, false>);
+      else e = counts ? run(route_mfma_kernel<D, G, 0, true>) : run(route_mfma_kernel<D, G, 0, false>);
+      if (e != hipSuccess) return e;
     }
     else
       PISA_LAUNCH("route_stage1", stream, (route_kernel<T, D, G, false>), dim3((unsigned)blocks),
