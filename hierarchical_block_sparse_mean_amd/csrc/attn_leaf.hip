@@ -106,6 +106,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
   T* s_vt = s_k + CP * KP;                   // [D][VP]
   // a tile's 16 output columns x D, staged so each lane stores 16-byte pieces
   __shared__ __align__(16) T s_o[NW][16][D + 16 / sizeof(T)];
+  __shared__ int32_t s_pr[kAttnChunk];  // the chunk's pair codes
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -142,6 +143,8 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
 #pragma unroll
     for (int e = 0; e < EPV; ++e) s_vt[(d + e) * VP + r] = ve[e];
   }
+  for (int i = threadIdx.x; i < kAttnChunk; i += blockDim.x)
+    s_pr[i] = p_begin + i < p_end ? a.pairs[p_begin + i] : -1;
   __syncthreads();
 
   const int w = threadIdx.x / kWave, lane = lane_id();
@@ -149,22 +152,18 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
   const int qi = col / G, hh = col % G;
   const T* qb = static_cast<const T*>(a.q);
   // column col of a tile = query qi (its pair) x head hh; the B operand of
-  // S^T = K Q^T is that query head's row
+  // S^T = K Q^T is that query head's row.  An empty column (pr < 0) reads
+  // query 0's row (finite data, never stored).
   auto load_q = [&](int32_t pr, Frag<T>* f) {
-    if (pr >= 0) {
-      const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + (pr >> 5)) * D;
+    const int64_t tq = pr >= 0 ? (pr >> 5) : 0;
+    const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + tq) * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) f[s].zero();
-    }
+    for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
   };
-  const int64_t stride = (int64_t)NW * TQ;
-  for (int64_t tile = p_begin + (int64_t)w * TQ; tile < p_end; tile += stride) {
-    const int32_t pr = (tile + qi < p_end) ? a.pairs[tile + qi] : -1;
-    Frag<T> fq[NS];
-    load_q(pr, fq);
+  // one tile of 16 / G_Q pairs; MASK: some column of the chunk sees fewer
+  // keys than the tile holds (causal diagonal leaf, last leaf, zero padding)
+  auto attend_tile = [&](const Frag<T>* fq, int32_t pr, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const bool live = pr >= 0;
     const int64_t t = live ? (pr >> 5) : -1;
     // K / V^T fragments are re-read from LDS every tile (an offset opaque to
@@ -186,22 +185,19 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
     }
     // column softmax statistics (keys are rows 4g+i of each 16-key block):
     // max on the raw dot products, then p = exp2((x - max) * scale*log2e)
-    const int lim = live ? (int)(a.causal ? (t - key0 + 1 < nkeys ? t - key0 + 1 : nkeys) : nkeys) : 0;
-    // the mask only where some column of the tile sees fewer keys than held
-    if (__ballot(lim < NKB * 16) != 0ull) {
+    if constexpr (MASK) {
+      const int lim = live ? (int)(a.causal ? (t - key0 + 1 < nkeys ? t - key0 + 1 : nkeys) : nkeys) : 0;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kb * 16 + 4 * g + i >= lim) acc[kb][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) acc[kb][i] = kb * 16 + 4 * g + i >= lim ? -INFINITY : acc[kb][i];
     }
     float mraw = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, acc[kb][i]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 16));
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    mraw = rows_max(mraw);
     const float sl2 = a.scale * 1.4426950408889634f;
     const float nb = -mraw * sl2;
     float l = 0.f;
@@ -213,8 +209,7 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
         acc[kb][i] = pv;
         l += pv;
       }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows_sum(l);
     const float m = mraw * a.scale;  // the partial's max logit (natural units)
     // O^T = V^T P^T, contraction over 32 keys = 16-key blocks (2s, 2s+1)
     floatx4 oacc[D / 16];
@@ -262,7 +257,40 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
       }
     }
     wave_sync();
+  };
+  // tiles w, w + W, ... of the chunk (W = waves), two query-row buffers: the
+  // next tile's rows load while the current tile is attended
+  const int n = (int)(p_end - p_begin);
+  const int stride = NW * TQ;
+  auto pair_at = [&](int i) -> int32_t { return i + qi < n ? s_pr[i + qi] : -1; };
+  auto run = [&](auto mask_c) {
+    Frag<T> fa[NS], fb[NS];
+    int i = w * TQ;
+    if (i >= n) return;
+    int32_t pa = pair_at(i), pb;
+    load_q(pa, fa);
+    while (true) {
+      pb = pair_at(i + stride);
+      load_q(pb, fb);
+      attend_tile(fa, pa, mask_c);
+      i += stride;
+      if (i >= n) break;
+      pa = pair_at(i + stride);
+      load_q(pa, fa);
+      attend_tile(fb, pb, mask_c);
+      i += stride;
+      if (i >= n) break;
+    }
+  };
+  // zero-padded keys (C < 16 NKB) always need the mask; otherwise only chunks
+  // holding a query that sees fewer than C keys of the leaf
+  bool part = CP > C;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t tq = s_pr[i] >> 5;
+    part |= (a.causal && tq - key0 + 1 < C) || nkeys < C;
   }
+  if (__syncthreads_or(part)) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---- merge the K partials of every (query, KV head) ---------------------------
