@@ -19,7 +19,7 @@ namespace pisa {
 struct __align__(16) RouteLds {
   int32_t cand[kWave];  // candidate block indices of the current level
   float score[kWave];   // their GQA-summed scores
-  float2 fb[16];        // (scale, bias) of the 16 rows of a tile
+  float2 fb[64];        // (scale, bias) of the rows of up to 4 tiles
 };
 
 // G dot products of one fp32 pyramid row with the G query vectors in LDS.

@@ -25,9 +25,9 @@ struct RouteArgs {
   int64_t cap;
   float scale;
   PyrGeom geo;
-  // stage 1: levels >= stage_level of the fp16 summaries (stage_rows rows from
-  // row stage_off of a head) sit in LDS; chunks workgroups per (b, h)
-  int32_t stage_level, stage_rows;
+  // stage 1: levels stage_level..stage_top of the fp16 summaries (stage_rows
+  // rows from row stage_off of a head) sit in LDS; chunks workgroups per (b, h)
+  int32_t stage_level, stage_top, stage_rows;
   int64_t stage_off;
   int32_t chunks;
 };
@@ -95,58 +95,86 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
 // columns.
 // hb / xb: the rows (pitch PITCH elements) and exponents of a head, in LDS
 // or in global memory; lvl: the child level's first row there.
+// Only G_Q of a tile's 16 columns carry query heads, so the results of
+// P = 16 / max(G_Q, 4) consecutive row tiles are packed into one accumulator
+// set (tile p's useful columns moved into lane bank(s) p by DPP row shifts)
+// before the scaling, the sibling LSE and the GQA sum, which then run once
+// per P tiles on lanes that all carry data.
 template <int D, int G, int PITCH>
-__device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq, const _Float16* hb,
+__device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq_p, const _Float16* hb,
                                                  const int32_t* xb, int32_t lvl, int32_t m_child, int32_t tl,
                                                  float sl2, int64_t* rows_out) {
   constexpr int NS = D / 32;
+  constexpr int GP = G < 4 ? 4 : G;  // lanes per packed tile
+  constexpr int P = 16 / GP;         // tiles per packed set
   const int lane = lane_id(), g = lane >> 4, col = lane & 15;
-  for (int rt = 0; rt * 16 < 2 * nA; ++rt) {
-    // A row `col` of the tile: child (row & 1) of candidate row >> 1
-    const int row = 16 * rt + col;
-    const int c = row >> 1;
-    const int32_t r = (c < nA) ? 2 * s.cand[c] + (row & 1) : 0x7fffffff;
-    const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
-    if (rows_out != nullptr) *rows_out += __popcll(__ballot(vrow) & 0xFFFFull);
-    // an invalid row reads row 0 of the level instead (finite data): its
-    // accumulator row gets scale 0 and bias -inf below.  Offsets within a
-    // head fit 32 bits.
-    const uint32_t rr = (uint32_t)(lvl + (vrow ? r : 0));
-    const int32_t er = xb[rr];
-    // step st covers elements [32 st, 32 st + 32): the four lane groups read
-    // one contiguous 64-byte span of the row per load.  All NS loads are
-    // issued before the first product (the barrier keeps the scheduler from
-    // sinking each load next to its use, which serialises the round trips).
-    halfx8 fa[NS];
+  const int qp = col / GP, hc = col % GP;  // packed: tile qp of the set, head hc
+  const int nt = (2 * nA + 15) >> 4;      // row tiles of this level
+  for (int rt0 = 0; rt0 < nt; rt0 += P) {
+    floatx4 acc[P];
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
-      fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)PITCH + 32 * st + 8 * g);
-    __builtin_amdgcn_sched_barrier(0);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < P; ++q) {
+      // A row `col` of tile rt: child (row & 1) of candidate row >> 1; an
+      // invalid row (or a tile past the last) reads row 0 of the level
+      // (finite data) and gets scale 0 and bias -inf below.  Offsets within
+      // a head fit 32 bits.
+      const int rt = rt0 + q;
+      const int row = 16 * rt + col;
+      const int c = row >> 1;
+      const int32_t r = (c < nA) ? 2 * s.cand[c] + (row & 1) : 0x7fffffff;
+      const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
+      if (rows_out != nullptr && rt < nt) *rows_out += __popcll(__ballot(vrow) & 0xFFFFull);
+      const uint32_t rr = (uint32_t)(lvl + (vrow ? r : 0));
+      const int32_t er = xb[rr];
+      // step st covers elements [32 st, 32 st + 32): the four lane groups
+      // read one contiguous 64-byte span of the row per load.  All NS loads
+      // are issued before the first product (the barrier keeps the
+      // scheduler from sinking each load next to its use).
+      halfx8 fa[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) acc = mma16x16x32(fa[st], fq[st], acc);
-    // accumulator row 4g+i: its (scale, bias) = (2^ex * scale*log2e, 0), or
-    // (0, -inf) for a missing child, comes from lane 4g+i through LDS; the
-    // column's own 2^eq (one per query head) is applied by each lane.  Both
-    // factors are exact powers of two times scale*log2e: one rounding.
-    if (g == 0) s.fb[col] = vrow ? float2{ldexpf(sl2, er), 0.f} : float2{0.f, -INFINITY};
+      for (int st = 0; st < NS; ++st)
+        fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)PITCH + 32 * st + 8 * g);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) acc[q] = mma16x16x32(fa[st], fq[st], acc[q]);
+      // (scale, bias) of row 16 q + col: (2^ex * scale*log2e, 0), or (0, -inf)
+      // for a missing child
+      if (g == 0) s.fb[16 * q + col] = vrow ? float2{ldexpf(sl2, er), 0.f} : float2{0.f, -INFINITY};
+    }
+    // pack: lane bank(s) of tile q take tile q's columns 0..GP-1
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[0][i];
+      if constexpr (P >= 2)
+        v = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(acc[1][i]), 0x110 + GP,
+                                                       0xF, P == 2 ? 0xC : 0x2, false));
+      if constexpr (P == 4) {
+        v = __int_as_float(
+            __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(acc[2][i]), 0x118, 0xF, 0x4, false));
+        v = __int_as_float(
+            __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(acc[3][i]), 0x11C, 0xF, 0x8, false));
+      }
+      x[i] = v;
+    }
     wave_sync();
-    const float4 fb01 = *reinterpret_cast<const float4*>(&s.fb[4 * g]);
-    const float4 fb23 = *reinterpret_cast<const float4*>(&s.fb[4 * g + 2]);
-    wave_sync();  // s.fb is rewritten by the next row tile
-    const float x0 = fmaf(ldexpf(acc[0], eq), fb01.x, fb01.y), x1 = fmaf(ldexpf(acc[1], eq), fb01.z, fb01.w);
-    const float x2 = fmaf(ldexpf(acc[2], eq), fb23.x, fb23.y), x3 = fmaf(ldexpf(acc[3], eq), fb23.z, fb23.w);
+    // rows 16 qp + 4 g + i of the set, head hc: logits in log2 units
+    const float4 fb01 = *reinterpret_cast<const float4*>(&s.fb[16 * qp + 4 * g]);
+    const float4 fb23 = *reinterpret_cast<const float4*>(&s.fb[16 * qp + 4 * g + 2]);
+    wave_sync();  // s.fb is rewritten by the next set
+    const float x0 = fmaf(ldexpf(x[0], eq_p), fb01.x, fb01.y), x1 = fmaf(ldexpf(x[1], eq_p), fb01.z, fb01.w);
+    const float x2 = fmaf(ldexpf(x[2], eq_p), fb23.x, fb23.y), x3 = fmaf(ldexpf(x[3], eq_p), fb23.z, fb23.w);
     // sibling LSE: max + log2(1 + 2^-|a - b|).  Child 0 of a candidate always
     // exists, so a stored score is finite; a missing child 1 (-inf) adds 0.
-    float u[2];
-    u[0] = fmaxf(x0, x1) + __log2f(1.f + exp2_nonpos(-fabsf(x0 - x1)));
-    u[1] = fmaxf(x2, x3) + __log2f(1.f + exp2_nonpos(-fabsf(x2 - x3)));
-    u[0] = lane_group_sum<G>(u[0]);
-    u[1] = lane_group_sum<G>(u[1]);
-    const int c0 = 8 * rt + 2 * g;
-    if (col == 0) {
-      if (c0 < nA) s.score[c0] = u[0];
-      if (c0 + 1 < nA) s.score[c0 + 1] = u[1];
+    float u0 = fmaxf(x0, x1) + __log2f(1.f + exp2_nonpos(-fabsf(x0 - x1)));
+    float u1 = fmaxf(x2, x3) + __log2f(1.f + exp2_nonpos(-fabsf(x2 - x3)));
+    u0 = lane_group_sum<G>(u0);
+    u1 = lane_group_sum<G>(u1);
+    const int c0 = 8 * (rt0 + qp) + 2 * g;
+    if (hc == 0 && rt0 + qp < nt) {
+      if (c0 < nA) s.score[c0] = u0;
+      if (c0 + 1 < nA) s.score[c0 + 1] = u1;
     }
   }
 }
@@ -198,6 +226,9 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
   // and block j of level l starts at j C 2^(l-1) <= t iff j <= (t / C) >> (l-1)
   const int32_t M1 = (int32_t)level_rows(a.N, a.C, 1);
   const int64_t tstep = (int64_t)a.chunks * kRouteWgWaves;
+  // diagnostics only: queries, scored candidates, rows, scored levels, kept
+  // blocks of this wave, added to the counters once at the end
+  unsigned long long w_q = 0, w_cands = 0, w_rows_sum = 0, w_levels = 0, w_kept = 0;
   for (int64_t t = (int64_t)chunk * kRouteWgWaves + w; t < a.N; t += tstep) {
     // B operand: column col = query head col of the group (zero beyond G_Q),
     // scaled by 2^-eq into fp16 (exact for bf16 values)
@@ -220,6 +251,8 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const int eq = row_exponent(mx);
+    // the exponent of head col % max(G, 4), the head a packed lane carries
+    const int eq_p = __shfl(eq, col % (G < 4 ? 4 : G));
     halfx8 fq[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st)
@@ -230,7 +263,7 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
     if (lane == 0) s.cand[0] = 0;
     int32_t kept = (lane == 0) ? 0 : -1;
     int nI = 1;
-    int64_t w_rows = 0, w_cands = 0, w_levels = 0;  // diagnostics only
+    int64_t w_rows = 0;  // diagnostics only
     int64_t* rows_ptr = CNT ? &w_rows : nullptr;
     wave_sync();
     const int32_t tc = (int32_t)t / a.C;
@@ -250,11 +283,11 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
         const int32_t m_child = ((M1 - 1) >> (l - 2)) + 1;
         const int32_t tl = causal ? (tc >> (l - 2)) : 0x7fffffff;
         const int32_t lvl = (int32_t)a.geo.level_off[l - 1];
-        if (l - 1 >= a.stage_level)
-          score_level_mfma<D, G, SP>(s, nA, fq, eq, s_rows, s_exs, lvl - (int32_t)a.stage_off, m_child, tl, sl2,
+        if (l - 1 >= a.stage_level && l - 1 <= a.stage_top)
+          score_level_mfma<D, G, SP>(s, nA, fq, eq_p, s_rows, s_exs, lvl - (int32_t)a.stage_off, m_child, tl, sl2,
                                      rows_ptr);
         else
-          score_level_mfma<D, G, D>(s, nA, fq, eq, hb, xb, lvl, m_child, tl, sl2, rows_ptr);
+          score_level_mfma<D, G, D>(s, nA, fq, eq_p, hb, xb, lvl, m_child, tl, sl2, rows_ptr);
         w_cands += nA;
         w_levels += 1;
         wave_sync();
@@ -281,13 +314,18 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
     if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
     else k2 = wave_sort_desc(k2);
     if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
-    if (CNT && lane == 0) {
-      atomicAdd(&a.counts[0], 1ull);
-      atomicAdd(&a.counts[1], (unsigned long long)w_cands);
-      atomicAdd(&a.counts[2], (unsigned long long)w_rows);
-      atomicAdd(&a.counts[3], (unsigned long long)w_levels);
-      atomicAdd(&a.counts[4], (unsigned long long)nI);
+    if (CNT) {
+      w_q += 1;
+      w_rows_sum += (unsigned long long)w_rows;
+      w_kept += (unsigned long long)nI;
     }
+  }
+  if (CNT && lane == 0) {
+    atomicAdd(&a.counts[0], w_q);
+    atomicAdd(&a.counts[1], w_cands);
+    atomicAdd(&a.counts[2], w_rows_sum);
+    atomicAdd(&a.counts[3], w_levels);
+    atomicAdd(&a.counts[4], w_kept);
   }
 }
 
@@ -300,8 +338,11 @@ static void route_stage_plan(const Problem& p, RouteArgs& a, size_t& lds) {
   const size_t pitch_bytes = (size_t)(p.D + 8) * 2 + 4;  // padded fp16 row + exponent
   const size_t budget = (size_t)144 * 1024;
   a.stage_level = p.geo.levels_cap + 1;
+  a.stage_top = p.geo.levels_cap;
   a.stage_rows = 0;
   a.stage_off = p.geo.rows;
+  // (staging only the finest level that fits instead was slower: the coarse
+  // levels are read by every query of the head)
   for (int32_t l = 1; l <= p.geo.levels_cap; ++l) {
     const int64_t rows = p.geo.rows - p.geo.level_off[l];
     if ((size_t)rows * pitch_bytes <= budget) {
@@ -324,7 +365,7 @@ hipError_t launch_route(const Problem& p, const void* q, const void* k, const fl
   const int64_t plane = (int64_t)p.B * p.Hkv * p.geo.rows * p.D;
   const _Float16* f16 = reinterpret_cast<const _Float16*>(pyr + plane);
   RouteArgs a{counts, q, k, pyr, f16, reinterpret_cast<const int32_t*>(f16 + plane), idx, score, p.B, p.N, p.Hq, p.Hkv, p.C, p.K, p.L, p.causal ? 1 : 0,
-              p.cap, p.scale, p.geo, 0, 0, 0, 1};
+              p.cap, p.scale, p.geo, 0, 0, 0, 0, 1};
   const int64_t blocks = (int64_t)p.B * p.Hkv * ((p.N + kRouteWaves - 1) / kRouteWaves);
   return dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
     using T = std::remove_pointer_t<decltype(tp)>;
