@@ -41,7 +41,8 @@ static BwdLayout bwd_layout(const Problem& p) {
   BwdLayout L{};
   L.M1 = level_rows(p.N, p.C, 1);
   L.Mb = cluster_bins(p.N, L.M1, kAttnBins);
-  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * p.D * 4) + (size_t)L.Mb * 16;
+  const size_t esz = p.dtype == 1 ? 2 : 4;  // partial dQ rows in the input dtype
+  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * p.D * esz) + (size_t)L.Mb * 16;
   const int64_t BH = (int64_t)p.B * p.Hkv;
   int64_t hmax = (int64_t)(kBwdBudget / per_head);
   if (hmax < 1) hmax = 1;
@@ -62,7 +63,7 @@ static BwdLayout bwd_layout(const Problem& p) {
   L.off_pairs = off;
   off = b256(off + 4 * (size_t)L.slots);
   L.off_dq = off;
-  off = b256(off + 4 * (size_t)L.slots * p.G * p.D);
+  off = b256(off + esz * (size_t)L.slots * p.G * p.D);
   L.off_hist = off;
   off = b256(off + cluster_scratch_bytes(L.heads, (int64_t)p.N * p.K, L.Mb));
   L.off_rowdot = off;
@@ -121,7 +122,7 @@ struct BwdArgs {
   const int32_t* offsets;
   const int32_t* chunk_off;
   const int32_t* pairs;
-  float* dq_part;  // [heads][N][K][G][D]
+  void* dq_part;  // [heads][N][K][G][D], input dtype
   float* dk_acc;   // [B][Hkv][N][D]
   float* dv_acc;
   int64_t ncl, M1, Mb, head0;
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
   __shared__ __align__(16) float s_ds[CP][16];
   __shared__ float s_lse[16], s_rd[16];
   __shared__ int32_t s_pr[16];
+  __shared__ int32_t s_cpr[kBwdChunk];  // the chunk's pair codes
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -187,6 +189,9 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
 #pragma unroll
     for (int e = 0; e < EPV; ++e) s_kt[(d + e) * TP + r] = ke[e];
   }
+  for (int i = threadIdx.x; i < kBwdChunk; i += blockDim.x) s_cpr[i] = p_begin + i < p_end ? a.pairs[p_begin + i] : -1;
+  __syncthreads();
+  const int n = (int)(p_end - p_begin);
 
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
@@ -202,29 +207,60 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
       dkt[di][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-  for (int64_t tile = p_begin; tile < p_end; tile += TQ) {
-    // stage the tile: column cc = query cc / G (pair tile + cc / G) x head cc % G
+  // a tile's staging work: 16 columns x D / EPV 16-byte pieces of q and dO
+  // (column cc = query cc / G of the tile x head cc % G), plus lse and D_t of
+  // the 16 columns; each thread fetches its share of the next tile into
+  // registers while the current tile is computed
+  constexpr int PIECES = 16 * (D / EPV);
+  constexpr int PPT = (PIECES + kBwdWaves * kWave - 1) / (kBwdWaves * kWave);  // pieces per thread
+  uint4 nq[PPT], ng[PPT];
+  float nlse = 0.f, nrd = 0.f;
+  int32_t npr = -1;
+  auto fetch = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int i = threadIdx.x + k * kBwdWaves * kWave;
+      nq[k] = uint4{0u, 0u, 0u, 0u};
+      ng[k] = uint4{0u, 0u, 0u, 0u};
+      if (i < PIECES) {
+        const int cc = i / (D / EPV), d = (i % (D / EPV)) * EPV;
+        const int jj = i0 + cc / G;
+        const int32_t pr = jj < n ? s_cpr[jj] : -1;
+        if (pr >= 0) {
+          const int64_t row = ((int64_t)b * a.Hq + h * G + cc % G) * a.N + (pr >> 5);
+          nq[k] = *reinterpret_cast<const uint4*>(qb + row * D + d);
+          ng[k] = *reinterpret_cast<const uint4*>(gb + row * D + d);
+        }
+      }
+    }
     if (threadIdx.x < 16) {
       const int cc = threadIdx.x;
-      const int32_t pr = tile + cc / G < p_end ? a.pairs[tile + cc / G] : -1;
-      s_pr[cc] = pr;
-      const int64_t row = ((int64_t)b * a.Hq + h * G + cc % G) * a.N + (pr >> 5);
-      s_lse[cc] = pr >= 0 ? a.lse[row] : 0.f;
-      s_rd[cc] = pr >= 0 ? a.rowdot[row] : 0.f;
+      const int jj = i0 + cc / G;
+      npr = jj < n ? s_cpr[jj] : -1;
+      const int64_t row = ((int64_t)b * a.Hq + h * G + cc % G) * a.N + (npr >= 0 ? (npr >> 5) : 0);
+      nlse = npr >= 0 ? a.lse[row] : 0.f;
+      nrd = npr >= 0 ? a.rowdot[row] : 0.f;
     }
-    for (int i = threadIdx.x; i < 16 * (D / EPV); i += blockDim.x) {
-      const int cc = i / (D / EPV), d = (i % (D / EPV)) * EPV;
-      const int32_t pr = tile + cc / G < p_end ? a.pairs[tile + cc / G] : -1;
-      uint4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
-      if (pr >= 0) {
-        const int64_t row = ((int64_t)b * a.Hq + h * G + cc % G) * a.N + (pr >> 5);
-        qv = *reinterpret_cast<const uint4*>(qb + row * D + d);
-        gv = *reinterpret_cast<const uint4*>(gb + row * D + d);
+  };
+  if (n > 0) fetch(0);
+  for (int i0 = 0; i0 < n; i0 += TQ) {
+    // stage the fetched tile
+    if (threadIdx.x < 16) {
+      s_pr[threadIdx.x] = npr;
+      s_lse[threadIdx.x] = nlse;
+      s_rd[threadIdx.x] = nrd;
+    }
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int i = threadIdx.x + k * kBwdWaves * kWave;
+      if (i < PIECES) {
+        const int cc = i / (D / EPV), d = (i % (D / EPV)) * EPV;
+        *reinterpret_cast<uint4*>(&s_q[cc][d]) = nq[k];
+        *reinterpret_cast<uint4*>(&s_do[cc][d]) = ng[k];
       }
-      *reinterpret_cast<uint4*>(&s_q[cc][d]) = qv;
-      *reinterpret_cast<uint4*>(&s_do[cc][d]) = gv;
     }
     __syncthreads();
+    if (i0 + TQ < n) fetch(i0 + TQ);  // the next tile's rows, in flight during this one
     // phase A: key blocks of this wave
     {
       Frag<T> fq[NS], fg[NS];
@@ -297,8 +333,13 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
       const int32_t pc = s_pr[col];
       if (pc >= 0) {
         const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (col % G);
-        *reinterpret_cast<float4*>(a.dq_part + rec * D + db * 16 + 4 * g) =
-            float4{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale, dqt[3] * a.scale};
+        T* dst = static_cast<T*>(a.dq_part) + rec * D + db * 16 + 4 * g;
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(dqt[0] * a.scale, dqt[1] * a.scale),
+                                                 pack_bf16x2(dqt[2] * a.scale, dqt[3] * a.scale)};
+        else
+          *reinterpret_cast<float4*>(dst) = float4{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale,
+                                                   dqt[3] * a.scale};
       }
     }
     __syncthreads();  // the next tile restages s_q, s_do, s_p, s_ds
@@ -326,7 +367,7 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
 // ---- dq = sum of the K partial rows of every (query, head) -----------------------
 struct BwdMergeArgs {
   const int32_t* idx;
-  const float* dq_part;
+  const void* dq_part;  // input dtype
   void* dq;
   int64_t head0, heads, M1;
   int32_t N, Hq, Hkv, K;
@@ -348,11 +389,23 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdMergeArgs a) {
     for (int s = 0; s < a.K; ++s) {
       const int32_t jl = sel[s];
       if (jl < 0 || jl >= a.M1) continue;
-      const float4 v = *reinterpret_cast<const float4*>(a.dq_part + (rec0 + s * G + hh) * D + d);
-      acc[0] += v.x;
-      acc[1] += v.y;
-      acc[2] += v.z;
-      acc[3] += v.w;
+      float v[4];
+      const T* src = static_cast<const T*>(a.dq_part) + (rec0 + s * G + hh) * D + d;
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(src);
+        v[0] = __uint_as_float(u.x << 16);
+        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(u.y << 16);
+        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(src);
+        v[0] = f.x;
+        v[1] = f.y;
+        v[2] = f.z;
+        v[3] = f.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += v[i];
     }
     T* out = static_cast<T*>(a.dq) + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D + d;
 #pragma unroll
@@ -387,7 +440,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
-  float* dq_part = reinterpret_cast<float*>(base + L.off_dq);
+  void* dq_part = base + L.off_dq;
   float* rowdot = reinterpret_cast<float*>(base + L.off_rowdot);
   float* dk_acc = reinterpret_cast<float*>(base + L.off_dk);
   float* dv_acc = reinterpret_cast<float*>(base + L.off_dv);
