@@ -613,8 +613,13 @@ def io_main(args) -> int:
         q, k = dev(data["q"]), dev(data["k"])
         del data
         out = {}
-        for algo, name in ((pisa.SELECT_TWO_STAGE, "two_stage"), (pisa.SELECT_FUSED, "one_stage")):
-            p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True, dtype="bf16", select_algo=algo)
+        # two-stage at both Q_tile values (queries sharing one read of a key
+        # fragment from LDS: one 16-column MFMA tile = 16/G_Q, two = 32/G_Q)
+        for algo, name, qt in ((pisa.SELECT_TWO_STAGE, "two_stage", 32 // G),
+                               (pisa.SELECT_TWO_STAGE, "two_stage_q16", 16 // G),
+                               (pisa.SELECT_FUSED, "one_stage", 0)):
+            p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True, dtype="bf16", select_algo=algo,
+                             q_tile=qt)
             pyr = pisa.alloc_pyramid(p)
             ws = pisa.workspace(pisa.select_workspace_bytes(p))
             idx = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device="cuda")
@@ -640,12 +645,19 @@ def io_main(args) -> int:
             log(f"G_Q={G} {name}: {out[name]['ms']:.3f} ms {out[name]['kernels']}")
             del pyr, ws, idx, score
         same = float((out["two_stage"]["idx"] == out["one_stage"]["idx"]).all(-1).mean())
+        same_qt = bool(np.array_equal(out["two_stage"]["idx"], out["two_stage_q16"]["idx"]))
         d, C, qt, chunk = w.D, w.C, 4, 256
         rows.append({
             "G_Q": G, "Hkv": hkv,
             "two_stage_ms": round(out["two_stage"]["ms"], 4), "one_stage_ms": round(out["one_stage"]["ms"], 4),
             "two_stage_kernels_ms": out["two_stage"]["kernels"], "one_stage_kernels_ms": out["one_stage"]["kernels"],
             "same_selection_rate": round(same, 5),
+            "q_tile_sweep": {
+                "q_tile": [16 // G, 32 // G],
+                "leaf_score_ms": [out["two_stage_q16"]["kernels"].get("leaf_score"),
+                                  out["two_stage"]["kernels"].get("leaf_score")],
+                "lds_key_bytes_per_pair": [2 * C * d * 2 * G // 16, 2 * C * d * 2 * G // 32],
+                "identical_selection": same_qt},
             "leaf_bytes_per_pair": {"one_stage": C * d * 2, "two_stage_pages": (G + C // qt) * d * 2,
                                     "two_stage_here": round(G * d * 2 + 2 * C * d * 2 / chunk, 1)},
         })

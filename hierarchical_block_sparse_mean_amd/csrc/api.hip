@@ -75,8 +75,12 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
   if (!supported_group(G)) return fail(PISA_ERR_UNSUPPORTED, "G_Q = Hq/Hkv must be 1, 2, 4, 8 or 16 (got %d)", G);
   if (p->K > 32) return fail(PISA_ERR_UNSUPPORTED, "K must be <= 32 (got %d)", p->K);
   if (p->C > 128) return fail(PISA_ERR_UNSUPPORTED, "C must be <= 128 (got %d)", p->C);
-  if (p->q_tile != 0 && p->q_tile != 16 / G)
-    return fail(PISA_ERR_UNSUPPORTED, "q_tile must be 0 or 16/G_Q = %d (got %d)", 16 / G, p->q_tile);
+  // stage-2 queries per key-fragment read: one 16-column tile (16/G_Q
+  // queries) or two (32/G_Q: 16-bit inputs, C = 32, 64 or 128)
+  const bool two_tiles = p->dtype == PISA_BF16 && (p->C == 32 || p->C == 64 || p->C == 128);
+  if (p->q_tile != 0 && p->q_tile != 16 / G && !(two_tiles && p->q_tile == 32 / G))
+    return fail(PISA_ERR_UNSUPPORTED, "q_tile must be 0, 16/G_Q = %d%s (got %d)", 16 / G,
+                two_tiles ? " or 32/G_Q" : "", p->q_tile);
   const int64_t cap = p->cap ? p->cap : p->N;
   if ((int64_t)p->B * p->Hkv * p->N * p->K > INT32_MAX || (int64_t)p->N * p->K > INT32_MAX)
     return fail(PISA_ERR_UNSUPPORTED, "B*Hkv*N*K exceeds 2^31-1");
@@ -94,7 +98,7 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
   out->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
   out->cap = cap;
   out->L = pisa::num_levels(p->N, p->C);
-  out->q_tile = 16 / G;
+  out->q_tile = p->q_tile ? p->q_tile : (two_tiles ? 32 / G : 16 / G);
   out->geo = make_geom(cap, p->C);
   return ok();
 }

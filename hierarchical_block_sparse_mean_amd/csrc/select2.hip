@@ -394,16 +394,17 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
       PISA_LAUNCH("leaf_score", stream, kern, dim3((unsigned)max_chunks), dim3(kS2Waves * kWave), lds, a);
       return hipSuccess;
     };
-    // two tiles per step for 16-bit inputs (fp32 query rows take twice the
-    // registers)
+    // tiles per step: q_tile / (16 / G_Q), two only for 16-bit inputs with
+    // whole 16-key blocks per leaf (fp32 query rows take twice the registers)
+    const bool tt2 = sizeof(T) == 2 && p.q_tile * G == 32;
     constexpr int TT2 = sizeof(T) == 2 ? 2 : 1;
     hipError_t e;
     if (p.C == 32)
-      e = run(leaf_score_kernel<T, D, G, 4, 2, TT2>);
+      e = tt2 ? run(leaf_score_kernel<T, D, G, 4, 2, TT2>) : run(leaf_score_kernel<T, D, G, 4, 2, 1>);
     else if (p.C == 64)
-      e = run(leaf_score_kernel<T, D, G, 8, 4, TT2>);
+      e = tt2 ? run(leaf_score_kernel<T, D, G, 8, 4, TT2>) : run(leaf_score_kernel<T, D, G, 8, 4, 1>);
     else if (p.C == 128)
-      e = run(leaf_score_kernel<T, D, G, 16, 8, TT2>);
+      e = tt2 ? run(leaf_score_kernel<T, D, G, 16, 8, TT2>) : run(leaf_score_kernel<T, D, G, 16, 8, 1>);
     else if (p.C <= 32)
       e = run(leaf_score_kernel<T, D, G, 4, 0, 1>);
     else if (p.C <= 64)

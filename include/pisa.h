@@ -85,8 +85,13 @@ typedef struct {
   int32_t causal;           /* 0 or 1                                          */
   int32_t dtype;            /* pisa_dtype of q, k, v, o                         */
   float scale;              /* logit scale; 0 => 1/sqrt(D)                      */
-  int32_t q_tile;           /* stage-2 queries per MFMA tile; 0 => 16/G_Q.
-                               Only changes the schedule, never the result.    */
+  int32_t q_tile;           /* stage-2 queries that share one read of a key
+                               fragment: 16/G_Q (one 16-column MFMA tile) or
+                               32/G_Q (two tiles; bf16 with C = 32, 64 or 128);
+                               0 => 32/G_Q where allowed, else 16/G_Q.  Only
+                               changes the schedule, never the result
+                               ([KER] Q_tile).  Other values:
+                               PISA_ERR_UNSUPPORTED.                            */
   int32_t cap;              /* token capacity of k/v rows and of the pyramid;
                                0 => N.  Must be >= N.                           */
   int32_t select_algo;      /* pisa_select_algo                                 */

@@ -72,6 +72,8 @@ FAKE = 4096  # a non-NULL address; validation must reject before using it
     (dict(N=1 << 26, K=1), pisa.PISA_ERR_UNSUPPORTED),
     (dict(cap=100), pisa.PISA_ERR_INVALID_ARG),
     (dict(q_tile=3), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(q_tile=8), pisa.PISA_ERR_UNSUPPORTED),  # two tiles per read: bf16 only
+    (dict(q_tile=8, dtype="bf16", C=48), pisa.PISA_ERR_UNSUPPORTED),  # and whole 16-key blocks per leaf
     (dict(select_algo=7), pisa.PISA_ERR_INVALID_ARG),
     (dict(attn_algo=-1), pisa.PISA_ERR_INVALID_ARG),
     (dict(scale=-1.0), pisa.PISA_ERR_INVALID_ARG),
@@ -83,6 +85,13 @@ def test_invalid_problem_rejected(lib, kw, status):
     assert lib.pisa_last_error()
     assert lib.pisa_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == status
     assert lib.pisa_pyramid_bytes(ctypes.byref(p)) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(q_tile=4), dict(q_tile=8, dtype="bf16"), dict(q_tile=0, dtype="bf16"),
+                                dict(q_tile=2, Hq=8, Hkv=1, dtype="bf16", C=128)])
+def test_q_tile_schedules_accepted(lib, kw):
+    p = _p(**kw).c()
+    assert lib.pisa_select_workspace_bytes(ctypes.byref(p)) > 0, lib.pisa_last_error()
 
 
 def test_null_pointers_and_small_workspace(lib):

@@ -107,6 +107,28 @@ def test_select(name, algo):
     log(f"  exempt fraction {ex:.4f}, exact-match rate {rate:.4f}")
 
 
+@pytest.mark.parametrize("name", ["bf16_g4_n4133", "bf16_g1_b2", "bf16_g2_d64", "bf16_g8", "bf16_g16_c32",
+                                  "bf16_c128_k32"])
+def test_select_q_tile_schedules_identical(name):
+    """Stage 2 with one 16-column tile per key-fragment read (q_tile = 16/G_Q)
+    and with two (32/G_Q) computes every column identically: the same indices
+    and bit-identical scores."""
+    c = case_data(name)
+    w = c["w"]
+    G = w.Hq // w.Hkv
+    log(f"[test_select_q_tile {name}]")
+    out = []
+    for qt in (16 // G, 32 // G):
+        p = _problem(w)
+        p.q_tile = qt
+        pyr = pisa.build_pyramid(p, c["dev"]["k"])
+        idx, score = pisa.select(p, c["dev"]["q"], c["dev"]["k"], pyr)
+        torch.cuda.synchronize()
+        out.append((idx.cpu().numpy(), score.cpu().numpy()))
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1].view(np.uint32), out[1][1].view(np.uint32))
+
+
 @pytest.mark.parametrize("algo", [pisa.ATTN_LEAF_MAJOR, pisa.ATTN_QUERY_MAJOR], ids=["leaf_major", "query_major"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_attention(name, algo):
