@@ -224,6 +224,20 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
   __threadfence_block();
   __syncthreads();
 
+  // top K of the keys in lanes [0, 2K) into lanes [0, K) (half sorts for K = 16
+  // or 32, unordered; a full wave sort otherwise), and a descending sort of
+  // lanes [0, K)
+  auto topk_keys = [&](uint64_t key) -> uint64_t {
+    if (K == 16) return top_half<16>(key);
+    if (K == 32) return top_half<32>(key);
+    return wave_sort_desc(key);
+  };
+  auto sort_k = [&](uint64_t key) -> uint64_t {
+    if (K == 16) return group_sort_desc<16>(key);
+    if (K == 32) return group_sort_desc<32>(key);
+    return wave_sort_desc(key);
+  };
+
   // ---- 2. descent, levels L1 .. 2 ----------------------------------------
   // wave 0: drop candidates beyond the level's rows (every block starts at or
   // before t = n), compacting the list; returns the new count
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
     __syncthreads();
     if (w == 0) {
       uint64_t key = (lane < nA) ? score_key(s_score[lane], s_cand[lane]) : 0ull;
-      key = wave_sort_desc(key);
+      key = topk_keys(key);  // nA > K here: lanes [0, K) all hold kept blocks
       int nI = nA < K ? nA : K;
       int32_t kept = (lane < nI) ? key_index(key) : -1;
       int ll = l, na = nI;
@@ -381,12 +395,14 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
   __syncthreads();
   if (w == 0) {
     uint64_t key = (lane < nA) ? score_key(s_score[lane], s_cand[lane]) : 0ull;
-    key = wave_sort_desc(key);
+    key = topk_keys(key);
     const int nI = nA < K ? nA : K;
-    const int32_t kept = (lane < nI) ? key_index(key) : -1;
-    const float kept_score = (lane < nI) ? key_score(key) : -INFINITY;
-    uint64_t k2 = (lane < nI) ? index_key(kept, kept_score) : 0ull;
-    k2 = wave_sort_desc(k2);
+    // the kept leaves are the nonzero keys of lanes [0, K) (nA may be < K)
+    const bool kv = lane < K && key != 0ull;
+    const int32_t kept = kv ? key_index(key) : -1;
+    const float kept_score = kv ? key_score(key) : -INFINITY;
+    uint64_t k2 = kv ? index_key(kept, kept_score) : 0ull;
+    k2 = sort_k(k2);
     const int32_t out_idx = (lane < nI) ? index_key_index(k2) : -1;
     const float out_score = (lane < nI) ? index_key_score(k2) : -INFINITY;
     if (lane < K) {
