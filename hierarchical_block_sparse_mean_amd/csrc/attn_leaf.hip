@@ -3,10 +3,11 @@
 // the o_t equation: softmax over the raw keys of the kept blocks, applied to
 // their raw values).
 //
-// The kept (query, leaf) pairs are grouped by leaf (the same histogram / scan
-// / scatter as the selector's clusters).  One workgroup holds a leaf's C keys
-// (row-major) and values (transposed) in LDS and streams the queries that
-// kept it, 16 MFMA columns = 16 / G_Q queries x G_Q heads at a time:
+// The kept (query, leaf) pairs are grouped by (query block, leaf) (the same
+// histogram / scan / scatter as the selector's clusters).  One workgroup
+// holds a leaf's C keys (row-major) and values (transposed) in LDS and
+// streams the queries of the block that kept it, 16 MFMA columns = 16 / G_Q
+// queries x G_Q heads at a time, the next tile's query rows in flight:
 //   S^T = K Q^T        (C x 16, v_mfma_f32_16x16x32_bf16, fp32 accumulate)
 //   P^T = exp(S^T - m) per column (the accumulator layout already is the
 //                      B-operand layout of the next product: no LDS trip)

@@ -8,18 +8,20 @@
 //   1. per tile of 8192 entries, an LDS histogram over the head's key blocks;
 //   2. per (head, bin), a running sum down the tiles gives the bin total and
 //      each tile's base within the bin; per head, an exclusive scan over the
-//      bins gives each bin's first pair; then one scan of the work-chunk
-//      counts of all clusters;
+//      bins gives each bin's first pair; then the work-chunk counts are
+//      scanned per head, over the head totals, and the head bases added back;
 //   3. per tile, an LDS cursor per bin scatters the pair code (t << 5) | slot.
 // A cluster is the set of entries of one (head, query block, key block): the
 // queries of a head are cut into blocks of 2^s consecutive positions (the
-// smallest s >= 12 whose bins still fit the LDS histogram), so that the work
-// on one block of queries is grouped together and the consumers' re-reads of
-// those queries' rows stay cache-resident.  Bins per head: Mb = blocks * M,
-// bin = (t >> s) * M + key block.  Heads with more key blocks than the LDS
-// histogram holds use one query block and a global-atomic fallback.  Either
-// way: counts[c], offsets[c] (first pair) and chunk_off[c] (first work chunk,
-// chunk_off[ncl] = total) for c = head * Mb + bin.
+// smallest s >= 12 whose bins stay within the caller's bin budget, itself at
+// most what the LDS histogram holds), so that the work on one block of
+// queries is grouped together and the consumers' re-reads of those queries'
+// rows stay cache-resident; a budget of M bins keeps one query block.  Bins
+// per head: Mb = blocks * M, bin = (t >> s) * M + key block.  Heads with more
+// key blocks than the LDS histogram holds use one query block and a
+// global-atomic fallback.  Either way: counts[c], offsets[c] (first pair) and
+// chunk_off[c] (first work chunk, chunk_off[ncl] = total) for
+// c = head * Mb + bin.
 #include "kernels.h"
 
 namespace pisa {

@@ -88,7 +88,7 @@ struct ClusterBufs {
   int32_t* hist;
 };
 // Bins per head of a clustering of N queries over M key blocks: query blocks
-// of 2^cluster_query_shift(N, M) positions times M (see cluster.hip).
+// of 2^cluster_query_shift(N, M, max_bins) positions times M (see cluster.hip).
 // max_bins: the clustering's bin budget per head (query blocks are added
 // while bins stay within it; M >= max_bins gives one query block).
 int32_t cluster_query_shift(int64_t N, int64_t M, int64_t max_bins);

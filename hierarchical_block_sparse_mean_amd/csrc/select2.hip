@@ -13,9 +13,10 @@
 // Design on gfx950: a cluster is a kept level-2 block (its two sibling leaves
 // are always candidates together), so one key tile of 2C keys serves both
 // leaves and each query row is read once per pair of leaves.  Tiles are 16
-// MFMA rows = 16 / G_Q queries x G_Q heads (v_mfma_f32_16x16x32_bf16; fp32
-// inputs use v_mfma_f32_16x16x4_f32).  The key tile sits in LDS with a
-// 16-byte row pad so that the 16 lanes of a fragment read hit distinct banks.
+// MFMA columns = 16 / G_Q queries x G_Q heads (v_mfma_f32_16x16x32_bf16; fp32
+// inputs use v_mfma_f32_16x16x4_f32); Q_tile = 16 / G_Q or, taking two tiles
+// per key-fragment read, 32 / G_Q.  The key tile sits in LDS with a 16-byte
+// row pad so that the 16 lanes of a fragment read hit distinct banks.
 #include "kernels.h"
 
 namespace pisa {
