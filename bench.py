@@ -163,7 +163,7 @@ def main() -> int:
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head with no "
-              "collective, see DESIGN.md", file=sys.stderr)
+              "collective (each rank would run these kernels on its own KV heads)", file=sys.stderr)
         return 2
     import numpy as np
     import torch
@@ -282,7 +282,7 @@ def main() -> int:
                                 f"{rc['child_rows']} child summary rows x d*4 B + G*d*elem (q) + K*4 per (t, h); "
                                 f"{rc['child_rows'] / max(1, rc['queries']):.1f} rows and "
                                 f"{rc['scored_levels'] / max(1, rc['queries']):.2f} scored levels per (t, h); "
-                                "rows are served from L2, so the fraction can exceed HBM peak")
+                                "coarse levels are read from LDS and finer rows from L2, so the fraction can exceed HBM peak")
     dominant = max(per_kernel, key=lambda n: per_kernel[n]["ms_per_step"])
     roofline = None
     if dominant in work:
@@ -301,6 +301,12 @@ def main() -> int:
                     "traffic": traffic_for(dominant, w.name, per_launch_bytes=None),
                     "avg_launch_ms": round(per_kernel[dominant]["avg_ms"], 4),
                     "work_per_launch": per_launch, "work_note": note}
+        if roofline["traffic"]:
+            # the measured HBM bytes per launch as a rate, next to the copy
+            # ceiling: how close the kernel's own data movement is to HBM
+            rate = roofline["traffic"] / avg_s / 1e9
+            roofline["traffic_GBps"] = round(rate, 1)
+            roofline["traffic_frac_of_measured_copy"] = round(rate / ceilings["copy_GBps"], 4)
     kernel_rooflines = {}
     for name, (bound, amount, unit, note) in work.items():
         if name not in per_kernel:
