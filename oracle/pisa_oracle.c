@@ -24,7 +24,7 @@
  *                          selection that scores every one of ceil(N/C)
  *                          block summaries per query
  *
- * Readings taken where the page is silent (each one is listed in the design doc):
+ * Readings taken where the page is silent:
  *   - 0-based block indices; children of block j are {2j, 2j+1} clipped to
  *     the level size (contiguous blocks, Concat order).  Leaf j holds tokens
  *     [jC, min(jC+C, N)).
