@@ -10,10 +10,11 @@
 //
 // Leaf-major, like the forward: the kept (query, leaf) pairs are clustered by
 // leaf; a workgroup holds the leaf's K, V and K^T in LDS and walks its query
-// tiles (16 columns = 16/G_Q queries x G_Q heads), all waves on one tile:
-//   phase A (waves split the 16-key blocks): S^T = K Q^T and dP^T = V dO^T on
-//     MFMA, p = exp(z - lse) from the forward's lse, dS = p (dP - D), both
-//     written to LDS;
+// tiles (16 columns = 16/G_Q queries x G_Q heads), all waves on one round of
+// tiles (two tiles for 16-bit inputs, one for fp32) between barriers:
+//   phase A (waves split the (16-key block, tile) items): S^T = K Q^T and
+//     dP^T = V dO^T on MFMA, p = exp(z - lse) from the forward's lse,
+//     dS = p (dP - D), both written to LDS;
 //   phase B (waves split the 16-dim blocks): dV^T += dO^T P and dK^T += Q^T dS
 //     (16x16x16 MFMA over the tile's columns, accumulated in registers across
 //     tiles), and dQ^T = K^T dS^T (16x16x32 MFMA over the keys) written as a
@@ -25,7 +26,11 @@
 
 namespace pisa {
 
-constexpr int kBwdWaves = 4;
+// waves per workgroup: 8 when a leaf tile fills most of the LDS (C > 64) and
+// d has a 16-dim block per wave, so that one resident workgroup still keeps
+// 8 waves in flight; 4 otherwise
+template <int D, int NKB>
+constexpr int bwd_waves() { return NKB >= 8 && D >= 128 ? 8 : 4; }
 constexpr int kBwdChunk = 256;                   // (query, slot) pairs per workgroup
 constexpr size_t kBwdBudget = (size_t)8 << 30;  // partial dQ rows per head chunk
 
@@ -105,6 +110,12 @@ __device__ __forceinline__ floatx4 mma16(const float* a4, const float* b4, float
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, ua), __builtin_bit_cast(shortx4, ub),
                                                   acc, 0, 0, 0);
 }
+// B given as four bf16 values (raw bits, 8 bytes)
+__device__ __forceinline__ floatx4 mma16_braw(const float* a4, uint2 b4, floatx4 acc) {
+  const uint2 ua = {pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3])};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, ua), __builtin_bit_cast(shortx4, b4),
+                                                  acc, 0, 0, 0);
+}
 __device__ __forceinline__ floatx4 mma16(const float* a4, const float* b4, floatx4 acc, float) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], b4[i], acc, 0, 0, 0);
@@ -133,7 +144,8 @@ struct BwdArgs {
 };
 
 template <typename T, int D, int G, int NKB>
-__global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void attn_bwd_kernel(BwdArgs a) {
+  constexpr int NW = bwd_waves<D, NKB>();
   constexpr int NS = D / 32;
   constexpr int TQ = 16 / G;
   constexpr int CP = NKB * 16;
@@ -141,18 +153,27 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
   constexpr int KP = D + EPV;               // row pitch of K, V, q, dO tiles
   constexpr int TP = CP + EPV;              // row pitch of K^T
   constexpr int NDB = D / 16;
-  constexpr int DBW = NDB / kBwdWaves;  // dim blocks per wave
+  constexpr int DBW = NDB / NW;  // dim blocks per wave
+  static_assert(DBW >= 1 && NDB % NW == 0, "every wave owns whole 16-dim blocks");
   constexpr float kLog2e = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
   T* s_v = s_k + CP * KP;                    // [CP][KP]
   T* s_kt = s_v + CP * KP;                   // [D][TP]
-  __shared__ __align__(16) T s_q[16][KP];    // the tile's query rows, one per column
-  __shared__ __align__(16) T s_do[16][KP];   // and their output gradients
-  __shared__ __align__(16) float s_p[CP][16];
-  __shared__ __align__(16) float s_ds[CP][16];
-  __shared__ float s_lse[16], s_rd[16];
-  __shared__ int32_t s_pr[16];
+  // RT tiles of 16 columns per round of barriers: two for 16-bit inputs,
+  // whose p and dS are staged in bf16 (the rounding the MFMA operands apply
+  // anyway), one for fp32 inputs (fp32 staging)
+  constexpr bool B16 = sizeof(T) == 2;
+  constexpr int RT = B16 ? 2 : 1;
+  constexpr int NC = 16 * RT;  // columns per round
+  constexpr int PPITCH = NC + 4;  // p / dS row pitch (elements): conflict-free 8/16-byte reads
+  using PT = std::conditional_t<B16, uint16_t, float>;
+  __shared__ __align__(16) T s_q[NC][KP];    // the round's query rows, one per column
+  __shared__ __align__(16) T s_do[NC][KP];   // and their output gradients
+  __shared__ __align__(16) PT s_p[CP][PPITCH];
+  __shared__ __align__(16) PT s_ds[CP][PPITCH];
+  __shared__ float s_lse[NC], s_rd[NC];
+  __shared__ int32_t s_pr[NC];
   __shared__ int32_t s_cpr[kBwdChunk];  // the chunk's pair codes
 
   const int64_t chunk = blockIdx.x;
@@ -207,19 +228,19 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
       dkt[di][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // a tile's staging work: 16 columns x D / EPV 16-byte pieces of q and dO
-  // (column cc = query cc / G of the tile x head cc % G), plus lse and D_t of
-  // the 16 columns; each thread fetches its share of the next tile into
-  // registers while the current tile is computed
-  constexpr int PIECES = 16 * (D / EPV);
-  constexpr int PPT = (PIECES + kBwdWaves * kWave - 1) / (kBwdWaves * kWave);  // pieces per thread
+  // a round's staging work: NC columns x D / EPV 16-byte pieces of q and dO
+  // (column cc = query cc / G of the round x head cc % G), plus lse and D_t of
+  // the columns; each thread fetches its share of the next round into
+  // registers while the current round is computed
+  constexpr int PIECES = NC * (D / EPV);
+  constexpr int PPT = (PIECES + NW * kWave - 1) / (NW * kWave);  // pieces per thread
   uint4 nq[PPT], ng[PPT];
   float nlse = 0.f, nrd = 0.f;
   int32_t npr = -1;
   auto fetch = [&](int i0) {
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int i = threadIdx.x + k * kBwdWaves * kWave;
+      const int i = threadIdx.x + k * NW * kWave;
       nq[k] = uint4{0u, 0u, 0u, 0u};
       ng[k] = uint4{0u, 0u, 0u, 0u};
       if (i < PIECES) {
@@ -233,7 +254,7 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
         }
       }
     }
-    if (threadIdx.x < 16) {
+    if (threadIdx.x < NC) {
       const int cc = threadIdx.x;
       const int jj = i0 + cc / G;
       npr = jj < n ? s_cpr[jj] : -1;
@@ -242,17 +263,25 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
       nrd = npr >= 0 ? a.rowdot[row] : 0.f;
     }
   };
+  auto to_pt = [](float x) -> PT {
+    if constexpr (B16) return f32_to_bf16(x);
+    else return x;
+  };
+  auto from_pt = [](PT x) -> float {
+    if constexpr (B16) return bf16_to_f32(x);
+    else return x;
+  };
   if (n > 0) fetch(0);
-  for (int i0 = 0; i0 < n; i0 += TQ) {
-    // stage the fetched tile
-    if (threadIdx.x < 16) {
+  for (int i0 = 0; i0 < n; i0 += TQ * RT) {
+    // stage the fetched round
+    if (threadIdx.x < NC) {
       s_pr[threadIdx.x] = npr;
       s_lse[threadIdx.x] = nlse;
       s_rd[threadIdx.x] = nrd;
     }
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int i = threadIdx.x + k * kBwdWaves * kWave;
+      const int i = threadIdx.x + k * NW * kWave;
       if (i < PIECES) {
         const int cc = i / (D / EPV), d = (i % (D / EPV)) * EPV;
         *reinterpret_cast<uint4*>(&s_q[cc][d]) = nq[k];
@@ -260,89 +289,105 @@ __global__ __launch_bounds__(kBwdWaves* kWave) PISA_MFMA_REGS void attn_bwd_kern
       }
     }
     __syncthreads();
-    if (i0 + TQ < n) fetch(i0 + TQ);  // the next tile's rows, in flight during this one
-    // phase A: key blocks of this wave
-    {
+    if (i0 + TQ * RT < n) fetch(i0 + TQ * RT);  // the next round's rows, in flight during this one
+    // phase A: (key block, tile) items of this wave
+    for (int item = w; item < NKB * RT; item += NW) {
+      const int kb = item % NKB, tt = item / NKB;
+      const int cc = tt * 16 + col;
       Frag<T> fq[NS], fg[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        fq[s].load(&s_q[col][g * (D / 4) + 8 * s]);
-        fg[s].load(&s_do[col][g * (D / 4) + 8 * s]);
+        fq[s].load(&s_q[cc][g * (D / 4) + 8 * s]);
+        fg[s].load(&s_do[cc][g * (D / 4) + 8 * s]);
       }
-      const int32_t prc = s_pr[col];
+      const int32_t prc = s_pr[cc];
       int lim = 0;
       if (prc >= 0) {
         const int64_t t = prc >> 5;
         lim = a.causal ? (int)((t - key0 + 1) < nkeys ? (t - key0 + 1) : nkeys) : nkeys;
       }
-      const float lse2 = s_lse[col] * kLog2e, rd = s_rd[col];
-      for (int kb = w; kb < NKB; kb += kBwdWaves) {
-        floatx4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+      const float lse2 = s_lse[cc] * kLog2e, rd = s_rd[cc];
+      floatx4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          Frag<T> fk, fv;
-          fk.load(s_k + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
-          fv.load(s_v + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
-          st = mma(fk, fq[s], st);
-          dpt = mma(fv, fg[s], dpt);
-        }
-        // lane (g, col): keys kb*16 + 4g + i of column col
+      for (int s = 0; s < NS; ++s) {
+        Frag<T> fk, fv;
+        fk.load(s_k + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+        fv.load(s_v + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+        st = mma(fk, fq[s], st);
+        dpt = mma(fv, fg[s], dpt);
+      }
+      // lane (g, col): keys kb*16 + 4g + i of column cc
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb * 16 + 4 * g + i;
-          const float pv = key < lim ? exp2_nonpos(fminf(fmaf(st[i], sl2, -lse2), 0.f)) : 0.f;
-          s_p[key][col] = pv;
-          s_ds[key][col] = pv * (dpt[i] - rd);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb * 16 + 4 * g + i;
+        const float pv = key < lim ? exp2_nonpos(fminf(fmaf(st[i], sl2, -lse2), 0.f)) : 0.f;
+        s_p[key][cc] = to_pt(pv);
+        s_ds[key][cc] = to_pt(pv * (dpt[i] - rd));
       }
     }
     __syncthreads();
-    // phase B: dim blocks of this wave
+    // phase B: dim blocks of this wave, over the round's tiles
 #pragma unroll
     for (int di = 0; di < DBW; ++di) {
       const int db = w * DBW + di;
       const int dim = db * 16 + col;  // A row of this lane
-      float ag[4], aq[4];
+      float ag[RT][4], aq[RT][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ag[e] = load1<T>(&s_do[4 * g + e][dim]);
-        aq[e] = load1<T>(&s_q[4 * g + e][dim]);
-      }
+      for (int tt = 0; tt < RT; ++tt)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float4 pp = *reinterpret_cast<const float4*>(&s_p[kb * 16 + col][4 * g]);
-        const float4 dd = *reinterpret_cast<const float4*>(&s_ds[kb * 16 + col][4 * g]);
-        const float bp[4] = {pp.x, pp.y, pp.z, pp.w};
-        const float bd[4] = {dd.x, dd.y, dd.z, dd.w};
-        dvt[di][kb] = mma16(ag, bp, dvt[di][kb], T{});
-        dkt[di][kb] = mma16(aq, bd, dkt[di][kb], T{});
-      }
-      // dQ^T for these 16 dims: K^T (dims x keys) times dS^T (keys x columns)
-      floatx4 dqt = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 4; ++e) {
+          ag[tt][e] = load1<T>(&s_do[tt * 16 + 4 * g + e][dim]);
+          aq[tt][e] = load1<T>(&s_q[tt * 16 + 4 * g + e][dim]);
+        }
 #pragma unroll
-      for (int ks = 0; ks < CP / 32; ++ks) {
-        Frag<T> fa, fb;
-        fa.load(s_kt + dim * TP + ks * 32 + g * 8);
-        float x[8];
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = s_ds[ks * 32 + g * 8 + e][col];
-        fb.set(x);
-        dqt = mma(fa, fb, dqt);
-      }
-      // lane (g, col): dims db*16 + 4g + i of column col
-      const int32_t pc = s_pr[col];
-      if (pc >= 0) {
-        const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (col % G);
-        T* dst = static_cast<T*>(a.dq_part) + rec * D + db * 16 + 4 * g;
-        if constexpr (sizeof(T) == 2)
-          *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(dqt[0] * a.scale, dqt[1] * a.scale),
-                                                 pack_bf16x2(dqt[2] * a.scale, dqt[3] * a.scale)};
-        else
-          *reinterpret_cast<float4*>(dst) = float4{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale,
-                                                   dqt[3] * a.scale};
+        for (int tt = 0; tt < RT; ++tt) {
+          if constexpr (B16) {
+            const uint2 pp = *reinterpret_cast<const uint2*>(&s_p[kb * 16 + col][tt * 16 + 4 * g]);
+            const uint2 dd = *reinterpret_cast<const uint2*>(&s_ds[kb * 16 + col][tt * 16 + 4 * g]);
+            dvt[di][kb] = mma16_braw(ag[tt], pp, dvt[di][kb]);
+            dkt[di][kb] = mma16_braw(aq[tt], dd, dkt[di][kb]);
+          } else {
+            const float4 pp = *reinterpret_cast<const float4*>(&s_p[kb * 16 + col][tt * 16 + 4 * g]);
+            const float4 dd = *reinterpret_cast<const float4*>(&s_ds[kb * 16 + col][tt * 16 + 4 * g]);
+            const float bp[4] = {pp.x, pp.y, pp.z, pp.w};
+            const float bd[4] = {dd.x, dd.y, dd.z, dd.w};
+            dvt[di][kb] = mma16(ag[tt], bp, dvt[di][kb], T{});
+            dkt[di][kb] = mma16(aq[tt], bd, dkt[di][kb], T{});
+          }
+        }
+      // dQ^T for these 16 dims and each tile: K^T (dims x keys) times dS^T
+      // (keys x columns)
+#pragma unroll
+      for (int tt = 0; tt < RT; ++tt) {
+        const int cc = tt * 16 + col;
+        floatx4 dqt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < CP / 32; ++ks) {
+          Frag<T> fa, fb;
+          fa.load(s_kt + dim * TP + ks * 32 + g * 8);
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = from_pt(s_ds[ks * 32 + g * 8 + e][cc]);
+          fb.set(x);
+          dqt = mma(fa, fb, dqt);
+        }
+        // lane (g, col): dims db*16 + 4g + i of column cc
+        const int32_t pc = s_pr[cc];
+        if (pc >= 0) {
+          const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (col % G);
+          T* dst = static_cast<T*>(a.dq_part) + rec * D + db * 16 + 4 * g;
+          if constexpr (B16)
+            *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(dqt[0] * a.scale, dqt[1] * a.scale),
+                                                   pack_bf16x2(dqt[2] * a.scale, dqt[3] * a.scale)};
+          else
+            *reinterpret_cast<float4*>(dst) = float4{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale,
+                                                     dqt[3] * a.scale};
+        }
       }
     }
-    __syncthreads();  // the next tile restages s_q, s_do, s_p, s_ds
+    __syncthreads();  // the next round restages s_q, s_do, s_p, s_ds
   }
   // this chunk's share of dK, dV: lane (g, col) holds dims db*16 + 4g + i of key kb*16 + col
 #pragma unroll
@@ -474,7 +519,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value;
       constexpr int G = decltype(gc)::value;
-      auto run = [&](auto kern, int nkb) -> hipError_t {
+      auto run = [&](auto kern, int nkb, int nw) -> hipError_t {
         const int cp = nkb * 16, epv = 16 / (int)sizeof(T);
         const size_t lds = (2 * (size_t)cp * (D + epv) + (size_t)D * (cp + epv)) * sizeof(T);
         if (lds > 65536) {
@@ -482,16 +527,16 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
           if (e != hipSuccess) return e;
         }
-        PISA_LAUNCH("attn_bwd", stream, kern, dim3((unsigned)max_chunks), dim3(kBwdWaves * kWave), lds, ba);
+        PISA_LAUNCH("attn_bwd", stream, kern, dim3((unsigned)max_chunks), dim3(nw * kWave), lds, ba);
         return hipGetLastError();
       };
       hipError_t e;
       if (p.C <= 32)
-        e = run(attn_bwd_kernel<T, D, G, 2>, 2);
+        e = run(attn_bwd_kernel<T, D, G, 2>, 2, bwd_waves<D, 2>());
       else if (p.C <= 64)
-        e = run(attn_bwd_kernel<T, D, G, 4>, 4);
+        e = run(attn_bwd_kernel<T, D, G, 4>, 4, bwd_waves<D, 4>());
       else
-        e = run(attn_bwd_kernel<T, D, G, 8>, 8);
+        e = run(attn_bwd_kernel<T, D, G, 8>, 8, bwd_waves<D, 8>());
       if (e != hipSuccess) return e;
       const int64_t waves = heads * p.N;
       PISA_LAUNCH("bwd_merge", stream, (bwd_merge_kernel<T, D, G>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
