@@ -177,16 +177,43 @@ __device__ __forceinline__ float rows_sum(float x) {
   return a + b;
 }
 
-__device__ __forceinline__ int shfl_xor_fast(int x, int m) {
-  if (m == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  if (m == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  if (m == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
-  return __shfl_xor(x, m);
+// 32-bit x from lane (lane ^ m) for m = 1, 2, 4, 8 (a constant after
+// unrolling) by DPP within a row of 16 lanes: quad permutations for 1 and 2;
+// for 4, banks 0 and 2 of the row read lane + 4 (row_shl:4) and banks 1 and 3
+// lane - 4 (row_shr:4); for 8, a rotation of the row by 8.  No LDS traffic.
+__device__ __forceinline__ uint32_t xor_lane_dpp(uint32_t x, int m) {
+  const int v = (int)x;
+  if (m == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if (m == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if (m == 8) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  const int t = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0x5, false);           // row_shl:4, banks 0, 2
+  return (uint32_t)__builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false);        // row_shr:4, banks 1, 3
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64_fast(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)shfl_xor_fast((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)shfl_xor_fast((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
+
+// The 64-bit values of lane l and of lane l ^ m (m a power of two below 64,
+// a constant after unrolling) as (a, b): for m < 16, a is the lane's own
+// value; for m = 16, 32 the gfx950 permlane swaps exchange whole rows (or
+// halves) and the order of the two depends on the lane, which a
+// compare-exchange that keeps the larger or the smaller does not see.
+__device__ __forceinline__ void xor_pair_u64(uint64_t v, int m, uint64_t& a, uint64_t& b) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  if (m == 16 || m == 32) {
+    uint32_t l0, l1, h0, h1;
+    if (m == 16) {
+      const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+      const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+      l0 = rl[0], l1 = rl[1], h0 = rh[0], h1 = rh[1];
+    } else {
+      const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      l0 = rl[0], l1 = rl[1], h0 = rh[0], h1 = rh[1];
+    }
+    a = ((uint64_t)h0 << 32) | l0;
+    b = ((uint64_t)h1 << 32) | l1;
+  } else {
+    a = v;
+    b = ((uint64_t)xor_lane_dpp(hi, m) << 32) | xor_lane_dpp(lo, m);
+  }
 }
 
 // 2^x for x <= 0 (or -inf) on the hardware exp unit alone, without the
@@ -229,26 +256,11 @@ __device__ __forceinline__ int32_t index_key_index(uint64_t key) {
 }
 __device__ __forceinline__ float index_key_score(uint64_t key) { return float_from_order((uint32_t)key); }
 
-// Bitonic sort of one 64-bit key per lane, descending across the wave
-// (lane 0 ends with the largest key).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t other = shfl_xor_u64(key, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc = (lane & k) == 0;
-      const bool take_max = (lower == desc);
-      key = ((key > other) == take_max) ? key : other;
-    }
-  }
-  return key;
-}
-
 // Bitonic sort inside aligned groups of N lanes (N a power of two <= 64);
 // lanes [0, N) end in descending order (other groups alternate direction).
+// Each compare-exchange takes the pair (own, partner) from xor_pair_u64 and
+// keeps the larger where take_max holds, else the smaller: one 64-bit
+// compare, a mask operation and two selects.
 template <int N>
 __device__ __forceinline__ uint64_t group_sort_desc(uint64_t key) {
   const int lane = lane_id();
@@ -256,24 +268,29 @@ __device__ __forceinline__ uint64_t group_sort_desc(uint64_t key) {
   for (int k = 2; k <= N; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t other = shfl_xor_u64_fast(key, j);
+      uint64_t x, y;
+      xor_pair_u64(key, j, x, y);
       const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      // keep the own key where (key > other) agrees with take_max: one
-      // 64-bit compare, a mask operation and two selects
-      key = ((key > other) == take_max) ? key : other;
+      key = ((x > y) == take_max) ? x : y;
     }
   }
   return key;
 }
 
+// Bitonic sort of one 64-bit key per lane, descending across the wave
+// (lane 0 ends with the largest key).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) { return group_sort_desc<kWave>(key); }
+
 // The K largest keys of lanes [0, 2K) land in lanes [0, K), in no particular
 // order: sort both K-lane halves (opposite directions) and keep the larger of
-// each pair (lane, lane + K).  K a power of two <= 32.
+// each pair (lane, lane + K) there (lanes [K, 2K) keep the smaller).  K a
+// power of two <= 32.
 template <int K>
 __device__ __forceinline__ uint64_t top_half(uint64_t key) {
   key = group_sort_desc<K>(key);
-  const uint64_t other = shfl_xor_u64(key, K);
-  return ((lane_id() & K) == 0 && other > key) ? other : key;
+  uint64_t x, y;
+  xor_pair_u64(key, K, x, y);
+  return (((lane_id() & K) == 0) == (x > y)) ? x : y;
 }
 
 // ---- pyramid geometry (capacity layout, see pisa.h) -----------------------
