@@ -15,33 +15,45 @@
 // and writes a partial (m, l, O) per (query, slot, head).  A merge pass per
 // (query, KV head) combines the K partials into o and lse.  Partial O is
 // stored in the input dtype (bf16 rounding is far inside the bf16 tolerance).
+// Where a query kept both leaves of a level-2 block (2j and 2j + 1, adjacent
+// in its ascending row) and 2C keys fit one tile (C <= 64), the pair goes to
+// a cluster of that block instead: a second launch attends the 2C keys in one
+// tile, so the query's rows are read once and one partial (under the slot of
+// the even leaf) is written for both; the odd leaf's slot gets m = -inf,
+// which the merge skips without reading its row.
 // Work is done in chunks of KV heads so the partial buffers stay bounded and
 // one chunk's queries stay cache-resident.
 #include "kernels.h"
 
 namespace pisa {
 
-// waves per workgroup: 8 when a leaf tile fills most of the LDS (C > 64), so
-// that one resident workgroup still keeps 8 waves in flight; 4 otherwise
+// waves per workgroup: 12 for tiles of 8 key blocks (their K, V^T and the
+// waves' output staging leave room for one workgroup per CU, so it brings
+// the waves), 8 otherwise (two workgroups per CU)
 template <int NKB>
-constexpr int attn_waves() { return NKB >= 8 ? 8 : 4; }
+constexpr int attn_waves() { return NKB >= 8 ? 12 : 8; }
 constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
 constexpr size_t kAttnBudget = (size_t)8 << 30;  // partial buffers per head chunk
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks
+static bool attn_pairs(const Problem& p) { return p.C <= 64; }
+
 struct AttnLayout {
   int64_t heads;  // (b, h) heads per chunk
-  int64_t M1, Mb, ncl, slots;  // Mb: cluster bins per head
-  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_m, off_l, off_o, off_hist, total;
+  int64_t M1, Mk, Mb, ncl, slots, max_chunks;  // Mk: key blocks (leaves, then level-2 blocks); Mb: bins per head
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_map, off_pairs, off_m, off_l, off_o, off_hist, total;
 };
 
 static AttnLayout attn_layout(const Problem& p) {
   AttnLayout L{};
   const size_t osz = p.dtype == 1 ? 2 : 4;
   L.M1 = level_rows(p.N, p.C, 1);
-  L.Mb = cluster_bins(p.N, L.M1, kAttnBins);
-  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * (8 + p.D * osz)) + (size_t)L.Mb * 16;
+  L.Mk = L.M1 + (attn_pairs(p) ? (L.M1 + 1) / 2 : 0);
+  L.Mb = cluster_bins(p.N, L.Mk, kAttnBins);
+  const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * (8 + p.D * osz)) + (size_t)L.Mb * 20 +
+                          (size_t)p.N * p.K / kAttnChunk * 4;
   const int64_t BH = (int64_t)p.B * p.Hkv;
   int64_t hmax = (int64_t)(kAttnBudget / per_head);
   if (hmax < 1) hmax = 1;
@@ -50,6 +62,7 @@ static AttnLayout attn_layout(const Problem& p) {
   L.heads = (BH + nchunks - 1) / nchunks;
   L.ncl = L.heads * L.Mb;
   L.slots = L.heads * (int64_t)p.N * p.K;
+  L.max_chunks = (L.slots + kAttnChunk - 1) / kAttnChunk + L.ncl;
   size_t off = 0;
   L.off_counts = off;
   off = a256(off + 4 * (size_t)L.ncl);
@@ -59,6 +72,8 @@ static AttnLayout attn_layout(const Problem& p) {
   off = a256(off + 4 * (size_t)(L.ncl + 1));
   L.off_chunks = off;
   off = a256(off + 4 * (size_t)(L.ncl + 1));
+  L.off_map = off;
+  off = a256(off + 4 * (size_t)L.max_chunks);
   L.off_pairs = off;
   off = a256(off + 4 * (size_t)L.slots);
   L.off_m = off;
@@ -82,19 +97,22 @@ struct AttnLeafArgs {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
+  const int32_t* chunk_map;  // work chunk -> cluster
   const int32_t* pairs;
   float* pm;   // [heads][N][K][G]
   float* pl;
   void* po;    // [heads][N][K][G][D] (input dtype)
-  int64_t ncl, M1, Mb, head0;
+  int64_t ncl, M1, Mk, Mb, head0;
   int32_t N, Hq, Hkv, C, K;
   int32_t causal;
   int64_t cap;
   float scale;
 };
 
-// NKB: 16-key blocks covering the leaf (even, C <= 16 NKB).
-template <typename T, int D, int G, int NKB>
+// NKB: 16-key blocks covering the tile (even, Ct <= 16 NKB), Ct = C keys of
+// a leaf, or 2C of a level-2 block (PAIRED: the launch over the level-2
+// block clusters; each launch skips the other kind's chunks).
+template <typename T, int D, int G, int NKB, bool PAIRED>
 __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn_leaf_kernel(AttnLeafArgs a) {
   constexpr int NW = attn_waves<NKB>();
   constexpr int NS = D / 32;                   // contraction steps of S
@@ -111,23 +129,18 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
-  int64_t lo = 0, hi = a.ncl;
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (a.chunk_off[mid] <= chunk) lo = mid;
-    else hi = mid;
-  }
-  const int64_t c = lo;
+  const int64_t c = a.chunk_map[chunk];
   const int64_t hl = c / a.Mb;  // head within the chunk
-  const int64_t j = c % a.M1;   // leaf
+  const int64_t jk = c % a.Mk;  // key block: leaf, or M_1 + level-2 block
+  if ((jk >= a.M1) != PAIRED) return;  // the other launch's cluster
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kAttnChunk;
   const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
   const int64_t p_end = p_begin + kAttnChunk < p_end_c ? p_begin + kAttnChunk : p_end_c;
 
-  const int C = a.C;
-  const int64_t key0 = j * (int64_t)C;
+  const int C = PAIRED ? 2 * a.C : a.C;  // keys of the tile
+  const int64_t key0 = (PAIRED ? jk - a.M1 : jk) * (int64_t)C;
   const int nkeys = (int)((a.N - key0) < C ? (a.N - key0) : C);
   const T* kh = static_cast<const T*>(a.k) + bh * a.cap * D;
   const T* vh = static_cast<const T*>(a.v) + bh * a.cap * D;
@@ -240,6 +253,10 @@ __global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn
       const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
       a.pm[rec] = m;
       a.pl[rec] = l;
+      if constexpr (PAIRED) {  // the odd leaf's slot (the next one) is covered here
+        a.pm[rec + G] = -INFINITY;
+        a.pl[rec + G] = 0.f;
+      }
     }
     wave_sync();
     {
@@ -377,11 +394,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
 hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, const void* v, const int32_t* idx,
                             void* o, float* lse, void* ws, hipStream_t stream) {
   const AttnLayout L = attn_layout(p);
+  const bool pairs_on = attn_pairs(p);
   char* base = static_cast<char*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
+  int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
   float* pm = reinterpret_cast<float*>(base + L.off_m);
   float* pl = reinterpret_cast<float*>(base + L.off_l);
@@ -392,12 +411,13 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     const int64_t entries = heads * p.N * p.K;
     const int64_t ncl = heads * L.Mb;
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
-    hipError_t err =
-        launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, kAttnChunk, cb, stream);
+    hipError_t err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.Mk, kAttnBins,
+                                     kAttnChunk, cb, stream, pairs_on ? L.M1 : 0);
     if (err != hipSuccess) return err;
-    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, pairs, pm, pl, po, ncl, L.M1, L.Mb, head0, p.N, p.Hq, p.Hkv, p.C,
-                    p.K,
-                    p.causal ? 1 : 0, p.cap, p.scale};
+    err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
+    if (err != hipSuccess) return err;
+    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, chunk_map, pairs, pm, pl, po, ncl, L.M1, L.Mk, L.Mb, head0,
+                    p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
     MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
     const int64_t max_chunks = (entries + kAttnChunk - 1) / kAttnChunk + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
@@ -416,12 +436,15 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
         return hipGetLastError();
       };
       hipError_t e;
-      if (p.C <= 32)
-        e = run(attn_leaf_kernel<T, D, G, 2>, 2, attn_waves<2>());
-      else if (p.C <= 64)
-        e = run(attn_leaf_kernel<T, D, G, 4>, 4, attn_waves<4>());
-      else
-        e = run(attn_leaf_kernel<T, D, G, 8>, 8, attn_waves<8>());
+      if (p.C <= 32) {
+        e = run(attn_leaf_kernel<T, D, G, 2, false>, 2, attn_waves<2>());
+        if (e == hipSuccess) e = run(attn_leaf_kernel<T, D, G, 4, true>, 4, attn_waves<4>());
+      } else if (p.C <= 64) {
+        e = run(attn_leaf_kernel<T, D, G, 4, false>, 4, attn_waves<4>());
+        if (e == hipSuccess) e = run(attn_leaf_kernel<T, D, G, 8, true>, 8, attn_waves<8>());
+      } else {
+        e = run(attn_leaf_kernel<T, D, G, 8, false>, 8, attn_waves<8>());
+      }
       if (e != hipSuccess) return e;
       const int64_t waves = heads * p.N;
       PISA_LAUNCH("attn_merge", stream, (attn_merge_kernel<T, D, G>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,

@@ -22,6 +22,12 @@
 // global-atomic fallback.  Either way: counts[c], offsets[c] (first pair) and
 // chunk_off[c] (first work chunk, chunk_off[ncl] = total) for
 // c = head * Mb + bin.
+//
+// Sibling pairing (attention only): an entry's key block is its leaf j,
+// except that an even leaf whose odd sibling is the row's next entry (rows
+// are ascending) becomes key block M_1 + j / 2, the level-2 block of both,
+// and the odd sibling's entry is dropped; the consumer attends both leaves
+// of such a block in one tile.
 #include "kernels.h"
 
 namespace pisa {
@@ -56,8 +62,26 @@ __device__ __forceinline__ int64_t bin_of(int32_t j, int64_t e_loc, int32_t K, i
   return ((e_loc / K) >> qshift) * M + j;
 }
 
-__global__ void hist_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int32_t qshift,
-                            int64_t Mb, int64_t tiles, int32_t* __restrict__ hist) {
+// key block of entry e (e_loc = t * K + slot within its head): keys[e], or
+// with sibling pairing (pair_m1 = M_1 > 0) the level-2 block M_1 + j / 2 for
+// an even leaf j followed by j + 1, and -1 for that odd sibling
+__device__ __forceinline__ int32_t entry_key(const int32_t* __restrict__ keys, int64_t e, int64_t e_loc, int32_t K,
+                                             int64_t pair_m1) {
+  int32_t j = keys[e];
+  if (pair_m1 > 0 && j >= 0) {
+    if (j >= pair_m1) return -1;  // not a leaf
+    const int32_t slot = (int32_t)(e_loc % K);
+    if ((j & 1) == 0) {
+      if (slot + 1 < K && j + 1 < pair_m1 && keys[e + 1] == j + 1) j = (int32_t)pair_m1 + (j >> 1);
+    } else if (slot > 0 && keys[e - 1] == j - 1) {
+      j = -1;
+    }
+  }
+  return j;
+}
+
+__global__ void hist_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int64_t pair_m1,
+                            int32_t qshift, int64_t Mb, int64_t tiles, int32_t* __restrict__ hist) {
   extern __shared__ int32_t s_h[];
   const int64_t head = blockIdx.y, tile = blockIdx.x;
   for (int64_t i = threadIdx.x; i < Mb; i += blockDim.x) s_h[i] = 0;
@@ -65,7 +89,8 @@ __global__ void hist_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_
   const int64_t lo = head * NK + tile * kHistTile;
   const int64_t hi = (tile + 1) * kHistTile < NK ? lo + kHistTile : head * NK + NK;
   for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) {
-    const int64_t bin = bin_of(keys[e], e - head * NK, K, M, qshift);
+    const int64_t el = e - head * NK;
+    const int64_t bin = bin_of(entry_key(keys, e, el, K, pair_m1), el, K, M, qshift);
     if (bin >= 0) atomicAdd(&s_h[bin], 1);
   }
   __syncthreads();
@@ -129,8 +154,8 @@ __device__ __forceinline__ int32_t pair_code(int64_t e_loc, int32_t K) {
   return (t << 5) | (int32_t)(e_loc - (int64_t)t * K);
 }
 
-__global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int32_t qshift,
-                               int64_t Mb, int64_t tiles, const int32_t* __restrict__ base,
+__global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int32_t K, int64_t M, int64_t pair_m1,
+                               int32_t qshift, int64_t Mb, int64_t tiles, const int32_t* __restrict__ base,
                                const int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
   extern __shared__ int32_t s_cur[];
   const int64_t head = blockIdx.y, tile = blockIdx.x;
@@ -140,8 +165,9 @@ __global__ void scatter_kernel(const int32_t* __restrict__ keys, int64_t NK, int
   const int64_t lo = head * NK + tile * kHistTile;
   const int64_t hi = (tile + 1) * kHistTile < NK ? lo + kHistTile : head * NK + NK;
   for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) {
-    const int64_t bin = bin_of(keys[e], e - head * NK, K, M, qshift);
-    if (bin >= 0) pairs[atomicAdd(&s_cur[bin], 1)] = pair_code(e - head * NK, K);
+    const int64_t el = e - head * NK;
+    const int64_t bin = bin_of(entry_key(keys, e, el, K, pair_m1), el, K, M, qshift);
+    if (bin >= 0) pairs[atomicAdd(&s_cur[bin], 1)] = pair_code(el, K);
   }
 }
 
@@ -212,10 +238,10 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 }
 
 __global__ void atomic_count_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int32_t K,
-                                    int64_t M, int32_t qshift, int64_t Mb, int32_t* counts) {
+                                    int64_t M, int64_t pair_m1, int32_t qshift, int64_t Mb, int32_t* counts) {
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t bin = bin_of(keys[e], e % NK, K, M, qshift);
+    const int64_t bin = bin_of(entry_key(keys, e, e % NK, K, pair_m1), e % NK, K, M, qshift);
     if (bin >= 0) atomicAdd(&counts[(e / NK) * Mb + bin], 1);
   }
 }
@@ -246,11 +272,11 @@ __global__ __launch_bounds__(1024) void offset_scan_kernel(const int32_t* __rest
 }
 
 __global__ void atomic_fill_kernel(const int32_t* __restrict__ keys, int64_t entries, int64_t NK, int32_t K,
-                                   int64_t M, int32_t qshift, int64_t Mb, const int32_t* __restrict__ offsets,
-                                   int32_t* cursor, int32_t* pairs) {
+                                   int64_t M, int64_t pair_m1, int32_t qshift, int64_t Mb,
+                                   const int32_t* __restrict__ offsets, int32_t* cursor, int32_t* pairs) {
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < entries;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t bin = bin_of(keys[e], e % NK, K, M, qshift);
+    const int64_t bin = bin_of(entry_key(keys, e, e % NK, K, pair_m1), e % NK, K, M, qshift);
     if (bin < 0) continue;
     const int64_t c = (e / NK) * Mb + bin;
     pairs[offsets[c] + atomicAdd(&cursor[c], 1)] = pair_code(e % NK, K);
@@ -269,8 +295,22 @@ static hipError_t launch_chunk_scan(const ClusterBufs& b, int64_t heads, int64_t
   return hipGetLastError();
 }
 
+// map[ch] = c for every work chunk ch of cluster c
+__global__ void chunk_map_kernel(const int32_t* __restrict__ chunk_off, int64_t ncl, int32_t* __restrict__ map) {
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < ncl; c += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t hi = chunk_off[c + 1];
+    for (int32_t ch = chunk_off[c]; ch < hi; ++ch) map[ch] = (int32_t)c;
+  }
+}
+
+hipError_t launch_chunk_map(const int32_t* chunk_off, int64_t ncl, int32_t* map, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
+  PISA_LAUNCH("cluster_chunks", stream, chunk_map_kernel, dim3(blocks), dim3(256), 0, chunk_off, ncl, map);
+  return hipGetLastError();
+}
+
 hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int64_t max_bins,
-                           int32_t chunk, const ClusterBufs& b, hipStream_t stream) {
+                           int32_t chunk, const ClusterBufs& b, hipStream_t stream, int64_t pair_m1) {
   const int64_t N = NK / K;
   const int32_t qs = cluster_query_shift(N, M, max_bins);
   const int64_t Mb = cluster_bins(N, M, max_bins);
@@ -285,27 +325,27 @@ hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32
     };
     if (big(hist_kernel) != hipSuccess || big(scatter_kernel) != hipSuccess) return hipErrorInvalidValue;
     PISA_LAUNCH("cluster_hist", stream, hist_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds, keys, NK,
-                K, M, qs, Mb, tiles, b.hist);
+                K, M, pair_m1, qs, Mb, tiles, b.hist);
     PISA_LAUNCH("cluster_scan", stream, col_scan_kernel, dim3((unsigned)((Mb + 255) / 256), (unsigned)heads),
                 dim3(256), 0, b.hist, Mb, tiles, b.counts);
     PISA_LAUNCH("cluster_scan", stream, bin_scan_kernel, dim3((unsigned)heads), dim3(1024), 0, b.counts, NK, Mb,
                 b.offsets);
     if (launch_chunk_scan(b, heads, Mb, chunk, stream) != hipSuccess) return hipGetLastError();
     PISA_LAUNCH("cluster_scatter", stream, scatter_kernel, dim3((unsigned)tiles, (unsigned)heads), dim3(256), lds,
-                keys, NK, K, M, qs, Mb, tiles, b.hist, b.offsets, b.pairs);
+                keys, NK, K, M, pair_m1, qs, Mb, tiles, b.hist, b.offsets, b.pairs);
     return hipGetLastError();
   }
   const int64_t entries = heads * NK;
   const unsigned ew = (unsigned)((entries + 255) / 256 < 65536 ? (entries + 255) / 256 : 65536);
   const unsigned cw = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
   PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cw), dim3(256), 0, b.counts, ncl, 0);
-  PISA_LAUNCH("cluster_count", stream, atomic_count_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, qs, Mb,
-              b.counts);
+  PISA_LAUNCH("cluster_count", stream, atomic_count_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, pair_m1,
+              qs, Mb, b.counts);
   PISA_LAUNCH("cluster_scan", stream, offset_scan_kernel, dim3(1), dim3(1024), 0, b.counts, ncl, b.offsets);
   if (launch_chunk_scan(b, heads, Mb, chunk, stream) != hipSuccess) return hipGetLastError();  // cursor as scratch
   PISA_LAUNCH("cluster_zero", stream, fill_i32_kernel, dim3(cw), dim3(256), 0, b.cursor, ncl, 0);
-  PISA_LAUNCH("cluster_fill", stream, atomic_fill_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, qs, Mb,
-              b.offsets, b.cursor, b.pairs);
+  PISA_LAUNCH("cluster_fill", stream, atomic_fill_kernel, dim3(ew), dim3(256), 0, keys, entries, NK, K, M, pair_m1,
+              qs, Mb, b.offsets, b.cursor, b.pairs);
   return hipGetLastError();
 }
 

@@ -97,12 +97,18 @@ size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t Mb);
 // keys: [heads][N][K] block indices (-1 = none), NK = N * K.  pairs holds,
 // per cluster c = head * Mb + (t >> shift) * M + block, the codes
 // (t << 5) | slot of its entries; the key block of cluster c is c % M.
+// pair_m1 > 0 (= M_1, ascending leaf rows, M = M_1 + ceil(M_1 / 2)): an even
+// leaf j kept together with j + 1 goes to key block M_1 + j / 2 under the
+// slot of j, and the entry of j + 1 is dropped.
 hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int64_t max_bins,
-                           int32_t chunk, const ClusterBufs& b, hipStream_t stream);
+                           int32_t chunk, const ClusterBufs& b, hipStream_t stream, int64_t pair_m1 = 0);
+// map[ch] = the cluster of work chunk ch, for ch < chunk_off[ncl]
+hipError_t launch_chunk_map(const int32_t* chunk_off, int64_t ncl, int32_t* map, hipStream_t stream);
 
-// Attention clusters (forward and backward): (query block, leaf) bins per
-// head, so one block of queries is attended together and its query rows are
-// re-read from cache.
+// Attention clusters (forward and backward): (query block, key block) bins
+// per head (key blocks: the leaves, and in the forward at C <= 64 also the
+// level-2 blocks of sibling pairs), so one block of queries is attended
+// together and its query rows are re-read from cache.
 constexpr int64_t kAttnBins = 8192;
 
 // attn_leaf.hip: leaf-major MFMA attention with a merge pass
