@@ -37,9 +37,9 @@ constexpr size_t kBwdBudget = (size_t)8 << 30;  // partial dQ rows per head chun
 static size_t b256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  int64_t heads, M1, Mb, ncl, slots;  // Mb: cluster bins per head
-  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_dq, off_hist, off_rowdot, off_dk, off_dv,
-      total;
+  int64_t heads, M1, Mb, ncl, slots, max_chunks;  // Mb: cluster bins per head
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_map, off_pairs, off_dq, off_hist, off_rowdot, off_dk,
+      off_dv, total;
 };
 
 static BwdLayout bwd_layout(const Problem& p) {
@@ -56,6 +56,7 @@ static BwdLayout bwd_layout(const Problem& p) {
   L.heads = (BH + nchunks - 1) / nchunks;
   L.ncl = L.heads * L.Mb;
   L.slots = L.heads * (int64_t)p.N * p.K;
+  L.max_chunks = (L.slots + kBwdChunk - 1) / kBwdChunk + L.ncl;
   size_t off = 0;
   L.off_counts = off;
   off = b256(off + 4 * (size_t)L.ncl);
@@ -65,6 +66,8 @@ static BwdLayout bwd_layout(const Problem& p) {
   off = b256(off + 4 * (size_t)(L.ncl + 1));
   L.off_chunks = off;
   off = b256(off + 4 * (size_t)(L.ncl + 1));
+  L.off_map = off;
+  off = b256(off + 4 * (size_t)L.max_chunks);
   L.off_pairs = off;
   off = b256(off + 4 * (size_t)L.slots);
   L.off_dq = off;
@@ -132,6 +135,7 @@ struct BwdArgs {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
+  const int32_t* chunk_map;  // work chunk -> cluster
   const int32_t* pairs;
   void* dq_part;  // [heads][N][K][G][D], input dtype
   float* dk_acc;   // [B][Hkv][N][D]
@@ -178,13 +182,7 @@ __global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void 
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
-  int64_t lo = 0, hi = a.ncl;
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (a.chunk_off[mid] <= chunk) lo = mid;
-    else hi = mid;
-  }
-  const int64_t c = lo;
+  const int64_t c = a.chunk_map[chunk];
   const int64_t hl = c / a.Mb;
   const int64_t j = c % a.M1;
   const int64_t bh = a.head0 + hl;
@@ -484,6 +482,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
+  int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
   void* dq_part = base + L.off_dq;
   float* rowdot = reinterpret_cast<float*>(base + L.off_rowdot);
@@ -511,7 +510,9 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
     err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, kBwdChunk, cb, stream);
     if (err != hipSuccess) return err;
-    BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1, L.Mb,
+    err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
+    if (err != hipSuccess) return err;
+    BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, chunk_map, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1, L.Mb,
                head0, p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
     BwdMergeArgs ma{idx, dq_part, dq, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
     const int64_t max_chunks = (entries + kBwdChunk - 1) / kBwdChunk + ncl;

@@ -28,8 +28,8 @@ constexpr int kTopkWaves = 4;
 // ---- workspace layout -------------------------------------------------------
 struct S2Layout {
   int64_t ncl;      // clusters = B * Hkv * bins per head
-  int64_t max_pairs;
-  size_t off_counts, off_cursor, off_offsets, off_chunks, off_pairs, off_scores, off_hist, total;
+  int64_t max_pairs, max_chunks;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_map, off_pairs, off_scores, off_hist, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -40,6 +40,7 @@ static S2Layout s2_layout(const Problem& p) {
   const int64_t Mb = cluster_bins(p.N, M2, M2);  // (query block, level-2 block) bins per head
   s.ncl = (int64_t)p.B * p.Hkv * Mb;
   s.max_pairs = (int64_t)p.B * p.Hkv * p.N * p.K;
+  s.max_chunks = (s.max_pairs + kS2Chunk - 1) / kS2Chunk + s.ncl;
   size_t off = 0;
   s.off_counts = off;
   off = align256(off + sizeof(int32_t) * s.ncl);
@@ -49,6 +50,8 @@ static S2Layout s2_layout(const Problem& p) {
   off = align256(off + sizeof(int32_t) * (s.ncl + 1));
   s.off_chunks = off;
   off = align256(off + sizeof(int32_t) * (s.ncl + 1));
+  s.off_map = off;
+  off = align256(off + sizeof(int32_t) * s.max_chunks);
   s.off_pairs = off;
   off = align256(off + sizeof(int32_t) * s.max_pairs);
   s.off_scores = off;
@@ -67,6 +70,7 @@ struct S2Args {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
+  const int32_t* chunk_map;  // work chunk -> cluster
   const int32_t* pairs;
   float* scores;  // [B][Hkv][N][K][2]
   int64_t ncl, M1, M2, Mb;  // Mb: cluster bins per head
@@ -99,14 +103,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_ker
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
-  // cluster c with chunk_off[c] <= chunk < chunk_off[c + 1]
-  int64_t lo = 0, hi = a.ncl;
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (a.chunk_off[mid] <= chunk) lo = mid;
-    else hi = mid;
-  }
-  const int64_t c = lo;
+  const int64_t c = a.chunk_map[chunk];  // chunk_off[c] <= chunk < chunk_off[c + 1]
   const int64_t bh = c / a.Mb;
   const int64_t j2 = c % a.M2;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
@@ -369,6 +366,7 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
+  int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
   float* scores = reinterpret_cast<float*>(base + L.off_scores);
   const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
@@ -376,7 +374,9 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
   hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, p.K, M2, M2, kS2Chunk, cb, stream);
   if (err != hipSuccess) return err;
-  S2Args a{q, k, counts, offsets, chunk_off, pairs, scores, L.ncl, M1, M2, cluster_bins(p.N, M2, M2), p.B, p.N, p.Hq, p.Hkv,
+  err = launch_chunk_map(chunk_off, L.ncl, chunk_map, stream);
+  if (err != hipSuccess) return err;
+  S2Args a{q, k, counts, offsets, chunk_off, chunk_map, pairs, scores, L.ncl, M1, M2, cluster_bins(p.N, M2, M2), p.B, p.N, p.Hq, p.Hkv,
            p.C, p.K,
            p.causal ? 1 : 0, p.cap, p.scale};
   const int64_t max_chunks = (entries + kS2Chunk - 1) / kS2Chunk + L.ncl;
