@@ -142,6 +142,19 @@ def attended_keys(idx, N: int, C: int, causal: bool):
     return int(keys.sum().item())
 
 
+def attention_partials(idx, C: int) -> int:
+    """Partial (query, slot) records the attention writes and the merge reads
+    per KV head: one per kept leaf, except that where C <= 64 a leaf kept
+    together with its sibling (even j followed by j + 1 in the ascending row)
+    shares one record with it."""
+    j = idx.long()
+    kept = int((j >= 0).sum().item())
+    if C > 64:
+        return kept
+    both = (j[..., :-1] >= 0) & (j[..., :-1] % 2 == 0) & (j[..., 1:] == j[..., :-1] + 1)
+    return kept - int(both.sum().item())
+
+
 def stage1_scored_keys(blk2, N: int, C: int, causal: bool):
     """Keys scored by stage 2: both leaves of every kept level-2 block."""
     import torch
@@ -253,7 +266,7 @@ def main() -> int:
     blk2 = ws[: w.B * w.Hkv * w.N * w.K * 4].view(torch.int32).view(w.B, w.Hkv, w.N, w.K)
     scored_keys, s1_pairs = stage1_scored_keys(blk2, w.N, w.C, w.causal)
     attn_keys = attended_keys(idx, w.N, w.C, w.causal)
-    kept_pairs = int((idx >= 0).sum().item())
+    partials = attention_partials(idx, w.C)
     M = [pisa.level_rows(w.N, w.C, l) for l in range(1, pisa.levels(w.N, w.C) + 1)]
     rc = pisa.route_counts(p, q, k, pyr) if w.dtype == "bf16" else None
     queries = w.B * w.Hkv * w.N
@@ -270,9 +283,10 @@ def main() -> int:
         # read every key once, write leaf means and the four levels above them
         "pyr_leaf": ("hbm", float(w.B * w.Hkv * (w.N * w.D * esize + sum(M[:5]) * w.D * 4)), "GB/s",
                      "N*d*elem read + (M1+..+M5)*d*4 written per (b, h)"),
-        # merge: read G partial rows (d elems + m, l) per kept pair, write o
-        "attn_merge": ("hbm", float(kept_pairs * G * (w.D * esize + 8) + w.B * w.Hq * w.N * w.D * esize), "GB/s",
-                       "per kept (query, leaf): G*(d*elem + 8) bytes of partials read; o written once"),
+        # merge: read G partial rows (d elems + m, l) per partial record, write o
+        "attn_merge": ("hbm", float(partials * G * (w.D * esize + 8) + w.B * w.Hq * w.N * w.D * esize), "GB/s",
+                       f"per partial record (query, kept leaf or kept sibling pair; {partials} records): "
+                       "G*(d*elem + 8) bytes read; o written once"),
     }
     if rc is not None:
         # per (t, h): the scored child summaries (fp32 rows, d*4 bytes each),
