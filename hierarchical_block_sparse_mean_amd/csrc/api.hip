@@ -285,9 +285,12 @@ pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k
   return hip_status(pisa::launch_attn_leaf(pr, q, k, v, idx, o, lse, ws, stream), "pisa_sparse_attn (leaf-major)");
 }
 
+// fp32 rows of d = 128 with C > 64: a leaf's K, V and K^T tiles exceed the LDS
+static bool bwd_shape_unsupported(const pisa::Problem& q) { return q.dtype == 0 && q.D == 128 && q.C > 64; }
+
 size_t pisa_attn_backward_workspace_bytes(const pisa_problem* p) {
   pisa::Problem q;
-  if (validate(p, &q) != PISA_OK) return 0;
+  if (validate(p, &q) != PISA_OK || bwd_shape_unsupported(q)) return 0;
   return pisa::attn_bwd_workspace_bytes(q);
 }
 
@@ -297,6 +300,8 @@ pisa_status pisa_sparse_attn_backward(const pisa_problem* p, const void* q, cons
   pisa::Problem pr;
   pisa_status s = validate(p, &pr);
   if (s != PISA_OK) return s;
+  if (bwd_shape_unsupported(pr))
+    return fail(PISA_ERR_UNSUPPORTED, "backward with fp32 rows of d = 128 needs C <= 64 (got C = %d)", pr.C);
   if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || o == nullptr || lse == nullptr ||
       dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
     return fail(PISA_ERR_INVALID_ARG, "q, k, v, idx, o, lse, dout, dq, dk and dv must be non-NULL");

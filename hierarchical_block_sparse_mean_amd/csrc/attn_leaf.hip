@@ -27,18 +27,34 @@
 
 namespace pisa {
 
+constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+// LDS of a workgroup: the tile's K (row-major) and V^T, the waves' output
+// staging, the chunk's pair codes
+template <typename T, int D, int NKB>
+constexpr size_t attn_lds_bytes(int nw) {
+  constexpr size_t e = 16 / sizeof(T);
+  return ((size_t)NKB * 16 * (D + e) + (size_t)D * (NKB * 16 + e) + (size_t)nw * 16 * (D + e)) * sizeof(T) +
+         4 * (size_t)kAttnChunk;
+}
 // waves per workgroup: 12 for tiles of 8 key blocks (their K, V^T and the
 // waves' output staging leave room for one workgroup per CU, so it brings
-// the waves), 8 otherwise (two workgroups per CU)
-template <int NKB>
-constexpr int attn_waves() { return NKB >= 8 ? 12 : 8; }
-constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
+// the waves), 8 otherwise (two workgroups per CU); fewer where that would
+// not fit the LDS (fp32 rows of d = 128 in 8-block tiles)
+template <typename T, int D, int NKB>
+constexpr int attn_waves() {
+  int nw = NKB >= 8 ? 12 : 8;
+  while (nw > 1 && attn_lds_bytes<T, D, NKB>(nw) > kLdsPerCu) --nw;
+  return nw;
+}
 constexpr size_t kAttnBudget = (size_t)8 << 30;  // partial buffers per head chunk
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks
-static bool attn_pairs(const Problem& p) { return p.C <= 64; }
+// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks, and
+// not for fp32 rows of d = 128 (such a tile leaves LDS for two waves only)
+static bool attn_pairs(const Problem& p) { return p.C <= 64 && (p.dtype == 1 || p.D <= 64); }
 
 struct AttnLayout {
   int64_t heads;  // (b, h) heads per chunk
@@ -113,8 +129,8 @@ struct AttnLeafArgs {
 // a leaf, or 2C of a level-2 block (PAIRED: the launch over the level-2
 // block clusters; each launch skips the other kind's chunks).
 template <typename T, int D, int G, int NKB, bool PAIRED>
-__global__ __launch_bounds__(attn_waves<NKB>() * kWave) PISA_MFMA_REGS void attn_leaf_kernel(AttnLeafArgs a) {
-  constexpr int NW = attn_waves<NKB>();
+__global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS void attn_leaf_kernel(AttnLeafArgs a) {
+  constexpr int NW = attn_waves<T, D, NKB>();
   constexpr int NS = D / 32;                   // contraction steps of S
   constexpr int TQ = 16 / G;                   // queries per 16-column tile
   constexpr int CP = NKB * 16;                 // keys held (zero padded)
@@ -437,13 +453,13 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
       };
       hipError_t e;
       if (p.C <= 32) {
-        e = run(attn_leaf_kernel<T, D, G, 2, false>, 2, attn_waves<2>());
-        if (e == hipSuccess) e = run(attn_leaf_kernel<T, D, G, 4, true>, 4, attn_waves<4>());
+        e = run(attn_leaf_kernel<T, D, G, 2, false>, 2, attn_waves<T, D, 2>());
+        if (e == hipSuccess && pairs_on) e = run(attn_leaf_kernel<T, D, G, 4, true>, 4, attn_waves<T, D, 4>());
       } else if (p.C <= 64) {
-        e = run(attn_leaf_kernel<T, D, G, 4, false>, 4, attn_waves<4>());
-        if (e == hipSuccess) e = run(attn_leaf_kernel<T, D, G, 8, true>, 8, attn_waves<8>());
+        e = run(attn_leaf_kernel<T, D, G, 4, false>, 4, attn_waves<T, D, 4>());
+        if (e == hipSuccess && pairs_on) e = run(attn_leaf_kernel<T, D, G, 8, true>, 8, attn_waves<T, D, 8>());
       } else {
-        e = run(attn_leaf_kernel<T, D, G, 8, false>, 8, attn_waves<8>());
+        e = run(attn_leaf_kernel<T, D, G, 8, false>, 8, attn_waves<T, D, 8>());
       }
       if (e != hipSuccess) return e;
       const int64_t waves = heads * p.N;

@@ -159,7 +159,9 @@ pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k
  * the outputs of pisa_sparse_attn for the same inputs (lse fp32 [B][Hq][N],
  * required).  Element types follow dtype; accumulation is fp32 (bf16 inputs:
  * p and dS are rounded to bf16 for the matrix products).  ws: at least
- * pisa_attn_backward_workspace_bytes(p) bytes, 256-byte aligned.            */
+ * pisa_attn_backward_workspace_bytes(p) bytes, 256-byte aligned.  fp32
+ * inputs with D = 128 need C <= 64 (a leaf's K, V and K^T tiles must fit
+ * the LDS): otherwise PISA_ERR_UNSUPPORTED, and the workspace size is 0.   */
 size_t pisa_attn_backward_workspace_bytes(const pisa_problem* p);
 pisa_status pisa_sparse_attn_backward(const pisa_problem* p, const void* q, const void* k, const void* v,
                                       const int32_t* idx, const void* o, const float* lse, const void* dout,

@@ -112,6 +112,19 @@ def test_null_pointers_and_small_workspace(lib):
     assert lib.pisa_build_pyramid(None, FAKE, FAKE, None) == pisa.PISA_ERR_INVALID_ARG
 
 
+def test_backward_shape_limit(lib):
+    """fp32 rows of d = 128 with C > 64 are rejected by the backward before
+    any pointer is used; the forward and the other shapes are accepted."""
+    big = _p(D=128, C=128).c()
+    assert lib.pisa_attn_backward_workspace_bytes(ctypes.byref(big)) == 0
+    args = [FAKE] * 10 + [FAKE, 1 << 40, None]
+    assert lib.pisa_sparse_attn_backward(ctypes.byref(big), *args) == pisa.PISA_ERR_UNSUPPORTED
+    assert "C <= 64" in lib.pisa_last_error().decode()
+    assert lib.pisa_attn_workspace_bytes(ctypes.byref(big)) > 0
+    for kw in (dict(D=128, C=64), dict(D=64, C=128), dict(D=128, C=128, dtype="bf16")):
+        assert lib.pisa_attn_backward_workspace_bytes(ctypes.byref(_p(**kw).c())) > 0, kw
+
+
 def test_decode_validation(lib):
     d = pisa.DecodeProblem(S=2, cap=100, Hq=4, Hkv=1, D=64, C=64, K=4, dtype="f32")
     args = [FAKE] * 7
