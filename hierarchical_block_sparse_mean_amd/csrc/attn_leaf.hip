@@ -19,8 +19,8 @@
 // in its ascending row) and 2C keys fit one tile (C <= 64), the pair goes to
 // a cluster of that block instead: a second launch attends the 2C keys in one
 // tile, so the query's rows are read once and one partial (under the slot of
-// the even leaf) is written for both; the odd leaf's slot gets m = -inf,
-// which the merge skips without reading its row.
+// the even leaf) is written for both; the merge recognises the odd leaf's
+// slot from idx and skips it.
 // Work is done in chunks of KV heads so the partial buffers stay bounded and
 // one chunk's queries stay cache-resident.
 #include "kernels.h"
@@ -269,10 +269,6 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
       const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
       a.pm[rec] = m;
       a.pl[rec] = l;
-      if constexpr (PAIRED) {  // the odd leaf's slot (the next one) is covered here
-        a.pm[rec + G] = -INFINITY;
-        a.pl[rec + G] = 0.f;
-      }
     }
     wave_sync();
     {
@@ -337,13 +333,44 @@ struct MergeArgs {
   float* lse;
   int64_t head0, heads, M1;
   int32_t N, Hq, Hkv, K;
+  int32_t pairs;  // sibling pairs were attended as one partial (under the even leaf's slot)
 };
 
-// One wave per (query, KV head): m and l of the K slots x G heads go through
-// LDS; each lane then owns 8 output dims of one head and issues the loads of
-// all its slots' partial rows before combining them.
+// 8 consecutive elements of a partial row, as loaded (16 or 32 bytes)
+template <typename T>
+struct Row8 {
+  uint4 v[sizeof(T) == 2 ? 1 : 2];
+  __device__ __forceinline__ void load(const T* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    v[0] = q[0];
+    if constexpr (sizeof(T) == 4) v[1] = q[1];
+  }
+  __device__ __forceinline__ void get(float* out) const {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t wv[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(wv[i] << 16);
+        out[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+    } else {
+      const uint32_t wv[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(wv[i]);
+    }
+  }
+};
+
+// One wave per (query, KV head).  The slots that hold a partial follow from
+// idx alone (a leaf of the problem, other than the odd half of a kept
+// sibling pair when pairs were attended together), so each lane, which owns
+// 8 output dims of one head, issues the loads of its first SG slots' rows
+// before the slots' m and l (staged through LDS) have arrived; the rows are
+// then combined with weights exp(m - max m).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+  constexpr int SG = sizeof(T) == 2 ? 16 : 8;          // slots whose rows are loaded together
+  constexpr int MLP = (32 * G + kWave - 1) / kWave;   // (m, l) entries per lane, at most
   __shared__ float s_m[4][32 * G], s_l[4][32 * G];
   __shared__ int32_t s_ok[4][32];
   const int w = threadIdx.x / kWave;
@@ -355,39 +382,77 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int32_t* sel = a.idx + (bh * a.N + t) * a.K;
   const int64_t rec0 = (hl * a.N + t) * a.K * G;  // record of (slot 0, head 0)
-  for (int i = lane; i < a.K; i += kWave) s_ok[w][i] = (sel[i] >= 0 && sel[i] < a.M1) ? 1 : 0;
-  for (int i = lane; i < a.K * G; i += kWave) {
-    s_m[w][i] = a.pm[rec0 + i];
-    s_l[w][i] = a.pl[rec0 + i];
+  for (int i = lane; i < a.K; i += kWave) {
+    const int32_t j = sel[i];
+    bool ok = j >= 0 && j < a.M1;
+    if (ok && a.pairs && (j & 1) && i > 0 && sel[i - 1] == j - 1) ok = false;
+    s_ok[w][i] = ok ? 1 : 0;
   }
-  wave_sync();
+  float mv[MLP], lv[MLP];
+#pragma unroll
+  for (int r = 0; r < MLP; ++r) {
+    const int i = lane + r * kWave;
+    mv[r] = i < a.K * G ? a.pm[rec0 + i] : 0.f;
+    lv[r] = i < a.K * G ? a.pl[rec0 + i] : 0.f;
+  }
+  wave_sync();  // s_ok
   const T* po = static_cast<const T*>(a.po);
-  for (int e0 = lane * 8; e0 < G * D; e0 += kWave * 8) {
+  auto issue = [&](int e0, int s0, Row8<T>* rows) {
+    const int hh = e0 / D, d = e0 % D;
+#pragma unroll
+    for (int u = 0; u < SG; ++u) {
+      const int s = s0 + u;
+      if (s < a.K && s_ok[w][s]) rows[u].load(po + (rec0 + s * G + hh) * D + d);
+      else rows[u] = Row8<T>{};
+    }
+  };
+  // where one pass of the lanes covers the G heads (G d <= 512), the first
+  // SG rows are in flight while m and l are staged
+  constexpr bool ONE = G * D <= 8 * kWave;
+  const int e_first = lane * 8;
+  Row8<T> first[ONE ? SG : 1];
+  if constexpr (ONE)
+    if (e_first < G * D) issue(e_first, 0, first);
+#pragma unroll
+  for (int r = 0; r < MLP; ++r) {
+    const int i = lane + r * kWave;
+    if (i < a.K * G) {
+      s_m[w][i] = mv[r];
+      s_l[w][i] = lv[r];
+    }
+  }
+  wave_sync();  // s_m, s_l
+  for (int e0 = e_first; e0 < G * D; e0 += kWave * 8) {
     const int hh = e0 / D, d = e0 % D;
     float M = -INFINITY;
     for (int s = 0; s < a.K; ++s)
       if (s_ok[w][s]) M = fmaxf(M, s_m[w][s * G + hh]);
     float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
-      for (int s0 = 0; s0 < a.K; s0 += 8) {
-        float v[8][8];
-        float wgt[8];
+      for (int s0 = 0; s0 < a.K; s0 += SG) {
+        Row8<T> rows[SG];
+        if constexpr (ONE) {
+          if (s0 == 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int s = s0 + u;
-          const bool ok = s < a.K && s_ok[w][s] && s_m[w][s * G + hh] != -INFINITY;
-          wgt[u] = ok ? __expf(s_m[w][s * G + hh] - M) : 0.f;
-          if (ok) load8<T>(po + (rec0 + s * G + hh) * D + d, v[u]);
-          else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+            for (int u = 0; u < SG; ++u) rows[u] = first[u];
+          } else {
+            issue(e0, s0, rows);
           }
-          if (ok) L += wgt[u] * s_l[w][s * G + hh];
+        } else {
+          issue(e0, s0, rows);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < SG; ++u) {
+          const int s = s0 + u;
+          if (s < a.K && s_ok[w][s] && s_m[w][s * G + hh] != -INFINITY) {
+            const float wgt = __expf(s_m[w][s * G + hh] - M);
+            L += wgt * s_l[w][s * G + hh];
+            float v[8];
+            rows[u].get(v);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt[u], v[u][i], acc[i]);
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+          }
+        }
       }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -434,7 +499,7 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     if (err != hipSuccess) return err;
     AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, chunk_map, pairs, pm, pl, po, ncl, L.M1, L.Mk, L.Mb, head0,
                     p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
-    MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
+    MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K, pairs_on ? 1 : 0};
     const int64_t max_chunks = (entries + kAttnChunk - 1) / kAttnChunk + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
       using T = std::remove_pointer_t<decltype(tp)>;
