@@ -416,8 +416,12 @@ struct BwdMergeArgs {
   int32_t N, Hq, Hkv, K;
 };
 
+// One wave per (query, KV head): the valid slots as a lane mask, then each
+// lane (8 dims of one head) issues the loads of up to 16 slots' rows at once
+// and sums them.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdMergeArgs a) {
+  constexpr int SG = 16;
   const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
   if (wid >= a.heads * a.N) return;
   const int lane = lane_id();
@@ -426,33 +430,31 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdMergeArgs a) {
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
   const int32_t* sel = a.idx + (bh * a.N + t) * a.K;
   const int64_t rec0 = (hl * a.N + t) * a.K * G;
-  for (int e0 = lane * 4; e0 < G * D; e0 += kWave * 4) {
+  const int32_t js = lane < a.K ? sel[lane] : -1;
+  const uint64_t okm = __ballot(js >= 0 && js < a.M1);  // K <= 32
+  const T* part = static_cast<const T*>(a.dq_part);
+  for (int e0 = lane * 8; e0 < G * D; e0 += kWave * 8) {
     const int hh = e0 / D, d = e0 % D;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.K; ++s) {
-      const int32_t jl = sel[s];
-      if (jl < 0 || jl >= a.M1) continue;
-      float v[4];
-      const T* src = static_cast<const T*>(a.dq_part) + (rec0 + s * G + hh) * D + d;
-      if constexpr (sizeof(T) == 2) {
-        const uint2 u = *reinterpret_cast<const uint2*>(src);
-        v[0] = __uint_as_float(u.x << 16);
-        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(u.y << 16);
-        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-      } else {
-        const float4 f = *reinterpret_cast<const float4*>(src);
-        v[0] = f.x;
-        v[1] = f.y;
-        v[2] = f.z;
-        v[3] = f.w;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.K; s0 += SG) {
+      Row8<T> rows[SG];
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        const int s = s0 + u;
+        if (s < a.K && ((okm >> s) & 1ull)) rows[u].load(part + (rec0 + s * G + hh) * D + d);
+        else rows[u] = Row8<T>{};
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += v[i];
+      for (int u = 0; u < SG; ++u) {
+        float v[8];
+        rows[u].get(v);  // zero for an invalid slot
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
     }
     T* out = static_cast<T*>(a.dq) + (((int64_t)b * a.Hq + h * G + hh) * a.N + t) * D + d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store1<T>(out + i, acc[i]);
+    for (int i = 0; i < 8; ++i) store1<T>(out + i, acc[i]);
   }
 }
 

@@ -67,6 +67,31 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* out) {
   }
 }
 
+// 8 consecutive elements of a row, as loaded (16 or 32 bytes), unpacked later
+template <typename T>
+struct Row8 {
+  uint4 v[sizeof(T) == 2 ? 1 : 2];
+  __device__ __forceinline__ void load(const T* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    v[0] = q[0];
+    if constexpr (sizeof(T) == 4) v[1] = q[1];
+  }
+  __device__ __forceinline__ void get(float* out) const {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t wv[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(wv[i] << 16);
+        out[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+    } else {
+      const uint32_t wv[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(wv[i]);
+    }
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ float load1(const T* p);
 template <>
