@@ -329,16 +329,26 @@ struct TopkArgs {
 };
 
 // KP: K when K is 16 or 32 (the 2K candidates sit in lanes [0, 2K): top K by
-// half sorts, then a K-lane index sort), else 0 (full wave sorts).
+// half sorts, then a K-lane index sort), else 0 (full wave sorts).  For
+// K = 16 a wave takes two (b, h, t) rows, one per 32-lane half (every
+// exchange of the half sorts stays inside a half).
+template <int KP>
+constexpr int topk_rows_per_wave() { return KP == 16 ? 2 : 1; }
+
 template <int KP>
 __global__ __launch_bounds__(kTopkWaves* kWave) void final_topk_kernel(TopkArgs a) {
-  const int64_t wid = (int64_t)blockIdx.x * kTopkWaves + threadIdx.x / kWave;
+  constexpr int QPW = topk_rows_per_wave<KP>();
+  const int lane0 = lane_id();
+  const int half = QPW == 2 ? lane0 >> 5 : 0;
+  const int lane = QPW == 2 ? lane0 & 31 : lane0;  // lane within the row's lanes
+  const int64_t wid0 = ((int64_t)blockIdx.x * kTopkWaves + threadIdx.x / kWave) * QPW;
   const int64_t total = (int64_t)a.B * a.Hkv * a.N;
-  if (wid >= total) return;
-  const int lane = lane_id();
+  if (wid0 >= total) return;  // uniform over the wave
+  const int64_t wid = wid0 + half;
+  const bool live = wid < total;
   const int slot = lane >> 1, l = lane & 1;
   uint64_t key = 0ull;
-  if (slot < a.K) {
+  if (live && slot < a.K) {
     const int32_t j2 = a.blk2[wid * a.K + slot];
     if (j2 >= 0) {
       const float sc = a.scores[(wid * a.K + slot) * 2 + l];
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void final_topk_kernel(TopkArgs 
   uint64_t k2 = kept ? index_key(key_index(key), key_score(key)) : 0ull;
   if (KP) k2 = group_sort_desc<(KP ? KP : 16)>(k2);
   else k2 = wave_sort_desc(k2);
-  if (lane < a.K) {
+  if (live && lane < a.K) {
     const bool v = k2 != 0ull;
     a.idx[wid * a.K + lane] = v ? index_key_index(k2) : -1;
     if (a.score) a.score[wid * a.K + lane] = v ? index_key_score(k2) : -INFINITY;
@@ -417,14 +427,18 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   });
   if (err != hipSuccess) return err;
   TopkArgs ta{blk2, scores, idx, score, p.B, p.N, p.Hkv, p.K};
-  const int64_t waves = (int64_t)p.B * p.Hkv * p.N;
-  const dim3 tgrid((unsigned)((waves + kTopkWaves - 1) / kTopkWaves)), tblock(kTopkWaves * kWave);
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.N;
+  auto grid = [&](int qpw) {
+    const int64_t waves = (rows + qpw - 1) / qpw;
+    return dim3((unsigned)((waves + kTopkWaves - 1) / kTopkWaves));
+  };
+  const dim3 tblock(kTopkWaves * kWave);
   if (p.K == 16)
-    PISA_LAUNCH("final_topk", stream, final_topk_kernel<16>, tgrid, tblock, 0, ta);
+    PISA_LAUNCH("final_topk", stream, final_topk_kernel<16>, grid(topk_rows_per_wave<16>()), tblock, 0, ta);
   else if (p.K == 32)
-    PISA_LAUNCH("final_topk", stream, final_topk_kernel<32>, tgrid, tblock, 0, ta);
+    PISA_LAUNCH("final_topk", stream, final_topk_kernel<32>, grid(topk_rows_per_wave<32>()), tblock, 0, ta);
   else
-    PISA_LAUNCH("final_topk", stream, final_topk_kernel<0>, tgrid, tblock, 0, ta);
+    PISA_LAUNCH("final_topk", stream, final_topk_kernel<0>, grid(topk_rows_per_wave<0>()), tblock, 0, ta);
   return hipGetLastError();
 }
 
