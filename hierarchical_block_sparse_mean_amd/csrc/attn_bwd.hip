@@ -32,7 +32,7 @@ namespace pisa {
 template <int D, int NKB>
 constexpr int bwd_waves() { return NKB >= 8 && D >= 128 ? 8 : 4; }
 constexpr int kBwdChunk = 256;                   // (query, slot) pairs per workgroup
-constexpr size_t kBwdBudget = (size_t)8 << 30;  // partial dQ rows per head chunk
+constexpr size_t kBwdBudget = (size_t)24 << 30;  // partial dQ rows per head chunk
 
 static size_t b256(size_t x) { return (x + 255) & ~(size_t)255; }
 

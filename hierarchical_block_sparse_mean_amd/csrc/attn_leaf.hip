@@ -48,7 +48,7 @@ constexpr int attn_waves() {
   while (nw > 1 && attn_lds_bytes<T, D, NKB>(nw) > kLdsPerCu) --nw;
   return nw;
 }
-constexpr size_t kAttnBudget = (size_t)8 << 30;  // partial buffers per head chunk
+constexpr size_t kAttnBudget = (size_t)24 << 30;  // partial buffers per head chunk
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
