@@ -261,10 +261,15 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
     }
     // partial record of (query, slot, head): column col holds rows 4g+i of
     // each d-block; stage the 16 x D tile in LDS, then store whole rows
+    // (the lane's 4 dims of a d-block are consecutive: one 8- or 16-byte store)
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store1<T>(&s_o[w][col][db * 16 + 4 * g + i], oacc[db][i]);
+    for (int db = 0; db < D / 16; ++db) {
+      T* dst = &s_o[w][col][db * 16 + 4 * g];
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(oacc[db][0], oacc[db][1]), pack_bf16x2(oacc[db][2], oacc[db][3])};
+      else
+        *reinterpret_cast<float4*>(dst) = float4{oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]};
+    }
     if (live && g == 0) {
       const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
       a.pm[rec] = m;
