@@ -30,12 +30,17 @@ namespace pisa {
 constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
 constexpr size_t kLdsPerCu = 160 * 1024;
 
+// V^T row pad (elements): rows 4 elements apart in bank offset, so the 8-byte
+// reads of 16 consecutive dims (rows) at one key offset fall in distinct
+// banks whether a pass serves 32 or 64 banks
+constexpr int kVtPad = 4;
+
 // LDS of a workgroup: the tile's K (row-major) and V^T, the waves' output
 // staging, the chunk's pair codes
 template <typename T, int D, int NKB>
 constexpr size_t attn_lds_bytes(int nw) {
   constexpr size_t e = 16 / sizeof(T);
-  return ((size_t)NKB * 16 * (D + e) + (size_t)D * (NKB * 16 + e) + (size_t)nw * 16 * (D + e)) * sizeof(T) +
+  return ((size_t)NKB * 16 * (D + e) + (size_t)D * (NKB * 16 + kVtPad) + (size_t)nw * 16 * (D + e)) * sizeof(T) +
          4 * (size_t)kAttnChunk;
 }
 // waves per workgroup: 12 for tiles of 8 key blocks (their K, V^T and the
@@ -135,7 +140,7 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
   constexpr int TQ = 16 / G;                   // queries per 16-column tile
   constexpr int CP = NKB * 16;                 // keys held (zero padded)
   constexpr int KP = D + 16 / (int)sizeof(T);  // K row pitch
-  constexpr int VP = CP + 16 / (int)sizeof(T); // V^T row pitch
+  constexpr int VP = CP + kVtPad;              // V^T row pitch
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
   T* s_vt = s_k + CP * KP;                   // [D][VP]
@@ -486,7 +491,7 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
       constexpr int D = decltype(dc)::value;
       constexpr int G = decltype(gc)::value;
       auto run = [&](auto kern, int nkb, int nw) -> hipError_t {
-        const size_t lds = ((size_t)nkb * 16 * (D + 16 / sizeof(T)) + (size_t)D * (nkb * 16 + 16 / sizeof(T))) *
+        const size_t lds = ((size_t)nkb * 16 * (D + 16 / sizeof(T)) + (size_t)D * (nkb * 16 + kVtPad)) *
                            sizeof(T);
         if (lds > 65536) {
           hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
