@@ -351,10 +351,10 @@ struct MergeArgs {
 // sibling pair when pairs were attended together), so each lane, which owns
 // 8 output dims of one head, issues the loads of its first SG slots' rows
 // before the slots' m and l (staged through LDS) have arrived; the rows are
-// then combined with weights exp(m - max m).
-template <typename T, int D, int G>
+// then combined with weights exp(m - max m).  SG: slots whose rows are loaded
+// together (K rounded up to 16 or 32 for 16-bit rows, half that for fp32).
+template <typename T, int D, int G, int SG>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  constexpr int SG = sizeof(T) == 2 ? 16 : 8;          // slots whose rows are loaded together
   constexpr int MLP = (32 * G + kWave - 1) / kWave;   // (m, l) entries per lane, at most
   __shared__ float s_m[4][32 * G], s_l[4][32 * G];
   __shared__ int32_t s_ok[4][32];
@@ -413,31 +413,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
     for (int s = 0; s < a.K; ++s)
       if (s_ok[w][s]) M = fmaxf(M, s_m[w][s * G + hh]);
     float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const Row8<T>* rows, int s0) {
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        const int s = s0 + u;
+        if (s < a.K && s_ok[w][s] && s_m[w][s * G + hh] != -INFINITY) {
+          const float wgt = __expf(s_m[w][s * G + hh] - M);
+          L += wgt * s_l[w][s * G + hh];
+          float v[8];
+          rows[u].get(v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+        }
+      }
+    };
     if (M != -INFINITY) {
-      for (int s0 = 0; s0 < a.K; s0 += SG) {
+      int s0 = 0;
+      if constexpr (ONE) {
+        consume(first, 0);
+        s0 = SG;
+      }
+      for (; s0 < a.K; s0 += SG) {
         Row8<T> rows[SG];
-        if constexpr (ONE) {
-          if (s0 == 0) {
-#pragma unroll
-            for (int u = 0; u < SG; ++u) rows[u] = first[u];
-          } else {
-            issue(e0, s0, rows);
-          }
-        } else {
-          issue(e0, s0, rows);
-        }
-#pragma unroll
-        for (int u = 0; u < SG; ++u) {
-          const int s = s0 + u;
-          if (s < a.K && s_ok[w][s] && s_m[w][s * G + hh] != -INFINITY) {
-            const float wgt = __expf(s_m[w][s * G + hh] - M);
-            L += wgt * s_l[w][s * G + hh];
-            float v[8];
-            rows[u].get(v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
-          }
-        }
+        issue(e0, s0, rows);
+        consume(rows, s0);
       }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -513,8 +512,12 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
       }
       if (e != hipSuccess) return e;
       const int64_t waves = heads * p.N;
-      PISA_LAUNCH("attn_merge", stream, (attn_merge_kernel<T, D, G>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                  ma);
+      const dim3 mgrid((unsigned)((waves + 3) / 4));
+      constexpr int sg = sizeof(T) == 2 ? 16 : 8;
+      if (p.K <= sg)
+        PISA_LAUNCH("attn_merge", stream, (attn_merge_kernel<T, D, G, sg>), mgrid, dim3(256), 0, ma);
+      else
+        PISA_LAUNCH("attn_merge", stream, (attn_merge_kernel<T, D, G, 2 * sg>), mgrid, dim3(256), 0, ma);
       return hipGetLastError();
     });
     if (err != hipSuccess) return err;
