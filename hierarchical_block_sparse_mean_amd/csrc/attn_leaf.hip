@@ -57,9 +57,18 @@ constexpr size_t kAttnBudget = (size_t)24 << 30;  // partial buffers per head ch
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks, and
-// not for fp32 rows of d = 128 (such a tile leaves LDS for two waves only)
-static bool attn_pairs(const Problem& p) { return p.C <= 64 && (p.dtype == 1 || p.D <= 64); }
+// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks; not
+// for fp32 rows of d = 128 (such a tile leaves LDS for two waves only), nor
+// where the level-2 blocks would push a head's clustering off its LDS
+// histogram (M_1 <= 16384 < M_1 + M_2: from about 700K to 1M tokens at
+// C = 64; measured 95 ms unpaired against 105 ms paired at 1M).  Beyond, both
+// take the global-atomic path and pairing pays again.
+static bool attn_pairs(const Problem& p) {
+  const int64_t M1 = level_rows(p.N, p.C, 1);
+  const bool leaves_in_lds = M1 <= kClusterLdsBins;
+  const bool pairs_in_lds = M1 + (M1 + 1) / 2 <= kClusterLdsBins;
+  return p.C <= 64 && (p.dtype == 1 || p.D <= 64) && (pairs_in_lds || !leaves_in_lds);
+}
 
 struct AttnLayout {
   int64_t heads;  // (b, h) heads per chunk

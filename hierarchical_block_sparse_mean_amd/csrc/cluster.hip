@@ -33,7 +33,7 @@
 namespace pisa {
 
 constexpr int kHistTile = 8192;     // entries per histogram tile
-constexpr int64_t kMaxBins = 16384; // LDS bins (64 KB)
+constexpr int64_t kMaxBins = kClusterLdsBins;
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -87,6 +87,9 @@ struct ClusterBufs {
   int32_t* pairs;
   int32_t* hist;
 };
+// Bins per head that the counting sort's LDS histogram holds (64 KB); a head
+// with more bins takes the global-atomic path
+constexpr int64_t kClusterLdsBins = 16384;
 // Bins per head of a clustering of N queries over M key blocks: query blocks
 // of 2^cluster_query_shift(N, M, max_bins) positions times M (see cluster.hip).
 // max_bins: the clustering's bin budget per head (query blocks are added
