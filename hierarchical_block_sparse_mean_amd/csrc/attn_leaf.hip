@@ -21,13 +21,17 @@
 // tile, so the query's rows are read once and one partial (under the slot of
 // the even leaf) is written for both; the merge recognises the odd leaf's
 // slot from idx and skips it.
-// Work is done in chunks of KV heads so the partial buffers stay bounded and
-// one chunk's queries stay cache-resident.
+// Work is done in chunks of KV heads so that the partial buffers stay within
+// a bound (24 GiB: all eight KV heads at once at 128K, two at a time at 256K).
 #include "kernels.h"
 
 namespace pisa {
 
-constexpr int kAttnChunk = 256;                   // (query, slot) pairs per workgroup
+// (query, slot) pairs per workgroup, at most: 512 for leaves of C <= 64 keys,
+// 1024 for longer ones (a longer chunk re-stages a leaf's K and V fewer
+// times; measured best per leaf size)
+constexpr int kAttnChunk = 1024;
+static int attn_chunk(const Problem& p) { return p.C > 64 ? 1024 : 512; }
 constexpr size_t kLdsPerCu = 160 * 1024;
 
 // V^T row pad (elements): rows 4 elements apart in bank offset, so the 8-byte
@@ -83,7 +87,7 @@ static AttnLayout attn_layout(const Problem& p) {
   L.Mk = L.M1 + (attn_pairs(p) ? (L.M1 + 1) / 2 : 0);
   L.Mb = cluster_bins(p.N, L.Mk, kAttnBins);
   const size_t per_head = (size_t)p.N * p.K * (4 + (size_t)p.G * (8 + p.D * osz)) + (size_t)L.Mb * 20 +
-                          (size_t)p.N * p.K / kAttnChunk * 4;
+                          (size_t)p.N * p.K / attn_chunk(p) * 4;
   const int64_t BH = (int64_t)p.B * p.Hkv;
   int64_t hmax = (int64_t)(kAttnBudget / per_head);
   if (hmax < 1) hmax = 1;
@@ -92,7 +96,7 @@ static AttnLayout attn_layout(const Problem& p) {
   L.heads = (BH + nchunks - 1) / nchunks;
   L.ncl = L.heads * L.Mb;
   L.slots = L.heads * (int64_t)p.N * p.K;
-  L.max_chunks = (L.slots + kAttnChunk - 1) / kAttnChunk + L.ncl;
+  L.max_chunks = (L.slots + attn_chunk(p) - 1) / attn_chunk(p) + L.ncl;
   size_t off = 0;
   L.off_counts = off;
   off = a256(off + 4 * (size_t)L.ncl);
@@ -134,6 +138,7 @@ struct AttnLeafArgs {
   void* po;    // [heads][N][K][G][D] (input dtype)
   int64_t ncl, M1, Mk, Mb, head0;
   int32_t N, Hq, Hkv, C, K;
+  int32_t chunk;  // pairs per work chunk (<= kAttnChunk)
   int32_t causal;
   int64_t cap;
   float scale;
@@ -165,9 +170,9 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
   if ((jk >= a.M1) != PAIRED) return;  // the other launch's cluster
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
-  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kAttnChunk;
+  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)a.chunk;
   const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
-  const int64_t p_end = p_begin + kAttnChunk < p_end_c ? p_begin + kAttnChunk : p_end_c;
+  const int64_t p_end = p_begin + a.chunk < p_end_c ? p_begin + a.chunk : p_end_c;
 
   const int C = PAIRED ? 2 * a.C : a.C;  // keys of the tile
   const int64_t key0 = (PAIRED ? jk - a.M1 : jk) * (int64_t)C;
@@ -187,7 +192,7 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
 #pragma unroll
     for (int e = 0; e < EPV; ++e) s_vt[(d + e) * VP + r] = ve[e];
   }
-  for (int i = threadIdx.x; i < kAttnChunk; i += blockDim.x)
+  for (int i = threadIdx.x; i < a.chunk; i += blockDim.x)
     s_pr[i] = p_begin + i < p_end ? a.pairs[p_begin + i] : -1;
   __syncthreads();
 
@@ -486,14 +491,14 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     const int64_t ncl = heads * L.Mb;
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
     hipError_t err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.Mk, kAttnBins,
-                                     kAttnChunk, cb, stream, pairs_on ? L.M1 : 0);
+                                     attn_chunk(p), cb, stream, pairs_on ? L.M1 : 0);
     if (err != hipSuccess) return err;
     err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
     if (err != hipSuccess) return err;
     AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, chunk_map, pairs, pm, pl, po, ncl, L.M1, L.Mk, L.Mb, head0,
-                    p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
+                    p.N, p.Hq, p.Hkv, p.C, p.K, attn_chunk(p), p.causal ? 1 : 0, p.cap, p.scale};
     MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K, pairs_on ? 1 : 0};
-    const int64_t max_chunks = (entries + kAttnChunk - 1) / kAttnChunk + ncl;
+    const int64_t max_chunks = (entries + attn_chunk(p) - 1) / attn_chunk(p) + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value;
