@@ -22,7 +22,7 @@
 namespace pisa {
 
 constexpr int kS2Waves = 4;
-constexpr int kS2Chunk = 256;  // queries of one cluster per workgroup
+constexpr int kS2Chunk = 1024;  // pairs of one cluster per workgroup (its key tile is staged once per chunk)
 constexpr int kTopkWaves = 4;
 
 // ---- workspace layout -------------------------------------------------------
