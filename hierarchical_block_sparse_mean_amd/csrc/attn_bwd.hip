@@ -31,7 +31,13 @@ namespace pisa {
 // 8 waves in flight; 4 otherwise
 template <int D, int NKB>
 constexpr int bwd_waves() { return NKB >= 8 && D >= 128 ? 8 : 4; }
-constexpr int kBwdChunk = 256;                   // (query, slot) pairs per workgroup
+// (query, slot) pairs per workgroup: a chunk stages its leaf's K, V and K^T
+// once and adds its dK, dV sums with atomics once; 1024 for leaves of more
+// than 64 keys (8 key blocks), 256 otherwise, where the pair codes' LDS would
+// cost the second resident workgroup (measured best per leaf size)
+template <int NKB>
+constexpr int bwd_chunk_max() { return NKB >= 8 ? 1024 : 256; }
+static int bwd_chunk(const Problem& p) { return p.C > 64 ? 1024 : 256; }
 constexpr size_t kBwdBudget = (size_t)24 << 30;  // partial dQ rows per head chunk
 
 static size_t b256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -56,7 +62,7 @@ static BwdLayout bwd_layout(const Problem& p) {
   L.heads = (BH + nchunks - 1) / nchunks;
   L.ncl = L.heads * L.Mb;
   L.slots = L.heads * (int64_t)p.N * p.K;
-  L.max_chunks = (L.slots + kBwdChunk - 1) / kBwdChunk + L.ncl;
+  L.max_chunks = (L.slots + bwd_chunk(p) - 1) / bwd_chunk(p) + L.ncl;
   size_t off = 0;
   L.off_counts = off;
   off = b256(off + 4 * (size_t)L.ncl);
@@ -142,6 +148,7 @@ struct BwdArgs {
   float* dv_acc;
   int64_t ncl, M1, Mb, head0;
   int32_t N, Hq, Hkv, C, K;
+  int32_t chunk;  // pairs per work chunk
   int32_t causal;
   int64_t cap;
   float scale;
@@ -178,7 +185,7 @@ __global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void 
   __shared__ __align__(16) PT s_ds[CP][PPITCH];
   __shared__ float s_lse[NC], s_rd[NC];
   __shared__ int32_t s_pr[NC];
-  __shared__ int32_t s_cpr[kBwdChunk];  // the chunk's pair codes
+  __shared__ int32_t s_cpr[bwd_chunk_max<NKB>()];  // the chunk's pair codes
 
   const int64_t chunk = blockIdx.x;
   if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
@@ -187,9 +194,9 @@ __global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void 
   const int64_t j = c % a.M1;
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
-  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kBwdChunk;
+  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)a.chunk;
   const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
-  const int64_t p_end = p_begin + kBwdChunk < p_end_c ? p_begin + kBwdChunk : p_end_c;
+  const int64_t p_end = p_begin + a.chunk < p_end_c ? p_begin + a.chunk : p_end_c;
 
   const int64_t key0 = j * (int64_t)a.C;
   const int nkeys = (int)((a.N - key0) < a.C ? (a.N - key0) : a.C);
@@ -208,7 +215,8 @@ __global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void 
 #pragma unroll
     for (int e = 0; e < EPV; ++e) s_kt[(d + e) * TP + r] = ke[e];
   }
-  for (int i = threadIdx.x; i < kBwdChunk; i += blockDim.x) s_cpr[i] = p_begin + i < p_end ? a.pairs[p_begin + i] : -1;
+  for (int i = threadIdx.x; i < bwd_chunk_max<NKB>(); i += blockDim.x)
+    s_cpr[i] = p_begin + i < p_end ? a.pairs[p_begin + i] : -1;
   __syncthreads();
   const int n = (int)(p_end - p_begin);
 
@@ -510,14 +518,14 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
     const int64_t entries = heads * p.N * p.K;
     const int64_t ncl = heads * L.Mb;
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
-    err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, kBwdChunk, cb, stream);
+    err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, bwd_chunk(p), cb, stream);
     if (err != hipSuccess) return err;
     err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
     if (err != hipSuccess) return err;
     BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, chunk_map, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1, L.Mb,
-               head0, p.N, p.Hq, p.Hkv, p.C, p.K, p.causal ? 1 : 0, p.cap, p.scale};
+               head0, p.N, p.Hq, p.Hkv, p.C, p.K, bwd_chunk(p), p.causal ? 1 : 0, p.cap, p.scale};
     BwdMergeArgs ma{idx, dq_part, dq, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
-    const int64_t max_chunks = (entries + kBwdChunk - 1) / kBwdChunk + ncl;
+    const int64_t max_chunks = (entries + bwd_chunk(p) - 1) / bwd_chunk(p) + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value;
