@@ -141,7 +141,11 @@ pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, con
  * leaves idx[b][h'/G_Q][t][*] (entries < 0 or >= ceil(N/C) ignored; keys
  * i > t masked when causal).  o has the input dtype; lse (may be NULL) is float [B][Hq][N], the
  * log-sum-exp of the attended logits.  A query with no attended key gets
- * o = 0 and lse = -inf.  ws: at least pisa_attn_workspace_bytes(p) bytes.   */
+ * o = 0 and lse = -inf.  ws: at least pisa_attn_workspace_bytes(p) bytes,
+ * 256-byte aligned (query-major: 256).  For the leaf-major schedule it holds
+ * the partial outputs of a chunk of KV heads, B*Hkv*N*K*G*(D*elem + 8) bytes
+ * capped near 24 GiB (about 18 GB for N = 131072, K = 16, 8 KV heads of
+ * G = 4, D = 128, bf16), plus the clusters.                                 */
 size_t pisa_attn_workspace_bytes(const pisa_problem* p);
 pisa_status pisa_sparse_attn(const pisa_problem* p, const void* q, const void* k, const void* v,
                              const int32_t* idx, void* o, float* lse, void* ws, size_t ws_bytes,
