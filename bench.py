@@ -666,7 +666,7 @@ def io_main(args) -> int:
             del pyr, ws, idx, score
         same = float((out["two_stage"]["idx"] == out["one_stage"]["idx"]).all(-1).mean())
         same_qt = bool(np.array_equal(out["two_stage"]["idx"], out["two_stage_q16"]["idx"]))
-        d, C, qt, chunk = w.D, w.C, 4, 256
+        d, C, qt, chunk = w.D, w.C, 4, 1024
         rows.append({
             "G_Q": G, "Hkv": hkv,
             "two_stage_ms": round(out["two_stage"]["ms"], 4), "one_stage_ms": round(out["one_stage"]["ms"], 4),
