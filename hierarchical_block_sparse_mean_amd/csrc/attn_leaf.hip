@@ -207,7 +207,7 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
     const int64_t tq = pr >= 0 ? (pr >> 5) : 0;
     const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + tq) * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
+    for (int s = 0; s < NS; ++s) f[s].load(qrow + 32 * s + 8 * g);
   };
   // one tile of 16 / G_Q pairs; MASK: some column of the chunk sees fewer
   // keys than the tile holds (causal diagonal leaf, last leaf, zero padding)
@@ -228,7 +228,7 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         Frag<T> fk;
-        fk.load(sk + (kb * 16 + col) * KP + g * (D / 4) + 8 * s);
+        fk.load(sk + (kb * 16 + col) * KP + 32 * s + 8 * g);
         acc[kb] = mma(fk, fq[s], acc[kb]);
       }
     }

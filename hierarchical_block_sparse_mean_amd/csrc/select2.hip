@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_ker
     const int64_t tq = prq >= 0 ? (prq >> 5) : 0;
     const T* qrow = qb + (((int64_t)b * a.Hq + h * G + hh) * a.N + tq) * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) f[s].load(qrow + g * (D / 4) + 8 * s);
+    for (int s = 0; s < NS; ++s) f[s].load(qrow + 32 * s + 8 * g);
   };
   // keys key_local < limit count for the column's query (t >= key0 + key_local)
   auto limit = [&](int32_t pr) -> int {
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_ker
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             Frag<T> fk;
-            fk.load(sk + ((leaf * CB0 + cb) * 16 + col) * PITCH + g * (D / 4) + 8 * s);
+            fk.load(sk + ((leaf * CB0 + cb) * 16 + col) * PITCH + 32 * s + 8 * g);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) acc[tt][cb] = mma(fk, fq[tt][s], acc[tt][cb]);
           }
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_ker
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           Frag<T> fk;
-          fk.load(sk + (cb * 16 + col) * PITCH + g * (D / 4) + 8 * s);
+          fk.load(sk + (cb * 16 + col) * PITCH + 32 * s + 8 * g);
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) acc[tt][cb] = mma(fk, fq[tt][s], acc[tt][cb]);
         }
