@@ -2,7 +2,8 @@
 on the same seeded inputs.  Sizes are ones the oracle finishes in seconds yet
 span several tiles and ragged tails; edge cases: N <= C (one level), K >= M1
 (dense attention), K >= M1/2 (every leaf a candidate), C not a multiple of 16,
-every supported GQA group size, both select schedules, decode level growth."""
+every supported GQA group size, both select schedules, decode level growth,
+K = 16 over an odd number of rows."""
 from __future__ import annotations
 
 import math
@@ -35,6 +36,9 @@ CASES = {
     "bf16_g16_c32": I.Workload("bf16_g16_c32", 1, 1500, 16, 1, 128, 32, 4, "bf16", True, seed=16),
     "bf16_c128_k32": I.Workload("bf16_c128_k32", 1, 8292, 8, 2, 128, 128, 32, "bf16", True, "shared_spans",
                                 seed=17),
+    # K = 16 over an odd number of (b, h, t) rows: the final top-K takes two
+    # rows per wave, so the last wave holds one
+    "f32_k16_odd_rows": I.Workload("f32_k16_odd_rows", 1, 1001, 4, 1, 64, 32, 16, "f32", True, seed=18),
 }
 # positions checked against the oracle (None = all)
 SAMPLED = {"bf16_c128_k32": np.unique(np.concatenate([np.arange(0, 300), np.arange(8292 - 200, 8292),
