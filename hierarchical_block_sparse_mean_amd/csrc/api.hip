@@ -100,6 +100,10 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
   out->L = pisa::num_levels(p->N, p->C);
   out->q_tile = p->q_tile ? p->q_tile : (two_tiles ? 32 / G : 16 / G);
   out->geo = make_geom(cap, p->C);
+  // kernels address the rows of one head's summaries with 32-bit offsets
+  if (out->geo.rows * (int64_t)p->D > INT32_MAX)
+    return fail(PISA_ERR_UNSUPPORTED, "summary rows per head (%lld) x D (%d) must be < 2^31: cap / C is too large",
+                (long long)out->geo.rows, p->D);
   return ok();
 }
 

@@ -34,7 +34,10 @@
  *     pisa_last_error() then describes the problem (thread-local string).
  *   - Supported in this version: g == 2 (the page's merge factor), D in
  *     {64, 128}, G_Q in {1, 2, 4, 8, 16}, 1 <= K <= 32, 1 <= C <= 128,
- *     N < 2^26, B * Hkv * N * K < 2^31.
+ *     N < 2^26, B * Hkv * N * K < 2^31, and the summary rows of one head
+ *     times D below 2^31 (rows = sum over levels of ceil(cap / (C 2^(l-1))),
+ *     about 2 cap / C: cap / C below about 8.4M at D = 128), so that every
+ *     element offset inside a head's summaries fits 32 bits.
  */
 #ifndef PISA_H_
 #define PISA_H_

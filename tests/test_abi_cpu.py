@@ -70,6 +70,9 @@ FAKE = 4096  # a non-NULL address; validation must reject before using it
     (dict(K=33), pisa.PISA_ERR_UNSUPPORTED),
     (dict(C=256), pisa.PISA_ERR_UNSUPPORTED),
     (dict(N=1 << 26, K=1), pisa.PISA_ERR_UNSUPPORTED),
+    # a head's summary rows x D must stay below 2^31 (32-bit offsets in a head)
+    (dict(N=1 << 25, C=1, K=1), pisa.PISA_ERR_UNSUPPORTED),
+    (dict(cap=(1 << 31) - 1), pisa.PISA_ERR_UNSUPPORTED),
     (dict(cap=100), pisa.PISA_ERR_INVALID_ARG),
     (dict(q_tile=3), pisa.PISA_ERR_UNSUPPORTED),
     (dict(q_tile=8), pisa.PISA_ERR_UNSUPPORTED),  # two tiles per read: bf16 only
@@ -85,6 +88,22 @@ def test_invalid_problem_rejected(lib, kw, status):
     assert lib.pisa_last_error()
     assert lib.pisa_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == status
     assert lib.pisa_pyramid_bytes(ctypes.byref(p)) == 0
+
+
+def test_summary_offset_bound_boundary(lib):
+    """Shapes whose per-head summary elements reach 2^31 are rejected, and
+    the largest accepted cap at C = 64, D = 64 sits just below that."""
+    def rows(cap, C):
+        return sum(oracle.level_rows(cap, C, l) for l in range(1, oracle.levels(cap, C) + 1))
+    ok_cap = (1 << 30)  # rows = 2^25 - 1, x 64 = 2^31 - 64
+    assert rows(ok_cap, 64) * 64 < 2 ** 31
+    p = _p(cap=ok_cap).c()
+    assert lib.pisa_pyramid_bytes(ctypes.byref(p)) > 0, lib.pisa_last_error()
+    bad_cap = ok_cap + 64 * 2 ** 6  # 64 more leaves: 146 more rows, past the bound
+    assert rows(bad_cap, 64) * 64 >= 2 ** 31
+    p = _p(cap=bad_cap).c()
+    assert lib.pisa_pyramid_bytes(ctypes.byref(p)) == 0
+    assert "2^31" in lib.pisa_last_error().decode()
 
 
 @pytest.mark.parametrize("kw", [dict(q_tile=4), dict(q_tile=8, dtype="bf16"), dict(q_tile=0, dtype="bf16"),
