@@ -1,0 +1,111 @@
+"""GPU path on exact ties, pinned by closed forms rather than by the oracle.
+
+With every query zero, every logit is exactly 0 on both the fp16 stage-1
+products and the bf16 / fp32 leaf and attention products, so
+  * each block's routing score is G_Q log(#valid children) and each leaf's
+    score G_Q log(#valid keys): every full block ties with every other;
+  * the tie rule (score descending, then the lower block index) then keeps,
+    at every level, the lowest-index full blocks, and the returned leaves of
+    query t are the first min(K, #valid leaves of t), ascending, -1 padded;
+  * attention weights every valid key of those leaves equally: o is the mean
+    of their values and lse the log of their number.
+The parity tests exempt near-ties (gaps below 1e-3), so the tie rule itself
+is checked only here.  Both selection schedules and both attention schedules
+are run; the inputs are ragged (partial last leaf and blocks with one
+child)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import ATTN_TOL, log, to_dev, to_host_f64
+from hierarchical_block_sparse_mean_amd import inputs as I
+from hierarchical_block_sparse_mean_amd import pisa
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "bf16_g4_c64_k8_causal": I.Workload("ties_bf16_g4", 1, 1500, 8, 2, 128, 64, 8, "bf16", True, seed=71),
+    "bf16_g16_c32_k4_b2": I.Workload("ties_bf16_g16", 2, 1100, 16, 1, 64, 32, 4, "bf16", False, seed=72),
+    "f32_g2_c48_k16_causal": I.Workload("ties_f32_g2", 1, 900, 4, 2, 64, 48, 16, "f32", True, seed=73),
+}
+
+
+def expected(w: I.Workload):
+    """idx [N][K] and per-slot key counts [N][K] of the closed form (the same
+    for every batch and KV head)."""
+    M1 = -(-w.N // w.C)
+    idx = np.full((w.N, w.K), -1, np.int64)
+    cnt = np.zeros((w.N, w.K), np.int64)
+    for t in range(w.N):
+        nvalid = min(M1, t // w.C + 1) if w.causal else M1
+        last = t + 1 if w.causal else w.N  # keys < last are valid
+        for s in range(min(w.K, nvalid)):
+            idx[t, s] = s
+            cnt[t, s] = min((s + 1) * w.C, last) - s * w.C
+    return idx, cnt
+
+
+@pytest.mark.parametrize("algo", [pisa.SELECT_AUTO, pisa.SELECT_FUSED], ids=["two_stage", "fused"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_zero_queries_select_lowest_leaves(name, algo):
+    w = CASES[name]
+    log(f"[test_zero_queries_select_lowest_leaves {name} algo={algo}]")
+    data = I.generate(w, with_v=False)
+    q = np.zeros_like(data["q"])  # +0.0 in fp32 and in bf16 bits
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype, select_algo=algo)
+    k = to_dev(data["k"])
+    pyr = pisa.build_pyramid(p, k)
+    idx, score = pisa.select(p, to_dev(q), k, pyr)
+    torch.cuda.synchronize()
+    e_idx, e_cnt = expected(w)
+    got = idx.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            bad = np.argwhere((got[b, h] != e_idx).any(axis=-1))
+            assert bad.size == 0, f"t={int(bad[0][0])}: got {got[b, h, bad[0][0]].tolist()} " \
+                                  f"want {e_idx[bad[0][0]].tolist()}"
+    if algo == pisa.SELECT_AUTO:
+        g = score.cpu().numpy().astype(np.float64)
+        want = np.where(e_idx >= 0, w.gq * np.log(np.maximum(e_cnt, 1)), -np.inf)
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                assert np.array_equal(np.isneginf(g[b, h]), e_idx < 0)
+                m = e_idx >= 0
+                err = np.abs(g[b, h][m] - want[m]).max()
+                assert err <= 1e-5 * max(1.0, np.abs(want[m]).max()), err
+
+
+@pytest.mark.parametrize("attn", [pisa.ATTN_LEAF_MAJOR, pisa.ATTN_QUERY_MAJOR], ids=["leaf_major", "query_major"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_zero_queries_attention_is_mean(name, attn):
+    w = CASES[name]
+    log(f"[test_zero_queries_attention_is_mean {name} attn={attn}]")
+    data = I.generate(w)
+    q = np.zeros_like(data["q"])
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype)
+    p.attn_algo = attn
+    e_idx, e_cnt = expected(w)
+    idx = np.broadcast_to(e_idx.astype(np.int32), (w.B, w.Hkv, w.N, w.K))
+    o, lse = pisa.sparse_attn(p, to_dev(q), to_dev(data["k"]), to_dev(data["v"]), to_dev(np.ascontiguousarray(idx)))
+    torch.cuda.synchronize()
+    v = I.widen(data["v"])  # [B][Hkv][N][D] float64
+    got_o = to_host_f64(o)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    n_keys = e_cnt.sum(axis=1)  # valid keys per query
+    # mean of the values of the keys [0, n_keys[t]) (the kept leaves are the
+    # first ones and, under the causal mask, end at t): prefix sums over keys
+    csum = np.cumsum(v, axis=2)
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = csum[b, h, n_keys - 1] / n_keys[:, None]  # [N][D]
+            for g in range(w.gq):
+                worst = max(worst, float(np.abs(got_o[b, h * w.gq + g] - ref).max()))
+                lerr = np.abs(got_lse[b, h * w.gq + g] - np.log(n_keys)).max()
+                assert lerr <= 1e-4 * max(1.0, math.log(n_keys.max())), lerr
+    assert worst <= ATTN_TOL[w.dtype], worst
+    log(f"  attention max-abs err {worst:.3g}")
