@@ -109,3 +109,55 @@ def test_zero_queries_attention_is_mean(name, attn):
                 assert lerr <= 1e-4 * max(1.0, math.log(n_keys.max())), lerr
     assert worst <= ATTN_TOL[w.dtype], worst
     log(f"  attention max-abs err {worst:.3g}")
+
+
+DECODE_CASES = {
+    # n0 = 1021 -> 1024: the new tokens fill the last leaf; K = 4 of 16 leaves
+    "bf16_g4_c64_k4": I.Workload("ties_dec_bf16", 3, 1021, 8, 2, 128, 64, 4, "bf16", True, seed=74, steps=3),
+    # K = 16 of 7 leaves: every leaf kept, the last one partial
+    "f32_g1_c48_k16": I.Workload("ties_dec_f32", 2, 300, 2, 2, 64, 48, 16, "f32", True, seed=75, steps=2),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_zero_queries_decode(name):
+    """The fused decode step on zero queries: the first min(K, leaves) leaves,
+    scores G_Q log(#keys), o the mean of their values (new token included)."""
+    w = DECODE_CASES[name]
+    log(f"[test_zero_queries_decode {name}]")
+    cache = I.decode_cache(w)
+    cap = cache["cap"]
+    dp = pisa.DecodeProblem(w.B, cap, w.Hq, w.Hkv, w.D, w.C, w.K, dtype=w.dtype)
+    kc, vc = to_dev(cache["k"]), to_dev(cache["v"])
+    pp = dp.prefill_problem(w.N)
+    pyr = pisa.build_pyramid(pp, kc, pisa.alloc_pyramid(pp))
+    length = torch.full((w.B,), w.N, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    v_host = I.widen(cache["v"]).copy()
+    for step in range(w.steps):
+        n = w.N + step  # position of the new token; keys 0..n are valid
+        tok = I.decode_token(w, step)
+        q0 = np.zeros_like(tok["q"])
+        idx = torch.empty((w.B, w.Hkv, w.K), dtype=torch.int32, device="cuda")
+        score = torch.empty((w.B, w.Hkv, w.K), dtype=torch.float32, device="cuda")
+        o, _, _ = pisa.decode_step(dp, kc, vc, pyr, length, to_dev(q0), to_dev(tok["k"]), to_dev(tok["v"]),
+                                   idx=idx, score=score, err=err)
+        torch.cuda.synchronize()
+        v_host[:, :, n] = I.widen(tok["v"])
+        M1 = n // w.C + 1
+        keep = min(w.K, M1)
+        e_idx = np.array([j if j < keep else -1 for j in range(w.K)])
+        cnt = np.array([min((j + 1) * w.C, n + 1) - j * w.C if j < keep else 0 for j in range(w.K)])
+        got = idx.cpu().numpy()
+        assert (got == e_idx).all(), f"step {step}: got {got.reshape(-1, w.K)[0].tolist()} want {e_idx.tolist()}"
+        g = score.cpu().numpy().astype(np.float64)
+        want = w.gq * np.log(np.maximum(cnt, 1))
+        m = e_idx >= 0
+        assert np.isneginf(g[..., ~m]).all()
+        assert np.abs(g[..., m] - want[m]).max() <= 1e-5 * max(1.0, np.abs(want[m]).max())
+        nk = int(cnt.sum())
+        ref = v_host[:, :, :nk].mean(axis=2)  # [B][Hkv][D]
+        got_o = to_host_f64(o).reshape(w.B, w.Hkv, w.gq, w.D)
+        err_o = np.abs(got_o - ref[:, :, None, :]).max()
+        assert err_o <= ATTN_TOL[w.dtype], f"step {step}: attention error {err_o:.3g}"
+    assert int(err.item()) == 0
