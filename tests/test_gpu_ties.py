@@ -10,9 +10,10 @@ products and the bf16 / fp32 leaf and attention products, so
   * attention weights every valid key of those leaves equally: o is the mean
     of their values and lse the log of their number.
 The parity tests exempt near-ties (gaps below 1e-3), so the tie rule itself
-is checked only here.  Both selection schedules and both attention schedules
-are run; the inputs are ragged (partial last leaf and blocks with one
-child)."""
+is checked only here.  Both selection schedules, both attention schedules,
+the fused decode step and the attention backward (whose dK vanishes and
+whose dV and dQ reduce to sums over the uniform weights) are run; the inputs
+are ragged (partial last leaf and blocks with one child)."""
 from __future__ import annotations
 
 import math
@@ -161,3 +162,55 @@ def test_zero_queries_decode(name):
         err_o = np.abs(got_o - ref[:, :, None, :]).max()
         assert err_o <= ATTN_TOL[w.dtype], f"step {step}: attention error {err_o:.3g}"
     assert int(err.item()) == 0
+
+
+BWD_CASES = {
+    "f32_g2_c48_k4_causal": I.Workload("ties_bwd_f32", 1, 900, 4, 2, 64, 48, 4, "f32", True, seed=76),
+    "bf16_g4_c32_k4_b2": I.Workload("ties_bwd_bf16", 2, 1100, 8, 2, 128, 32, 4, "bf16", False, seed=77),
+}
+BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_zero_queries_backward(name):
+    """Backward of sum(dO . o) on zero queries over the first leaves: every
+    probability is 1/n_t, so dK = scale * sum_t dS q_t is exactly zero,
+    dV_i = sum over the group's heads and the queries t with i < n_t of
+    dO_t / n_t, and dQ_t = scale / n_t * sum_{i < n_t} (dO_t.v_i - dO_t.o_t) k_i."""
+    w = BWD_CASES[name]
+    log(f"[test_zero_queries_backward {name}]")
+    data = I.generate(w)
+    q = np.zeros_like(data["q"])
+    dout = I.normal(w.seed, 11, w.B * w.Hq * w.N * w.D, dtype=w.dtype).reshape(w.B, w.Hq, w.N, w.D)
+    p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal, dtype=w.dtype)
+    e_idx, e_cnt = expected(w)
+    idx = to_dev(np.ascontiguousarray(np.broadcast_to(e_idx.astype(np.int32), (w.B, w.Hkv, w.N, w.K))))
+    qd, kd, vd, gd = (to_dev(x) for x in (q, data["k"], data["v"], dout))
+    o, lse = pisa.sparse_attn(p, qd, kd, vd, idx)
+    dq, dk, dv = pisa.sparse_attn_backward(p, qd, kd, vd, idx, o, lse, gd)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(w.D)
+    k64, v64, g64 = I.widen(data["k"]), I.widen(data["v"]), I.widen(dout)
+    n_t = e_cnt.sum(axis=1)  # keys [0, n_t) for query t
+    r_dv = np.zeros_like(v64)
+    r_dq = np.zeros_like(g64)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for gg in range(w.gq):
+                hq = h * w.gq + gg
+                # dV: dO_t / n_t added to keys [0, n_t), by sums over the end n_t
+                ends = np.zeros((w.N + 1, w.D))
+                np.add.at(ends, n_t, g64[b, hq] / n_t[:, None])
+                r_dv[b, h] += np.cumsum(ends[::-1], axis=0)[::-1][1:]
+                for t in range(w.N):
+                    kk, vv = k64[b, h, : n_t[t]], v64[b, h, : n_t[t]]
+                    o_t = vv.mean(axis=0)
+                    ds = vv @ g64[b, hq, t] - g64[b, hq, t] @ o_t
+                    r_dq[b, hq, t] = scale / n_t[t] * (ds @ kk)
+    got_dk = to_host_f64(dk)
+    assert (got_dk == 0.0).all(), f"dk not zero: max |dk| {np.abs(got_dk).max():.3g}"
+    for label, got, ref in (("dq", dq, r_dq), ("dv", dv, r_dv)):
+        err = np.abs(to_host_f64(got) - ref).max()
+        lim = BWD_TOL[w.dtype] * max(1.0, np.abs(ref).max())
+        log(f"  {label}: max err {err:.3g} (limit {lim:.3g})")
+        assert err <= lim, f"{name} {label}: {err} > {lim}"
