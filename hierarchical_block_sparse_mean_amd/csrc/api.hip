@@ -199,7 +199,12 @@ const char* pisa_version(void) { return "pisa-mi355x 0.1 (gfx950)"; }
 int32_t pisa_levels(int64_t n, int32_t C) { return (n < 1 || C < 1) ? 0 : pisa::num_levels(n, C); }
 
 int64_t pisa_level_rows(int64_t n, int32_t C, int32_t l) {
-  return (n < 1 || C < 1 || l < 1 || l > 62) ? 0 : pisa::level_rows(n, C, l);
+  if (n < 1 || C < 1 || l < 1 || l > 62) return 0;
+  // a block spans C 2^(l-1) tokens, which can exceed 64 bits for levels far
+  // above the top one (such a block holds all n tokens)
+  const unsigned __int128 span = (unsigned __int128)C << (l - 1);
+  const unsigned __int128 nn = (unsigned __int128)n;
+  return span >= nn ? 1 : (int64_t)((nn + span - 1) / span);
 }
 
 int64_t pisa_level_offset(int64_t cap, int32_t C, int32_t l) {

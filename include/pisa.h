@@ -114,7 +114,9 @@ typedef struct {
  * its children's summaries, the mean-pooling equation taken literally).     */
 size_t pisa_pyramid_bytes(const pisa_problem* p);
 int32_t pisa_levels(int64_t n, int32_t C);                 /* L(n)            */
-int64_t pisa_level_rows(int64_t n, int32_t C, int32_t l);  /* M_l(n)          */
+int64_t pisa_level_rows(int64_t n, int32_t C, int32_t l);  /* M_l(n) for 1 <= l <= 62
+                                                              (1 above L(n)); 0 for
+                                                              arguments out of range */
 int64_t pisa_level_offset(int64_t cap, int32_t C, int32_t l); /* first row    */
 
 /* Builds levels 1..L(N) of every (b, h) from k[b][h][0..N) (row stride cap).

@@ -50,6 +50,15 @@ def test_geometry_matches_oracle(lib, n, C):
     assert lib.pisa_level_offset(n, C, L + 1) == -1
 
 
+def test_level_rows_far_above_the_top(lib):
+    """Blocks of C 2^(l-1) tokens beyond 64 bits: one row, no overflow."""
+    assert lib.pisa_level_rows(1000, 128, 62) == 1
+    assert lib.pisa_level_rows(1000, 2 ** 31 - 1, 40) == 1
+    assert lib.pisa_level_rows(2 ** 62, 1, 62) == 2
+    assert lib.pisa_level_rows(2 ** 62 + 1, 1, 62) == 3
+    assert lib.pisa_level_rows(1000, 64, 63) == 0  # beyond the documented range
+
+
 def _p(**kw):
     base = dict(B=1, N=1024, Hq=4, Hkv=1, D=64, C=64, K=4, causal=False, dtype="f32")
     base.update(kw)
