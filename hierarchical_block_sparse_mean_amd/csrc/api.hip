@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -38,6 +39,15 @@ pisa_status hip_status(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// product of non-negative int32 factors, exact (at most 2^124)
+__int128 prod(std::initializer_list<int64_t> f) {
+  __int128 r = 1;
+  for (int64_t x : f) r *= x;
+  return r;
+}
+// tensors far beyond any device memory: every element offset fits int64 below
+constexpr int64_t kMaxTensorElems = (int64_t)1 << 46;
 
 bool supported_group(int32_t G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
 
@@ -82,8 +92,10 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
     return fail(PISA_ERR_UNSUPPORTED, "q_tile must be 0, 16/G_Q = %d%s (got %d)", 16 / G,
                 two_tiles ? " or 32/G_Q" : "", p->q_tile);
   const int64_t cap = p->cap ? p->cap : p->N;
-  if ((int64_t)p->B * p->Hkv * p->N * p->K > INT32_MAX || (int64_t)p->N * p->K > INT32_MAX)
-    return fail(PISA_ERR_UNSUPPORTED, "B*Hkv*N*K exceeds 2^31-1");
+  if (prod({p->B, p->Hkv, p->N, p->K}) > INT32_MAX) return fail(PISA_ERR_UNSUPPORTED, "B*Hkv*N*K exceeds 2^31-1");
+  // (q and o stay below 2^42 elements by the bound above)
+  if (prod({p->B, p->Hkv, cap, p->D}) >= kMaxTensorElems)
+    return fail(PISA_ERR_UNSUPPORTED, "k and v (B*Hkv*cap*D) would exceed 2^46 elements");
   if (p->N >= (1 << 26)) return fail(PISA_ERR_UNSUPPORTED, "N must be < 2^26 (got %d)", p->N);
   out->B = p->B;
   out->N = p->N;
@@ -355,6 +367,8 @@ pisa_status pisa_decode_step(const pisa_decode_problem* p, void* k_cache, void* 
   if (!supported_group(G)) return fail(PISA_ERR_UNSUPPORTED, "G_Q = Hq/Hkv must be 1, 2, 4, 8 or 16 (got %d)", G);
   if (p->K > 32) return fail(PISA_ERR_UNSUPPORTED, "K must be <= 32 (got %d)", p->K);
   if (p->C > 128) return fail(PISA_ERR_UNSUPPORTED, "C must be <= 128 (got %d)", p->C);
+  if (prod({p->S, p->Hkv, p->cap, p->D}) >= kMaxTensorElems || prod({p->S, p->Hq, p->D}) >= kMaxTensorElems)
+    return fail(PISA_ERR_UNSUPPORTED, "the caches would exceed 2^46 elements");
   if (k_cache == nullptr || v_cache == nullptr || pyr == nullptr || len == nullptr || q_new == nullptr ||
       k_new == nullptr || v_new == nullptr || o == nullptr)
     return fail(PISA_ERR_INVALID_ARG, "k_cache, v_cache, pyr, len, q_new, k_new, v_new and o must be non-NULL");

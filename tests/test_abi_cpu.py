@@ -82,6 +82,10 @@ FAKE = 4096  # a non-NULL address; validation must reject before using it
     # a head's summary rows x D must stay below 2^31 (32-bit offsets in a head)
     (dict(N=1 << 25, C=1, K=1), pisa.PISA_ERR_UNSUPPORTED),
     (dict(cap=(1 << 31) - 1), pisa.PISA_ERR_UNSUPPORTED),
+    # B*Hkv*N*K far beyond 64 bits (a plain int64 product would wrap negative)
+    (dict(B=2 ** 31 - 1, Hq=2 ** 30, Hkv=2 ** 30, N=2 ** 25, K=32), pisa.PISA_ERR_UNSUPPORTED),
+    # k/v beyond 2^46 elements through cap, with B*Hkv*N*K within 2^31
+    (dict(B=2 ** 16, Hq=2 ** 10, Hkv=2 ** 10, N=1, K=1, C=128, cap=2 ** 30), pisa.PISA_ERR_UNSUPPORTED),
     (dict(cap=100), pisa.PISA_ERR_INVALID_ARG),
     (dict(q_tile=3), pisa.PISA_ERR_UNSUPPORTED),
     (dict(q_tile=8), pisa.PISA_ERR_UNSUPPORTED),  # two tiles per read: bf16 only
@@ -162,6 +166,11 @@ def test_decode_validation(lib):
     bad = pisa.DecodeProblem(S=2, cap=100, Hq=4, Hkv=1, D=64, C=64, K=4, dtype="f32").c()
     assert lib.pisa_decode_step(ctypes.byref(bad), FAKE, None, *([FAKE] * 5), FAKE, None, None, None, None) == \
         pisa.PISA_ERR_INVALID_ARG
+    # caches beyond 2^46 elements (S*Hkv*cap*D, a product past 64 bits)
+    big = pisa.DecodeProblem(S=2 ** 31 - 1, cap=2 ** 31 - 1, Hq=2 ** 30, Hkv=2 ** 30, D=128, C=64, K=4,
+                             dtype="bf16").c()
+    assert lib.pisa_decode_step(ctypes.byref(big), *args, FAKE, None, None, None, None) == pisa.PISA_ERR_UNSUPPORTED
+    assert "2^46" in lib.pisa_last_error().decode()
 
 
 def test_pyramid_bytes(lib):
