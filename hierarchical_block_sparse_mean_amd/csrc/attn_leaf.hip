@@ -16,10 +16,11 @@
 // (query, KV head) combines the K partials into o and lse.  Partial O is
 // stored in the input dtype (bf16 rounding is far inside the bf16 tolerance).
 // Where a query kept both leaves of a level-2 block (2j and 2j + 1, adjacent
-// in its ascending row) and 2C keys fit one tile (C <= 64), the pair goes to
-// a cluster of that block instead: a second launch attends the 2C keys in one
-// tile, so the query's rows are read once and one partial (under the slot of
-// the even leaf) is written for both; the merge recognises the odd leaf's
+// in its ascending row) and 2C keys fit one tile (C <= 64, or C <= 128 for
+// 16-bit inputs, whose 256-key tile leaves LDS for five waves), the pair goes
+// to a cluster of that block instead: a second launch attends the 2C keys in
+// one tile, so the query's rows are read once and one partial (under the slot
+// of the even leaf) is written for both; the merge recognises the odd leaf's
 // slot from idx and skips it.
 // Work is done in chunks of KV heads so that the partial buffers stay within
 // a bound (24 GiB: all eight KV heads at once at 128K, two at a time at 256K).
@@ -61,8 +62,10 @@ constexpr size_t kAttnBudget = (size_t)24 << 30;  // partial buffers per head ch
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks; not
-// for fp32 rows of d = 128 (such a tile leaves LDS for two waves only), nor
+// sibling pairing: level-2 block tiles of 2C keys, at most 8 key blocks, or
+// 16 for 16-bit inputs (five waves fit beside a 256-key tile: 256K attention
+// 47.9 -> 46.4 ms, the merge reading fewer partials); not for fp32 rows of
+// d = 128 (an 8-block tile leaves LDS for two waves only), nor
 // where the level-2 blocks would push a head's clustering off its LDS
 // histogram (M_1 <= 16384 < M_1 + M_2: from about 700K to 1M tokens at
 // C = 64; measured 95 ms unpaired against 105 ms paired at 1M).  Beyond, both
@@ -71,7 +74,7 @@ static bool attn_pairs(const Problem& p) {
   const int64_t M1 = level_rows(p.N, p.C, 1);
   const bool leaves_in_lds = M1 <= kClusterLdsBins;
   const bool pairs_in_lds = M1 + (M1 + 1) / 2 <= kClusterLdsBins;
-  return p.C <= 64 && (p.dtype == 1 || p.D <= 64) && (pairs_in_lds || !leaves_in_lds);
+  return (p.C <= 64 ? (p.dtype == 1 || p.D <= 64) : p.dtype == 1) && (pairs_in_lds || !leaves_in_lds);
 }
 
 struct AttnLayout {
@@ -523,6 +526,8 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
         if (e == hipSuccess && pairs_on) e = run(attn_leaf_kernel<T, D, G, 8, true>, 8, attn_waves<T, D, 8>());
       } else {
         e = run(attn_leaf_kernel<T, D, G, 8, false>, 8, attn_waves<T, D, 8>());
+        if constexpr (sizeof(T) == 2)
+          if (e == hipSuccess && pairs_on) e = run(attn_leaf_kernel<T, D, G, 16, true>, 16, attn_waves<T, D, 16>());
       }
       if (e != hipSuccess) return e;
       const int64_t waves = heads * p.N;

@@ -29,6 +29,8 @@ CASES = {
     "bf16_c48_k5_causal": I.Workload("pairs_bf16_c48", 1, 1100, 8, 2, 128, 48, 5, "bf16", True, seed=92),
     "bf16_c32_k8_b2": I.Workload("pairs_bf16_c32", 2, 700, 8, 2, 128, 32, 8, "bf16", False, seed=93),
     "bf16_c64_k16_g4": I.Workload("pairs_bf16_c64", 1, 2100, 16, 4, 128, 64, 16, "bf16", True, seed=94),
+    # C = 128: 256-key pair tiles (bf16 only), ragged N
+    "bf16_c128_k6_causal": I.Workload("pairs_bf16_c128", 1, 2000, 8, 2, 128, 128, 6, "bf16", True, seed=97),
     # fp32 rows of d = 128: pairs are attended leaf by leaf (a 2C-key tile
     # would leave LDS for two waves), and 128-key leaf tiles run with fewer
     # waves
