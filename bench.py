@@ -142,14 +142,25 @@ def attended_keys(idx, N: int, C: int, causal: bool):
     return int(keys.sum().item())
 
 
-def attention_partials(idx, C: int) -> int:
+def attention_pairs(N: int, C: int, D: int, dtype: str) -> bool:
+    """Whether the library attends kept sibling pairs as one tile: C <= 64
+    (fp32 only with d = 64) or C <= 128 for bf16, unless the level-2 blocks
+    would push a head's clustering off its 16384-bin LDS histogram while the
+    leaves alone fit it."""
+    M1 = -(-N // C)
+    M2 = -(-M1 // 2)
+    fits = (dtype == "bf16" or D <= 64) if C <= 64 else dtype == "bf16"
+    return fits and (M1 + M2 <= 16384 or M1 > 16384)
+
+
+def attention_partials(idx, paired: bool) -> int:
     """Partial (query, slot) records the attention writes and the merge reads
-    per KV head: one per kept leaf, except that where C <= 64 a leaf kept
-    together with its sibling (even j followed by j + 1 in the ascending row)
-    shares one record with it."""
+    per KV head: one per kept leaf, except that with sibling pairing a leaf
+    kept together with its sibling (even j followed by j + 1 in the ascending
+    row) shares one record with it."""
     j = idx.long()
     kept = int((j >= 0).sum().item())
-    if C > 64:
+    if not paired:
         return kept
     both = (j[..., :-1] >= 0) & (j[..., :-1] % 2 == 0) & (j[..., 1:] == j[..., :-1] + 1)
     return kept - int(both.sum().item())
@@ -272,7 +283,7 @@ def main() -> int:
     blk2 = ws[: w.B * w.Hkv * w.N * w.K * 4].view(torch.int32).view(w.B, w.Hkv, w.N, w.K)
     scored_keys, s1_pairs = stage1_scored_keys(blk2, w.N, w.C, w.causal)
     attn_keys = attended_keys(idx, w.N, w.C, w.causal)
-    partials = attention_partials(idx, w.C)
+    partials = attention_partials(idx, attention_pairs(w.N, w.C, w.D, w.dtype))
     M = [pisa.level_rows(w.N, w.C, l) for l in range(1, pisa.levels(w.N, w.C) + 1)]
     rc = pisa.route_counts(p, q, k, pyr) if w.dtype == "bf16" else None
     queries = w.B * w.Hkv * w.N
