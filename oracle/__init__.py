@@ -79,6 +79,8 @@ def load(path: str = _LIB_PATH):
     lib.oracle_flat_select.restype = ctypes.c_int
     lib.oracle_exact_topk.argtypes = [P, vp, vp, vp, i64, vp, vp]
     lib.oracle_exact_topk.restype = ctypes.c_int
+    lib.oracle_leaf_scores.argtypes = [P, vp, vp, vp, i64, vp, i32, vp]
+    lib.oracle_leaf_scores.restype = ctypes.c_int
     lib.oracle_attention_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_attention_backward.restype = ctypes.c_int
     lib.oracle_counter_len.argtypes, lib.oracle_counter_len.restype = [], ctypes.c_int
@@ -253,6 +255,26 @@ def exact_topk(p: Problem, q, k, ts=None, lib=None, q_sampled: bool = False):
     if rc != 0:
         raise ValueError(f"oracle_exact_topk failed ({rc})")
     return idx, score
+
+
+def leaf_scores(p: Problem, q, k, leaves, ts=None, lib=None, q_sampled: bool = False):
+    """Level-1 block score (raw-key LSE, causally masked, summed over the GQA
+    group) of every listed leaf.  leaves: int [B][Hkv][nt][nl] (entries < 0
+    give -inf).  Returns float64 [B][Hkv][nt][nl]."""
+    lib = lib or load()
+    q, k, ts = _c(q), _c(k), _ts(p, ts)
+    nt = len(ts)
+    _check_q(p, q, nt, q_sampled)
+    leaves = np.ascontiguousarray(leaves, dtype=np.int32)
+    if leaves.ndim != 4 or leaves.shape[:3] != (p.B, p.Hkv, nt):
+        raise ValueError(f"leaves shape {leaves.shape} != {(p.B, p.Hkv, nt)} + (nl,)")
+    nl = leaves.shape[3]
+    out = np.empty(leaves.shape, np.float64)
+    rc = lib.oracle_leaf_scores(ctypes.byref(p.c_struct(_dtype_code(q, k), q_sampled)), q.ctypes.data, k.ctypes.data,
+                                ts.ctypes.data, nt, leaves.ctypes.data, nl, out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_leaf_scores failed ({rc})")
+    return out
 
 
 def decode_reference(p: Problem, q_new, k_prefix, v_prefix, lib=None):

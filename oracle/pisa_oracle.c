@@ -635,6 +635,47 @@ int oracle_exact_topk(const oracle_problem* p, const void* q, const void* k, con
   return 0;
 }
 
+/* ---- public: level-1 block score of given leaves ([SEL] score, l = 1) ---- *
+ * For every (b, h, sample s) and every listed leaf j = leaves[b][h][s][a]
+ * (a < nl): u = sum over the GQA group of the raw-key LSE of
+ * q_{h',t} . k_i * scale over the keys i of leaf j (i <= t when causal),
+ * [KER] GQA sum.  Entries < 0 or >= ceil(N/C), and leaves with no valid key,
+ * give -inf.  out: [B][Hkv][nt][nl].  This scores whatever set a selector
+ * returned, so a set can be checked without re-running the descent.        */
+int oracle_leaf_scores(const oracle_problem* p, const void* q, const void* k, const int32_t* ts, int64_t nt,
+                       const int32_t* leaves, int32_t nl, double* out) {
+  if (p->Hq % p->Hkv != 0 || nl < 0) return 1;
+  const int32_t G = p->Hq / p->Hkv;
+  const int64_t M1 = oracle_level_rows(p->N, p->C, 1);
+  for (int32_t b = 0; b < p->B; ++b)
+    for (int32_t h = 0; h < p->Hkv; ++h) {
+      const int64_t kbase = ((int64_t)b * p->Hkv + h) * (int64_t)p->N * p->D;
+#pragma omp parallel
+      {
+        double* buf = (double*)malloc(sizeof(double) * p->C);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t s = 0; s < nt; ++s) {
+          const int64_t t = ts[s];
+          const int64_t o = (((int64_t)b * p->Hkv + h) * nt + s) * nl;
+          for (int32_t a = 0; a < nl; ++a) {
+            const int64_t j = leaves[o + a];
+            double u = -INFINITY;
+            if (j >= 0 && j < M1) {
+              u = 0.0;
+              for (int32_t g = 0; g < G; ++g) {
+                int64_t nk = 0;
+                u += score_leaf(p, q, k, query_offset(p, b, h * G + g, t, s, nt), kbase, j, t, buf, &nk);
+              }
+            }
+            out[o + a] = u;
+          }
+        }
+        free(buf);
+      }
+    }
+  return 0;
+}
+
 /* ---- public: pyramid of every (b, h) head, stacked [B][Hkv][rows][D] --- */
 int oracle_build_pyramid(const oracle_problem* p, const void* k, double* pyr) {
   const int64_t rows = oracle_pyramid_rows(p->N, p->C);

@@ -222,6 +222,106 @@ def check_leaf_scores(lib, causal: bool) -> None:
             assert abs(float(total) - score[0, 0, s, a]) < 1e-11 * max(1.0, abs(float(total)))
 
 
+def check_leaf_score_entry(lib, causal: bool) -> None:
+    """oracle_leaf_scores scores arbitrary leaf lists (any order, -1 entries,
+    the ragged last leaf, leaves past the causal frontier) by the same
+    long-double brute force; on the descent's own sets it gives the scores
+    the descent reports."""
+    N, G, D, C = 1000, 4, 32, 64
+    q, k, _ = tiny_inputs(N=N, Hq=G, Hkv=1, D=D, seed=23)
+    p = oracle.Problem(1, N, G, 1, D, C, 3, causal=causal)
+    ts = [0, 63, 64, 130, 511, 999]
+    lists = np.array([[15, 0, -1, 3, 7], [0, 1, 15, 2, -1], [1, 0, 9, 15, 4], [2, 1, 0, 3, 12],
+                      [7, 8, 3, -1, 15], [15, 14, 0, 6, 2]], np.int32)[None, None]
+    got = oracle.leaf_scores(p, q, k, lists, ts=ts, lib=lib)
+    qq = np.array(q[0], dtype=np.longdouble)
+    kk = np.array(k[0, 0], dtype=np.longdouble)
+    scale = np.longdouble(1) / np.sqrt(np.longdouble(D))
+    for s, t in enumerate(ts):
+        for a, j in enumerate(lists[0, 0, s]):
+            lo, hi = j * C, min(j * C + C, N)
+            if causal:
+                hi = min(hi, t + 1)
+            if j < 0 or hi <= lo:
+                assert got[0, 0, s, a] == -np.inf, (t, j)
+                continue
+            total = np.longdouble(0)
+            for g in range(G):
+                z = (kk[lo:hi] @ qq[g, t]) * scale
+                m = z.max()
+                total += m + np.log(np.exp(z - m).sum())
+            assert abs(float(total) - got[0, 0, s, a]) < 1e-11 * max(1.0, abs(float(total))), (t, j)
+    idx, score, _, _ = oracle.select(p, q, k, ts=ts, lib=lib)
+    again = oracle.leaf_scores(p, q, k, idx, ts=ts, lib=lib)
+    np.testing.assert_array_equal(again, score)
+
+
+# --------------------------------------------------------------------------
+# Work counters: closed forms on shapes whose candidate sets the rules of
+# [SEL] fix regardless of the data (non-causal: every block valid; causal:
+# keys that grow with their index, so every top-K keeps the highest valid
+# blocks and the valid children can be counted by hand)
+# --------------------------------------------------------------------------
+def check_counters_noncausal(lib) -> None:
+    """N = 1024, C = 64, K = 4, levels 16 -> 8 -> 4 -> 2 -> 1, every block
+    valid: levels 5..3 hold 1, 2 and 4 candidates (kept without scoring);
+    level 2 holds the 8 children of those 4 and scores them (8 blocks, 2 child
+    summaries each); the 4 kept give 8 candidate leaves, scored on 64 raw keys
+    each.  Per query: 8 scored blocks, 16 child dots, 8 leaf pairs, 512 leaf
+    key dots, one scored level >= 2."""
+    N, G, D = 1024, 4, 16
+    q, k, _ = tiny_inputs(N=N, Hq=G, Hkv=1, D=D, seed=27)
+    p = oracle.Problem(1, N, G, 1, D, 64, 4, causal=False)
+    ts = list(range(0, N, 7))
+    nt = len(ts)
+    _, _, _, c = oracle.select(p, q, k, ts=ts, lib=lib)
+    assert c["queries"] == nt
+    assert c["scored_blocks"] == 8 * nt, c
+    assert c["child_dots"] == 16 * nt, c
+    assert c["leaf_pairs"] == 8 * nt, c
+    assert c["leaf_key_dots"] == 512 * nt, c
+    assert c["scored_levels"] == nt, c
+    assert c["max_candidates"] == 8 and c["max_kept"] == 4, c
+    assert c["per_level_candidates"][1:6] == [8 * nt, 8 * nt, 4 * nt, 2 * nt, nt], c["per_level_candidates"][:6]
+
+
+def check_counters_causal(lib) -> None:
+    """Causal, N = 1024, C = 64, K = 2, two query heads equal to e_0 and keys
+    k_i = 0.375 i e_0 (logit 0.046875 i at D = 64): later blocks always score
+    higher, so each scored level keeps its two highest valid blocks.  Counted
+    by hand from the validity rule (a block is valid iff its first token is
+    <= t) for three positions:
+      t = 100: levels 5..2 hold the single valid block 0, level 1 the leaves
+               {0, 1} -- nothing scored, idx {0, 1};
+      t = 700: level 3 {0, 1, 2} scored (children 0..5 all valid: 6 dots),
+               keeps {1, 2}; level 2 {2, 3, 4, 5} scored (children 4..10
+               valid, 11 starts at 704: 7 dots), keeps {4, 5}; leaves
+               {8, 9, 10} valid (64 + 64 + 61 keys), idx {9, 10};
+      t = 1023: level 3 {0..3} (8 dots) keeps {2, 3}; level 2 {4..7} (8 dots)
+               keeps {6, 7}; leaves {12..15} (256 keys), idx {14, 15}.
+    The group sum adds per-head scores; the counters count per KV group."""
+    N, D, C, K = 1024, 64, 64, 2
+    q = np.zeros((1, 2, N, D), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, D), np.float32)
+    k[0, 0, :, 0] = 0.375 * np.arange(N, dtype=np.float32)
+    p = oracle.Problem(1, N, 2, 1, D, C, K, causal=True)
+    expect = {
+        100: dict(idx=[0, 1], scored_blocks=0, child_dots=0, leaf_pairs=0, leaf_key_dots=0, scored_levels=0,
+                  levels=[2, 1, 1, 1, 1]),
+        700: dict(idx=[9, 10], scored_blocks=7, child_dots=13, leaf_pairs=3, leaf_key_dots=189, scored_levels=2,
+                  levels=[3, 4, 3, 2, 1]),
+        1023: dict(idx=[14, 15], scored_blocks=8, child_dots=16, leaf_pairs=4, leaf_key_dots=256, scored_levels=2,
+                   levels=[4, 4, 4, 2, 1]),
+    }
+    for t, e in expect.items():
+        idx, _, _, c = oracle.select(p, q, k, ts=[t], lib=lib)
+        assert idx[0, 0, 0].tolist() == e["idx"], (t, idx[0, 0, 0])
+        for name in ("scored_blocks", "child_dots", "leaf_pairs", "leaf_key_dots", "scored_levels"):
+            assert c[name] == e[name], (t, name, c[name], e[name])
+        assert c["per_level_candidates"][1:6] == e["levels"], (t, c["per_level_candidates"][:6])
+
+
 # --------------------------------------------------------------------------
 # Bounds ([SEL]: candidate sets <= gK, kept <= K)
 # --------------------------------------------------------------------------
@@ -562,6 +662,10 @@ ALL_CHECKS = [
     ("table_descent_causal", lambda lib: check_table_descent(lib, True)),
     ("leaf_scores_noncausal", lambda lib: check_leaf_scores(lib, False)),
     ("leaf_scores_causal", lambda lib: check_leaf_scores(lib, True)),
+    ("leaf_score_entry_noncausal", lambda lib: check_leaf_score_entry(lib, False)),
+    ("leaf_score_entry_causal", lambda lib: check_leaf_score_entry(lib, True)),
+    ("counters_noncausal", lambda lib: check_counters_noncausal(lib)),
+    ("counters_causal", lambda lib: check_counters_causal(lib)),
     ("bounds", lambda lib: check_bounds(lib)),
     ("dense_noncausal", lambda lib: check_dense_equivalence(lib, False)),
     ("dense_causal", lambda lib: check_dense_equivalence(lib, True)),

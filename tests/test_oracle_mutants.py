@@ -38,6 +38,15 @@ MUTANTS = [
     ("flat_uses_first_head_only", "            for (int32_t g = 0; g < G; ++g) {\n              int64_t qoff",
      "            for (int32_t g = 0; g < 1; ++g) {\n              int64_t qoff"),
     ("backward_drops_row_term", "            const double ds = z[a] * (dp - Dt);", "            const double ds = z[a] * dp;"),
+    ("child_dots_count_invalid_children",
+     "              if (!(p->causal && block_start(r, p->C, l - 1) > t)) cnt[CNT_CHILD_DOTS] += 1;",
+     "              cnt[CNT_CHILD_DOTS] += 1;"),
+    ("leaf_key_dots_ignore_causal_mask", "            if (must_score) cnt[CNT_LEAF_KEY_DOTS] += (g == 0) ? nk : 0;",
+     "            if (must_score) cnt[CNT_LEAF_KEY_DOTS] += (g == 0) ? p->C : 0;"),
+    ("leaf_key_dots_counted_per_head", "            if (must_score) cnt[CNT_LEAF_KEY_DOTS] += (g == 0) ? nk : 0;",
+     "            if (must_score) cnt[CNT_LEAF_KEY_DOTS] += nk;"),
+    ("unscored_leaf_level_counted", "        if (must_score) {\n          if (l == 1) {",
+     "        if (1) {\n          if (l == 1) {"),
     ("backward_dk_unscaled", "              dk[ko + d] += p->scale * ds * widen(q, p->dtype, qoff + d);",
      "              dk[ko + d] += ds * widen(q, p->dtype, qoff + d);"),
 ]
