@@ -109,9 +109,10 @@ hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32
 hipError_t launch_chunk_map(const int32_t* chunk_off, int64_t ncl, int32_t* map, hipStream_t stream);
 
 // Attention clusters (forward and backward): (query block, key block) bins
-// per head (key blocks: the leaves, and in the forward at C <= 64 also the
-// level-2 blocks of sibling pairs), so one block of queries is attended
-// together and its query rows are re-read from cache.
+// per head (key blocks: the leaves, and in the forward also the level-2
+// blocks of sibling pairs wherever 2C keys fit one tile: C <= 64, or
+// C <= 128 for 16-bit inputs, except fp32 rows of d = 128), so one block of
+// queries is attended together and its query rows are re-read from cache.
 constexpr int64_t kAttnBins = 8192;
 
 // attn_leaf.hip: leaf-major MFMA attention with a merge pass

@@ -248,6 +248,13 @@ def select(p: Problem, q, k, pyr, idx=None, score=None, ws=None, with_score: boo
     return idx, score
 
 
+def select_level2(p: Problem, ws: torch.Tensor) -> torch.Tensor:
+    """View of the stage-1 result a two-stage select left in its workspace:
+    int32 [B][Hkv][N][K], the level-2 blocks kept per (b, h, t), -1 padded."""
+    n = p.B * p.Hkv * p.N * p.K
+    return ws[: 4 * n].view(torch.int32).view(p.B, p.Hkv, p.N, p.K)
+
+
 def attn_workspace_bytes(p: Problem) -> int:
     return load().pisa_attn_workspace_bytes(ctypes.byref(p.c()))
 

@@ -135,7 +135,12 @@ pisa_status pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyr,
  * padded; score (may be NULL) the GQA-summed leaf LSE of each kept leaf
  * (-inf padded).  Reads pyr built by pisa_build_pyramid for the same k.
  * ws: device workspace of at least pisa_select_workspace_bytes(p) bytes
- * (256-byte aligned); its contents on entry do not matter.                  */
+ * (256-byte aligned); its contents on entry do not matter.  After a
+ * two-stage call (select_algo AUTO or TWO_STAGE) has completed, the first
+ * B*Hkv*N*K int32 of ws hold the stage-1 result: per (b, h, t) the level-2
+ * blocks kept by the descent ([B][Hkv][N][K], -1 padded), whose children are
+ * the candidate leaves stage 2 scored.  Exposed so a caller can check the
+ * final set against those candidates; a fused call leaves ws unspecified.  */
 size_t pisa_select_workspace_bytes(const pisa_problem* p);
 pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, const float* pyr,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes,

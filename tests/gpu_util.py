@@ -9,6 +9,8 @@ import sys
 import numpy as np
 import torch
 
+import oracle
+
 NEAR_TIE = 1e-3
 SCORE_RTOL = 1e-4
 ATTN_TOL = {"f32": 1e-3, "bf16": 2e-2}
@@ -67,3 +69,69 @@ def check_attention(g_o, o_ref, dtype, label=""):
     tol = ATTN_TOL[dtype]
     assert err <= tol, f"{label}: attention max-abs error {err:.3g} > {tol}"
     return float(err)
+
+
+def check_gpu_sets(op, q, k, ts, g_idx, g_score, g_blk2=None, q_sampled=False, label=""):
+    """Checks on the GPU's own selection that hold whichever member of a
+    near-tie it kept (coarse-to-fine top-K section: per-level top-K, keep-all
+    rule, LSE score; kernel-implementation section: GQA sum):
+
+    (a) the reported score of every kept leaf equals the oracle's level-1
+        score of that leaf (raw-key LSE summed over the group) within
+        1e-4 * max(1, |u|); padding slots are -inf;
+    (b) given the level-2 blocks stage 1 kept (g_blk2), the set is a top-K of
+        their valid children by the oracle's leaf scores: it holds
+        min(K, #valid children) of them, and no child left out scores more
+        than the band above a kept one (band = the 1e-3 near-tie width plus
+        the score tolerance on both sides).
+
+    g_idx, g_score, g_blk2: [B][Hkv][nt][K] at positions ts (None = all).
+    Returns counts for the log: rows checked by (a) and by (b), and the
+    largest score error."""
+    g_idx = np.asarray(g_idx)
+    g_score = np.asarray(g_score, np.float64)
+    B, Hkv, nt, K = g_idx.shape
+    pos = np.arange(op.N) if ts is None else np.asarray(ts)
+    sc = oracle.leaf_scores(op, q, k, g_idx, ts=pos, q_sampled=q_sampled)
+    kept = g_idx >= 0
+    assert np.isfinite(sc[kept]).all(), f"{label}: a kept leaf has no valid key"
+    err = np.abs(g_score[kept] - sc[kept])
+    lim = SCORE_RTOL * np.maximum(1.0, np.abs(sc[kept]))
+    assert (err <= lim).all(), f"{label}: GPU score of its own leaf off by {err.max():.3g}"
+    assert np.isneginf(g_score[~kept]).all(), f"{label}: padding score not -inf"
+    out = {"rows": int(B * Hkv * nt), "score_err": float(err.max()) if err.size else 0.0, "topk_checked": 0}
+    if g_blk2 is None:
+        return out
+    M1 = -(-op.N // op.C)
+    j2 = np.asarray(g_blk2, np.int64)
+    cand = np.stack([2 * j2, 2 * j2 + 1], axis=-1).reshape(B, Hkv, nt, 2 * K)
+    has = np.repeat(j2 >= 0, 2, axis=-1)
+    t = pos.reshape(1, 1, nt, 1)
+    valid = has & (cand < M1) & ((not op.causal) | (cand * op.C <= t))
+    cand = np.where(valid, cand, -1).astype(np.int32)
+    csc = oracle.leaf_scores(op, q, k, cand, ts=pos, q_sampled=q_sampled)
+    for b in range(B):
+        for h in range(Hkv):
+            for s in range(nt):
+                v = cand[b, h, s][valid[b, h, s]]
+                u = csc[b, h, s][valid[b, h, s]]
+                gk = g_idx[b, h, s][kept[b, h, s]]
+                where = f"{label}: (b={b}, h={h}, t={int(pos[s])})"
+                assert set(gk.tolist()) <= set(v.tolist()), f"{where}: kept {gk} not among children {v}"
+                assert len(gk) == min(K, len(v)), f"{where}: kept {len(gk)} of {len(v)} children (K={K})"
+                if len(v) > K:
+                    inside = np.isin(v, gk)
+                    lo, hi = u[inside].min(), u[~inside].max()
+                    band = NEAR_TIE + 2 * SCORE_RTOL * max(1.0, abs(lo), abs(hi))
+                    assert lo >= hi - band, f"{where}: left-out child scores {hi:.6g} > kept {lo:.6g} + {band:.3g}"
+    out["topk_checked"] = int(B * Hkv * nt)
+    return out
+
+
+def check_attention_on_gpu_idx(op, q, k, v, ts, g_idx, g_o, dtype, q_sampled=False, label=""):
+    """pisa_sparse_attn's output on the GPU's own selection against the
+    oracle's attention on that same selection, at every sampled position
+    (block-sparse attention section, the o_t equation)."""
+    pos = np.arange(op.N) if ts is None else np.asarray(ts)
+    r_o, _ = oracle.attention(op, q, k, v, np.ascontiguousarray(g_idx, dtype=np.int32), ts=pos, q_sampled=q_sampled)
+    return check_attention(g_o, r_o, dtype, label)

@@ -31,6 +31,10 @@ CASES = {
     "bf16_c64_k16_g4": I.Workload("pairs_bf16_c64", 1, 2100, 16, 4, 128, 64, 16, "bf16", True, seed=94),
     # C = 128: 256-key pair tiles (bf16 only), ragged N
     "bf16_c128_k6_causal": I.Workload("pairs_bf16_c128", 1, 2000, 8, 2, 128, 128, 6, "bf16", True, seed=97),
+    # the 256-key pair tile at d = 64, and with a 16-head group (one query per
+    # 16-column MFMA tile)
+    "bf16_c128_d64_k8": I.Workload("pairs_bf16_c128_d64", 1, 2300, 4, 2, 64, 128, 8, "bf16", True, seed=98),
+    "bf16_c128_g16_k5": I.Workload("pairs_bf16_c128_g16", 1, 1900, 16, 1, 128, 128, 5, "bf16", False, seed=99),
     # fp32 rows of d = 128: pairs are attended leaf by leaf (a 2C-key tile
     # would leave LDS for two waves), and 128-key leaf tiles run with fewer
     # waves

@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import check_attention, check_selection, log, to_dev, to_host_f64
+from gpu_util import (check_attention, check_attention_on_gpu_idx, check_gpu_sets, check_selection, log,
+                      to_dev, to_host_f64)
 from hierarchical_block_sparse_mean_amd import inputs as I
 from hierarchical_block_sparse_mean_amd import pisa
 
@@ -105,10 +106,20 @@ def test_select(name, algo):
     log(f"[test_select {name} algo={algo}]")
     p = _problem(w, algo)
     pyr = pisa.build_pyramid(p, c["dev"]["k"])
-    idx, score = pisa.select(p, c["dev"]["q"], c["dev"]["k"], pyr)
+    ws = pisa.workspace(pisa.select_workspace_bytes(p))
+    idx, score = pisa.select(p, c["dev"]["q"], c["dev"]["k"], pyr, ws=ws)
     torch.cuda.synchronize()
-    ex, rate = check_selection(_sel(idx, c["ts"]), _sel(score, c["ts"]), c["o_idx"], c["o_score"], c["o_gap"], name)
-    log(f"  exempt fraction {ex:.4f}, exact-match rate {rate:.4f}")
+    g_idx, g_score = _sel(idx, c["ts"]), _sel(score, c["ts"])
+    ex, rate = check_selection(g_idx, g_score, c["o_idx"], c["o_score"], c["o_gap"], name)
+    # the GPU's own sets, wherever they differ from the oracle's (near-ties):
+    # reported scores are the oracle's scores of those leaves, and the set is a
+    # top-K of the children of the level-2 blocks stage 1 kept
+    blk2 = _sel(pisa.select_level2(p, ws), c["ts"]) if algo == pisa.SELECT_TWO_STAGE else None
+    differ = int((~(g_idx == c["o_idx"]).all(-1)).sum())
+    chk = check_gpu_sets(_oproblem(w), c["data"]["q"], c["data"]["k"], c["ts"], g_idx, g_score, blk2, label=name)
+    log(f"  exempt fraction {ex:.4f}, exact-match rate {rate:.4f}; {differ} rows differ from the oracle; "
+        f"GPU-set checks: scores on {chk['rows']} rows (max err {chk['score_err']:.2g}), top-K within the "
+        f"level-2 children on {chk['topk_checked']} rows")
 
 
 @pytest.mark.parametrize("name", ["bf16_g4_n4133", "bf16_g1_b2", "bf16_g2_d64", "bf16_g8", "bf16_g16_c32",
@@ -197,11 +208,12 @@ def test_end_to_end(name):
     torch.cuda.synchronize()
     gidx = idx.cpu().numpy()
     same = (gidx == c["o_idx"]).all(-1)  # [B][Hkv][N]
-    ok = np.repeat(same, w.gq, axis=1)  # per query head
-    got = to_host_f64(o)
-    err = np.abs(got - c["o_o"]).max(axis=-1)[ok].max()
-    assert err <= {"f32": 1e-3, "bf16": 2e-2}[w.dtype]
-    assert ok.mean() > 0.95
+    assert same.mean() > 0.95
+    # attention on the GPU's own selection at every position, differing
+    # (near-tied) rows included
+    err = check_attention_on_gpu_idx(_oproblem(w), c["data"]["q"], c["data"]["k"], c["data"]["v"], None, gidx,
+                                     to_host_f64(o), w.dtype, label=name)
+    log(f"[test_end_to_end {name}] {int((~same).sum())} rows differ from the oracle; attention err {err:.3g}")
 
 
 # ---- decode ------------------------------------------------------------------
@@ -239,13 +251,17 @@ def test_decode(name):
         k_host[:, :, n], v_host[:, :, n] = tok["k"], tok["v"]
         kp = np.ascontiguousarray(k_host[:, :, : n + 1])
         vp = np.ascontiguousarray(v_host[:, :, : n + 1])
-        r_idx, r_score, r_gap, r_o, _ = oracle.decode_reference(op, tok["q"], kp, vp)
-        check_selection(idx.cpu().numpy()[:, :, None], score.cpu().numpy()[:, :, None], r_idx[:, :, None],
-                        r_score[:, :, None], r_gap[:, :, None], f"{name} step {step}")
-        same = (idx.cpu().numpy() == r_idx).all(-1)
-        got = to_host_f64(o)
-        okh = np.repeat(same, w.gq, axis=1)
-        assert np.abs(got - r_o).max(axis=-1)[okh].max() <= {"f32": 1e-3, "bf16": 2e-2}[w.dtype]
+        r_idx, r_score, r_gap, _, _ = oracle.decode_reference(op, tok["q"], kp, vp)
+        g_idx, g_score = idx.cpu().numpy()[:, :, None], score.cpu().numpy()[:, :, None]
+        check_selection(g_idx, g_score, r_idx[:, :, None], r_score[:, :, None], r_gap[:, :, None],
+                        f"{name} step {step}")
+        # the GPU's own set: its scores, and attention over it, at every
+        # sequence (the fused kernel exposes no level-2 set)
+        opn = oracle.Problem(w.B, n + 1, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True)
+        q1 = np.ascontiguousarray(tok["q"][:, :, None, :])
+        check_gpu_sets(opn, q1, kp, [n], g_idx, g_score, q_sampled=True, label=f"{name} step {step}")
+        check_attention_on_gpu_idx(opn, q1, kp, vp, [n], g_idx, to_host_f64(o)[:, :, None], w.dtype,
+                                   q_sampled=True, label=f"{name} step {step}")
         assert (length.cpu().numpy() == n + 1).all()
     assert int(err.item()) == 0
     # the incrementally updated pyramid equals a rebuild over the prefix
