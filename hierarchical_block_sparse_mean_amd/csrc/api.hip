@@ -121,6 +121,49 @@ pisa_status validate(const pisa_problem* p, pisa::Problem* out) {
 
 size_t blk2_bytes(const pisa::Problem& q) { return align256(sizeof(int32_t) * (size_t)q.B * q.Hkv * q.N * q.K); }
 
+// ---- library-owned selection scratch (pisa_select_noalloc) ------------------
+// One array per GPU, alive until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: the device address of each
+// GPU's copy is looked up once per device (hipGetSymbolAddress with that
+// device current) and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[PISA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+pisa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PISA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PISA_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(PISA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PISA_OK;
+}
+
+// pisa_select's work once its arguments are validated: stage 1 into the
+// first part of ws, then stage 2 and the final top-K (or the fused program)
+pisa_status run_select(const pisa::Problem& pr, int32_t algo, const void* q, const void* k, const float* pyr,
+                       int32_t* idx, float* score, void* ws, hipStream_t stream) {
+  if (algo == PISA_SELECT_FUSED)
+    return hip_status(pisa::launch_route(pr, q, k, pyr, idx, score, true, stream), "pisa_select (fused)");
+  int32_t* blk2 = static_cast<int32_t*>(ws);
+  void* ws2 = static_cast<char*>(ws) + blk2_bytes(pr);
+  hipError_t e = pisa::launch_route(pr, q, k, pyr, blk2, nullptr, false, stream);
+  if (e != hipSuccess) return hip_status(e, "pisa_select (stage 1)");
+  return hip_status(pisa::launch_stage2(pr, q, k, blk2, idx, score, ws2, stream), "pisa_select (stage 2)");
+}
+
 // ---- per-kernel timer ------------------------------------------------------
 struct TimerRecord {
   const char* name;
@@ -255,17 +298,33 @@ pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, con
   if (s != PISA_OK) return s;
   if (q == nullptr || k == nullptr || pyr == nullptr || idx == nullptr)
     return fail(PISA_ERR_INVALID_ARG, "q, k, pyr and idx must be non-NULL");
-  if (p->select_algo == PISA_SELECT_FUSED)
-    return hip_status(pisa::launch_route(pr, q, k, pyr, idx, score, true, stream), "pisa_select (fused)");
+  if (p->select_algo == PISA_SELECT_FUSED) return run_select(pr, p->select_algo, q, k, pyr, idx, score, nullptr, stream);
   const size_t need = blk2_bytes(pr) + pisa::stage2_workspace_bytes(pr);
   if (ws == nullptr || ws_bytes < need)
     return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws == nullptr ? 0 : ws_bytes);
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(PISA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  int32_t* blk2 = static_cast<int32_t*>(ws);
-  void* ws2 = static_cast<char*>(ws) + blk2_bytes(pr);
-  hipError_t e = pisa::launch_route(pr, q, k, pyr, blk2, nullptr, false, stream);
-  if (e != hipSuccess) return hip_status(e, "pisa_select (stage 1)");
-  return hip_status(pisa::launch_stage2(pr, q, k, blk2, idx, score, ws2, stream), "pisa_select (stage 2)");
+  return run_select(pr, p->select_algo, q, k, pyr, idx, score, ws, stream);
+}
+
+pisa_status pisa_select_noalloc(const pisa_problem* p, const void* q, const void* k, const float* pyr, int32_t* idx,
+                                float* score, hipStream_t stream) {
+  pisa::Problem pr;
+  pisa_status s = validate(p, &pr);
+  if (s != PISA_OK) return s;
+  if (q == nullptr || k == nullptr || pyr == nullptr || idx == nullptr)
+    return fail(PISA_ERR_INVALID_ARG, "q, k, pyr and idx must be non-NULL");
+  const size_t need = p->select_algo == PISA_SELECT_FUSED ? 0 : blk2_bytes(pr) + pisa::stage2_workspace_bytes(pr);
+  if (need > (size_t)PISA_NOALLOC_SCRATCH_BYTES)
+    return fail(PISA_ERR_WORKSPACE,
+                "pisa_select_noalloc: this problem needs %zu bytes of scratch, beyond the library's %zu; "
+                "call pisa_select with a workspace instead",
+                need, (size_t)PISA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    s = scratch_address(&ws);
+    if (s != PISA_OK) return s;
+  }
+  return run_select(pr, p->select_algo, q, k, pyr, idx, score, ws, stream);
 }
 
 pisa_status pisa_route_counts(const pisa_problem* p, const void* q, const void* k, const float* pyr,

@@ -32,7 +32,7 @@ EXPORTS = [
     "pisa_pyramid_bytes", "pisa_levels", "pisa_level_rows", "pisa_level_offset", "pisa_build_pyramid",
     "pisa_select_workspace_bytes", "pisa_select", "pisa_attn_workspace_bytes", "pisa_sparse_attn",
     "pisa_attn_backward_workspace_bytes", "pisa_sparse_attn_backward", "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
-    "pisa_route_counts",
+    "pisa_route_counts", "pisa_select_noalloc",
     "pisa_last_error", "pisa_version",
 ]
 
@@ -80,6 +80,7 @@ def load(path: str = LIB_PATH):
         "pisa_build_pyramid": ([P, vp, vp, vp], ctypes.c_int),
         "pisa_select_workspace_bytes": ([P], sz),
         "pisa_select": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "pisa_select_noalloc": ([P, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "pisa_attn_workspace_bytes": ([P], sz),
         "pisa_sparse_attn": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_attn_backward_workspace_bytes": ([P], sz),
@@ -245,6 +246,23 @@ def select(p: Problem, q, k, pyr, idx=None, score=None, ws=None, with_score: boo
         ws = workspace(select_workspace_bytes(p), dev)
     _check(load().pisa_select(ctypes.byref(p.c()), q.data_ptr(), k.data_ptr(), pyr.data_ptr(), idx.data_ptr(),
                               _ptr(score), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return idx, score
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PISA_NOALLOC_SCRATCH_BYTES
+
+
+def select_noalloc(p: Problem, q, k, pyr, idx, score=None, stream=None):
+    """pisa_select_noalloc: pisa_select with the library's own per-GPU
+    scratch (no workspace argument, nothing allocated by the call).  idx (and
+    score, if given) must be preallocated.  Returns (idx, score)."""
+    _need(q, "q", (p.B, p.Hq, p.N, p.D), p.torch_dtype)
+    _need(k, "k", (p.B, p.Hkv, p.cap_tokens, p.D), p.torch_dtype)
+    _need(idx, "idx", (p.B, p.Hkv, p.N, p.K), torch.int32)
+    if score is not None:
+        _need(score, "score", (p.B, p.Hkv, p.N, p.K), torch.float32)
+    _check(load().pisa_select_noalloc(ctypes.byref(p.c()), q.data_ptr(), k.data_ptr(), pyr.data_ptr(),
+                                      idx.data_ptr(), _ptr(score), _stream(stream)))
     return idx, score
 
 

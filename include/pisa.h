@@ -146,6 +146,24 @@ pisa_status pisa_select(const pisa_problem* p, const void* q, const void* k, con
                         int32_t* idx, float* score, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ---- selection without a caller workspace --------------------------------- *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and results as pisa_select, with the workspace taken
+ * from a scratch array of PISA_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on (from the first call on that GPU until the process
+ * ends).  The call allocates and frees nothing.  A problem whose
+ * pisa_select_workspace_bytes exceeds PISA_NOALLOC_SCRATCH_BYTES returns
+ * PISA_ERR_WORKSPACE before anything is launched (128 MiB holds, e.g.,
+ * N = 32768 with 8 KV heads and K = 16).  The scratch needs no clearing:
+ * like pisa_select's workspace, its contents on entry do not matter.  Every
+ * call on one GPU uses that GPU's one array, so calls that overlap on a GPU
+ * (other streams, other host threads) race; serialise them.  Other errors
+ * as pisa_select.                                                          */
+#define PISA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+pisa_status pisa_select_noalloc(const pisa_problem* p, const void* q, const void* k, const float* pyr,
+                                int32_t* idx, float* score, hipStream_t stream);
+
 /* ---- block-sparse attention [BSA] --------------------------------------- *
  * o[b][h'][t] = sum_i softmax_i(q . k_i * scale) v_i over the keys i of the
  * leaves idx[b][h'/G_Q][t][*] (entries < 0 or >= ceil(N/C) ignored; keys

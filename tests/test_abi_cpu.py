@@ -144,6 +144,25 @@ def test_null_pointers_and_small_workspace(lib):
     assert lib.pisa_build_pyramid(None, FAKE, FAKE, None) == pisa.PISA_ERR_INVALID_ARG
 
 
+def test_noalloc_select_host_checks(lib):
+    """pisa_select_noalloc validates like pisa_select and refuses, before any
+    device work, a problem whose workspace exceeds the library's scratch."""
+    small = _p().c()
+    assert lib.pisa_select_noalloc(ctypes.byref(small), FAKE, None, FAKE, FAKE, None, None) == \
+        pisa.PISA_ERR_INVALID_ARG
+    assert lib.pisa_select_noalloc(None, FAKE, FAKE, FAKE, FAKE, None, None) == pisa.PISA_ERR_INVALID_ARG
+    big = pisa.Problem(B=1, N=131072, Hq=32, Hkv=8, D=128, C=64, K=16, causal=True, dtype="bf16")
+    assert pisa.select_workspace_bytes(big) > pisa.NOALLOC_SCRATCH_BYTES
+    assert lib.pisa_select_noalloc(ctypes.byref(big.c()), FAKE, FAKE, FAKE, FAKE, None, None) == \
+        pisa.PISA_ERR_WORKSPACE
+    assert b"scratch" in lib.pisa_last_error()
+    fits = pisa.Problem(B=1, N=32768, Hq=32, Hkv=8, D=128, C=64, K=16, causal=True, dtype="bf16")
+    assert pisa.select_workspace_bytes(fits) <= pisa.NOALLOC_SCRATCH_BYTES
+    with open(os.path.join(ROOT, "include", "pisa.h")) as f:
+        assert "#define PISA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in f.read()
+    assert pisa.NOALLOC_SCRATCH_BYTES == 128 << 20
+
+
 def test_backward_shape_limit(lib):
     """fp32 rows of d = 128 with C > 64 are rejected by the backward before
     any pointer is used; the forward and the other shapes are accepted."""
