@@ -11,14 +11,19 @@
 //      children (sibling rows fetched by all waves at once), so the cached
 //      pyramid stays equal to a rebuild over the prefix;
 //   2. the descent for the new query (t = n, every block valid): the child
-//      rows of a scored level are spread over all waves, 8 lanes per fp32
-//      row; wave 0 keeps the top K and expands them;
+//      rows of a scored level are spread over all waves, 8 lanes per row of
+//      the pyramid's fp16 block-floating-point copy (row * 2^-ex, half the
+//      bytes of the fp32 row; the same rows prefill stage 1 scores); wave 0
+//      keeps the top K and expands them;
 //   3. leaf level: each candidate leaf's C raw keys against the G_Q query
 //      heads on MFMA (keys as rows, heads as columns), its per-head max and
-//      log-sum-exp kept in LDS; wave 0 keeps the final top K;
+//      log-sum-exp kept in LDS, and, where they fit, its raw logits too;
+//      wave 0 keeps the final top K;
 //   4. attention: the per-head max and denominator over the kept leaves come
 //      from those LDS values, so every wave's partial output over its leaves
-//      is already on the common scale; partials add through LDS.
+//      is already on the common scale; partials add through LDS.  The kept
+//      leaves' logits are read back from LDS (their keys are not fetched a
+//      second time), so only their values are read here.
 #include "kernels.h"
 
 namespace pisa {
@@ -44,6 +49,10 @@ struct DecodeKArgs {
 };
 
 constexpr int kDecMaxCand = 64;  // 2K, K <= 32
+// raw logits of the candidate leaves kept in LDS for the attention phase
+// (2K candidates x C keys x G_Q heads; 32 KB: K = 16, C = 64, G_Q = 4);
+// larger problems recompute the kept leaves' logits from their keys
+constexpr int kDecLogitFloats = 8192;
 
 // N consecutive elements (N = 4 or 8) as fp32
 template <typename T, int N>
@@ -113,6 +122,7 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
   __shared__ float s_M[G], s_L[G];
   __shared__ int32_t s_state[2];  // level, candidate count
   __shared__ __align__(16) float s_p[NW][CP][G];
+  __shared__ float s_logit[kDecLogitFloats];  // [candidate][key][head] raw dot products
   constexpr int kUpdFloats = NW * D + (kMaxLevels + 1) * D;  // leaf-mean partials + sibling rows
   constexpr int kOutFloats = NW * G * D;                     // partial outputs
   __shared__ __align__(16) float s_u[kUpdFloats > kOutFloats ? kUpdFloats : kOutFloats];
@@ -283,7 +293,8 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
     // score the nA > K candidates of level l by their children at level l - 1
     {
       const int64_t m_child = level_rows(n1, C, l - 1);
-      const float* child_level = pbase + a.geo.level_off[l - 1] * D;
+      const _Float16* child_level = hbase + a.geo.level_off[l - 1] * D;
+      const int32_t* child_ex = xbase + a.geo.level_off[l - 1];
       constexpr int DL = D / 8;  // dims per lane, 8 lanes per row
       const int sub = lane & 7;
       for (int base = 0; base < 2 * nA; base += NW * 8) {
@@ -294,16 +305,16 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
         float dot[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) dot[g] = 0.f;
+        int32_t er = 0;
         if (valid) {
-          const float* row = child_level + r * D + sub * DL;
+          const _Float16* row = child_level + r * D + sub * DL;
+          er = child_ex[r];
           float rv[DL];
 #pragma unroll
-          for (int e = 0; e < DL; e += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(row + e);
-            rv[e] = x.x;
-            rv[e + 1] = x.y;
-            rv[e + 2] = x.z;
-            rv[e + 3] = x.w;
+          for (int e = 0; e < DL; e += 8) {
+            const halfx8 x = *reinterpret_cast<const halfx8*>(row + e);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) rv[e + c8] = (float)x[c8];
           }
 #pragma unroll
           for (int g = 0; g < G; ++g)
@@ -316,10 +327,12 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
               dot[g] = fmaf(rv[e + 3], qv.w, dot[g]);
             }
         }
+        // the row is stored as row * 2^-er: its logits scale by 2^er
+        const float rscale = ldexpf(a.scale, er);
         float u = 0.f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float x = valid ? group_sum<8>(dot[g]) * a.scale : -INFINITY;
+          const float x = valid ? group_sum<8>(dot[g]) * rscale : -INFINITY;
           u += lse2(x, __shfl_xor(x, 8));  // the sibling child sits 8 lanes away
         }
         if ((lane & 15) == 0 && i < nA) s_score[i] = u;
@@ -359,6 +372,8 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
     else fq[st].zero();
   }
   const float sl2 = a.scale * kLog2e;
+  // the candidates' raw logits stay in LDS for the attention phase if they fit
+  const bool keep_logits = nA * CP * G <= kDecLogitFloats;
   for (int i = w; i < nA; i += NW) {
     const int64_t lo = (int64_t)s_cand[i] * C;
     const int64_t hi = lo + C < n1 ? lo + C : n1;
@@ -374,6 +389,11 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
         acc[kb][e] = ok ? acc[kb][e] : -INFINITY;
         mx = fmaxf(mx, acc[kb][e]);
       }
+    if (keep_logits && col < G)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_logit[(i * CP + kb * 16 + 4 * g4 + e) * G + col] = acc[kb][e];
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float sum = 0.f;
@@ -441,16 +461,32 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
     const int64_t lo = (int64_t)s_sel[c] * C;
     const int64_t hi = lo + C < n1 ? lo + C : n1;
     const int nk = (int)(hi - lo);
-    floatx4 acc[NKB];
-    leaf_dots<T, D, NKB>(fq, kbase, knew, n, lo, hi, acc);
+    if (keep_logits) {
+      // p from the logits phase 3 left in LDS (lane = key group x head, the
+      // same arithmetic as from recomputed dot products)
+      const int slot = s_slot[c];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kb * 16 + 4 * g4 + e;
-        const float p = key < nk ? exp2_nonpos(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
-        if (col < G) s_p[w][key][col] = p;
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int key = kb * 16 + 4 * g4 + e;
+          if (col < G) {
+            const float x = s_logit[(slot * CP + key) * G + col];
+            s_p[w][key][col] = key < nk ? exp2_nonpos(fmaf(x, sl2, -mcol)) : 0.f;
+          }
+        }
+    } else {
+      floatx4 acc[NKB];
+      leaf_dots<T, D, NKB>(fq, kbase, knew, n, lo, hi, acc);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kb * 16 + 4 * g4 + e;
+          const float p = key < nk ? exp2_nonpos(fmaf(acc[kb][e], sl2, -mcol)) : 0.f;
+          if (col < G) s_p[w][key][col] = p;
+        }
+    }
     wave_sync();
     float acc_o[G][DPV];
 #pragma unroll
