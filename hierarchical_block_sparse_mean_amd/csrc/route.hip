@@ -95,15 +95,20 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_kernel(RouteArgs a) 
 // columns.
 // hb / xb: the rows (pitch PITCH elements) and exponents of a head, in LDS
 // or in global memory; lvl: the child level's first row there.
+// GATHER (rows in global memory, pitch D): a row tile is gathered as
+// 128-byte pieces, eight lanes per piece and eight rows per load (a load in
+// the MFMA operand layout, sixteen rows of 64 bytes, is served about three
+// times slower from L2), written to the wave's LDS tile (16 rows, pitch
+// PITCH) and read back in the operand layout.
 // Only G_Q of a tile's 16 columns carry query heads, so the results of
 // P = 16 / max(G_Q, 4) consecutive row tiles are packed into one accumulator
 // set (tile p's useful columns moved into lane bank(s) p by DPP row shifts)
 // before the scaling, the sibling LSE and the GQA sum, which then run once
 // per P tiles on lanes that all carry data.
-template <int D, int G, int PITCH>
+template <int D, int G, int PITCH, bool GATHER>
 __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const halfx8* fq, int eq_p, const _Float16* hb,
                                                  const int32_t* xb, int32_t lvl, int32_t m_child, int32_t tl,
-                                                 float sl2, int64_t* rows_out) {
+                                                 float sl2, int64_t* rows_out, _Float16* tile) {
   constexpr int NS = D / 32;
   constexpr int GP = G < 4 ? 4 : G;  // lanes per packed tile
   constexpr int P = 16 / GP;         // tiles per packed set
@@ -131,9 +136,31 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
       // are issued before the first product (the barrier keeps the
       // scheduler from sinking each load next to its use).
       halfx8 fa[NS];
+      if constexpr (GATHER) {
+        // load st: rows (lane / 8) + 8 (st % 2) of the tile, elements
+        // [64 (st / 2) + 8 (lane % 8), + 8): NS loads cover 16 rows x D
+        halfx8 gv[NS];
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
-        fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)PITCH + 32 * st + 8 * g);
+        for (int st = 0; st < NS; ++st) {
+          const int slot = (lane >> 3) + 8 * (st & 1);
+          const int rowg = 16 * rt + slot;
+          const int cg = rowg >> 1;
+          const int32_t rg = (cg < nA) ? 2 * s.cand[cg] + (rowg & 1) : 0x7fffffff;
+          const uint32_t rrg = (uint32_t)(lvl + ((rg < m_child && rg <= tl) ? rg : 0));
+          gv[st] = *reinterpret_cast<const halfx8*>(hb + rrg * (uint32_t)D + 64 * (st >> 1) + 8 * (lane & 7));
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+          *reinterpret_cast<halfx8*>(tile + ((lane >> 3) + 8 * (st & 1)) * PITCH + 64 * (st >> 1) + 8 * (lane & 7)) =
+              gv[st];
+        wave_sync();
+#pragma unroll
+        for (int st = 0; st < NS; ++st) fa[st] = *reinterpret_cast<const halfx8*>(tile + col * PITCH + 32 * st + 8 * g);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+          fa[st] = *reinterpret_cast<const halfx8*>(hb + rr * (uint32_t)PITCH + 32 * st + 8 * g);
+      }
       __builtin_amdgcn_sched_barrier(0);
       acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -200,6 +227,8 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
   constexpr float kLog2e = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ RouteLds s_r[kRouteWgWaves];
+  // each wave's tile of 16 gathered rows (levels below the LDS stage)
+  __shared__ __align__(16) _Float16 s_tile[kRouteWgWaves][16 * SP];
   _Float16* s_rows = reinterpret_cast<_Float16*>(smem_raw);                             // [stage_rows][SP]
   int32_t* s_exs = reinterpret_cast<int32_t*>(smem_raw + (size_t)a.stage_rows * SP * 2);  // [stage_rows]
   const int w = threadIdx.x / kWave, lane = lane_id();
@@ -228,7 +257,7 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
   const int64_t tstep = (int64_t)a.chunks * kRouteWgWaves;
   // diagnostics only: queries, scored candidates, rows, scored levels, kept
   // blocks of this wave, added to the counters once at the end
-  unsigned long long w_q = 0, w_cands = 0, w_rows_sum = 0, w_levels = 0, w_kept = 0;
+  unsigned long long w_q = 0, w_cands = 0, w_rows_sum = 0, w_levels = 0, w_kept = 0, w_rows_mem = 0;
   for (int64_t t = (int64_t)chunk * kRouteWgWaves + w; t < a.N; t += tstep) {
     // B operand: column col = query head col of the group (zero beyond G_Q),
     // scaled by 2^-eq into fp16 (exact for bf16 values)
@@ -263,8 +292,9 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
     if (lane == 0) s.cand[0] = 0;
     int32_t kept = (lane == 0) ? 0 : -1;
     int nI = 1;
-    int64_t w_rows = 0;  // diagnostics only
+    int64_t w_rows = 0, w_rows_lds = 0;  // diagnostics only
     int64_t* rows_ptr = CNT ? &w_rows : nullptr;
+    int64_t* rows_lds_ptr = CNT ? &w_rows_lds : nullptr;
     wave_sync();
     const int32_t tc = (int32_t)t / a.C;
     for (int32_t l = a.L; l >= 2; --l) {
@@ -284,10 +314,10 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
         const int32_t tl = causal ? (tc >> (l - 2)) : 0x7fffffff;
         const int32_t lvl = (int32_t)a.geo.level_off[l - 1];
         if (l - 1 >= a.stage_level && l - 1 <= a.stage_top)
-          score_level_mfma<D, G, SP>(s, nA, fq, eq_p, s_rows, s_exs, lvl - (int32_t)a.stage_off, m_child, tl, sl2,
-                                     rows_ptr);
+          score_level_mfma<D, G, SP, false>(s, nA, fq, eq_p, s_rows, s_exs, lvl - (int32_t)a.stage_off, m_child, tl,
+                                            sl2, rows_lds_ptr, nullptr);
         else
-          score_level_mfma<D, G, D>(s, nA, fq, eq_p, hb, xb, lvl, m_child, tl, sl2, rows_ptr);
+          score_level_mfma<D, G, SP, true>(s, nA, fq, eq_p, hb, xb, lvl, m_child, tl, sl2, rows_ptr, s_tile[w]);
         w_cands += nA;
         w_levels += 1;
         wave_sync();
@@ -316,7 +346,8 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
     if (lane < a.K) a.idx[(bh * a.N + t) * a.K + lane] = (lane < nI) ? index_key_index(k2) : -1;
     if (CNT) {
       w_q += 1;
-      w_rows_sum += (unsigned long long)w_rows;
+      w_rows_sum += (unsigned long long)(w_rows + w_rows_lds);
+      w_rows_mem += (unsigned long long)w_rows;
       w_kept += (unsigned long long)nI;
     }
   }
@@ -324,6 +355,7 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
     atomicAdd(&a.counts[0], w_q);
     atomicAdd(&a.counts[1], w_cands);
     atomicAdd(&a.counts[2], w_rows_sum);
+    atomicAdd(&a.counts[5], w_rows_mem);
     atomicAdd(&a.counts[3], w_levels);
     atomicAdd(&a.counts[4], w_kept);
   }
@@ -336,7 +368,9 @@ __global__ __launch_bounds__(kRouteWgWaves* kWave) PISA_MFMA_REGS void route_mfm
 static void route_stage_plan(const Problem& p, RouteArgs& a, size_t& lds) {
   constexpr int wg_per_cu = 1;
   const size_t pitch_bytes = (size_t)(p.D + 8) * 2 + 4;  // padded fp16 row + exponent
-  const size_t budget = (size_t)144 * 1024;
+  // 160 KB per CU less the waves' candidate lists (1 KB each) and their
+  // gather tiles (16 rows of (D + 8) fp16 each)
+  const size_t budget = (size_t)160 * 1024 - (size_t)kRouteWgWaves * (1024 + 16 * (p.D + 8) * 2);
   a.stage_level = p.geo.levels_cap + 1;
   a.stage_top = p.geo.levels_cap;
   a.stage_rows = 0;

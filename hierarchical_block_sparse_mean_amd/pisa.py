@@ -32,7 +32,7 @@ EXPORTS = [
     "pisa_pyramid_bytes", "pisa_levels", "pisa_level_rows", "pisa_level_offset", "pisa_build_pyramid",
     "pisa_select_workspace_bytes", "pisa_select", "pisa_attn_workspace_bytes", "pisa_sparse_attn",
     "pisa_attn_backward_workspace_bytes", "pisa_sparse_attn_backward", "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
-    "pisa_route_counts", "pisa_select_noalloc",
+    "pisa_route_counts", "pisa_select_noalloc", "pisa_probe_gather",
     "pisa_last_error", "pisa_version",
 ]
 
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
         "pisa_select_workspace_bytes": ([P], sz),
         "pisa_select": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_select_noalloc": ([P, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "pisa_probe_gather": ([vp, i64, i32, i32, i32, i64, vp, vp], ctypes.c_int),
         "pisa_attn_workspace_bytes": ([P], sz),
         "pisa_sparse_attn": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_attn_backward_workspace_bytes": ([P], sz),
@@ -404,14 +405,22 @@ def timer_report() -> dict:
 
 def route_counts(p: Problem, q, k, pyr, ws=None, stream=None) -> dict:
     """Work counters of the stage-1 routing kernel (diagnostic run)."""
-    counts = torch.zeros(5, dtype=torch.int64, device=q.device)
+    counts = torch.zeros(6, dtype=torch.int64, device=q.device)
     if ws is None:
         ws = workspace(select_workspace_bytes(p), q.device)
     _check(load().pisa_route_counts(ctypes.byref(p.c()), q.data_ptr(), k.data_ptr(), pyr.data_ptr(),
                                     counts.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
     c = counts.cpu().tolist()
-    return {"queries": c[0], "scored_candidates": c[1], "child_rows": c[2], "scored_levels": c[3], "kept_level2": c[4]}
+    return {"queries": c[0], "scored_candidates": c[1], "child_rows": c[2], "scored_levels": c[3], "kept_level2": c[4],
+            "child_rows_from_memory": c[5]}
 
 
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+def probe_gather(table: torch.Tensor, rows_per_head: int, heads: int, D: int, workgroups: int, tiles_per_wave: int,
+                 sink: torch.Tensor, stream=None) -> None:
+    """Measurement probe: pisa_probe_gather over an fp16 table [heads][rows][D]."""
+    _check(load().pisa_probe_gather(table.data_ptr(), rows_per_head, heads, D, workgroups, tiles_per_wave,
+                                    sink.data_ptr(), _stream(stream)))

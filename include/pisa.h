@@ -247,13 +247,29 @@ int32_t pisa_timer_report(char* buf, size_t cap);
 
 /* Work counters of the bf16 stage-1 routing kernel (the same kernel as
  * pisa_select's stage 1, with counting enabled): adds to the device uint64
- * counts[5] (caller-zeroed) the number of (query, KV head) routed, the
- * candidates scored at levels >= 2, the valid child summary rows gathered,
- * the levels scored, and the kept level-2 blocks.  ws: at least
+ * counts[6] (caller-zeroed) the number of (query, KV head) routed, the
+ * candidates scored at levels >= 2, the valid child summary rows read, the
+ * levels scored, the kept level-2 blocks, and the valid child rows among
+ * those read from device memory (the rest come from the coarse levels the
+ * kernel stages in LDS).  ws: at least
  * pisa_select_workspace_bytes(p) bytes (its first part receives the kept
  * level-2 blocks).  For measurement only; not part of the hot path.          */
 pisa_status pisa_route_counts(const pisa_problem* p, const void* q, const void* k, const float* pyr,
                               uint64_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Measurement probe, not part of the method: gathers tiles of 16 fp16 rows
+ * of D elements at pseudo-random rows of a table, loaded the way stage-1
+ * routing loads the child summaries it does not hold in LDS (128-byte pieces
+ * of a row per eight lanes, then through an LDS tile into the MFMA operand
+ * layout), so that a benchmark can time the on-chip gather rate stage 1 is
+ * bounded by.
+ * table: device fp16 [heads][rows_per_head][D] (D 64 or 128); workgroups of
+ * 16 waves, workgroup i reading head i % heads; every wave gathers
+ * tiles_per_wave tiles (a multiple of 4), i.e. tiles_per_wave * 16 * D * 2
+ * bytes; sink: device uint32 [workgroups * 16 * 64] receives checksums.
+ * Returns PISA_ERR_INVALID_ARG for a bad argument (nothing launched).       */
+pisa_status pisa_probe_gather(const void* table, int64_t rows_per_head, int32_t heads, int32_t D,
+                              int32_t workgroups, int64_t tiles_per_wave, uint32_t* sink, hipStream_t stream);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* pisa_last_error(void);

@@ -40,6 +40,11 @@ CASES = {
     # K = 16 over an odd number of (b, h, t) rows: the final top-K takes two
     # rows per wave, so the last wave holds one
     "f32_k16_odd_rows": I.Workload("f32_k16_odd_rows", 1, 1001, 4, 1, 64, 32, 16, "f32", True, seed=18),
+    # pyramids larger than stage 1's LDS stage (about 268 summary rows at
+    # d = 128, 740 at d = 64): the finer levels are gathered from memory
+    "bf16_d64_gathered": I.Workload("bf16_d64_gathered", 1, 20000, 4, 2, 64, 32, 8, "bf16", True, seed=19),
+    "bf16_d128_gathered": I.Workload("bf16_d128_gathered", 1, 9000, 16, 4, 128, 16, 8, "bf16", True,
+                                     "leaf_per_query", seed=20),
 }
 # positions checked against the oracle (None = all)
 SAMPLED = {"bf16_c128_k32": np.unique(np.concatenate([np.arange(0, 300), np.arange(8292 - 200, 8292),
@@ -123,7 +128,7 @@ def test_select(name, algo):
 
 
 @pytest.mark.parametrize("name", ["bf16_g4_n4133", "bf16_g1_b2", "bf16_g2_d64", "bf16_g8", "bf16_g16_c32",
-                                  "bf16_c128_k32"])
+                                  "bf16_c128_k32", "bf16_d64_gathered"])
 def test_select_q_tile_schedules_identical(name):
     """Stage 2 with one 16-column tile per key-fragment read (q_tile = 16/G_Q)
     and with two (32/G_Q) computes every column identically: the same indices
@@ -298,9 +303,11 @@ def test_decode_capacity_flag():
     assert torch.equal(before, kc)
 
 
-def test_route_counts():
-    """The stage-1 work counters count what the oracle's descent counts."""
-    c = case_data("bf16_g4_n4133")
+@pytest.mark.parametrize("name", ["bf16_g4_n4133", "bf16_d128_gathered"])
+def test_route_counts(name):
+    """The stage-1 work counters count what the oracle's descent counts; rows
+    come from memory only where the pyramid is larger than the LDS stage."""
+    c = case_data(name)
     w = c["w"]
     p = _problem(w)
     pyr = pisa.build_pyramid(p, c["dev"]["k"])
@@ -310,3 +317,8 @@ def test_route_counts():
     # identical descents except on near-tied queries
     assert abs(rc["scored_candidates"] - cnt["scored_blocks"]) <= 0.002 * cnt["scored_blocks"]
     assert abs(rc["child_rows"] - cnt["child_dots"]) <= 0.002 * cnt["child_dots"]
+    if name == "bf16_g4_n4133":
+        assert rc["child_rows_from_memory"] == 0
+    else:
+        assert 0 < rc["child_rows_from_memory"] < rc["child_rows"]
+    log(f"[test_route_counts {name}] {rc}")
