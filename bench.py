@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--scaling", action="store_true",
                     help="selection-time scaling and PISA-vs-flat crossover at C=64, K=16 over --scaling-n")
     ap.add_argument("--scaling-n", default="32768,65536,131072,262144,524288,1048576")
+    ap.add_argument("--scaling-positions", type=int, default=48,
+                    help="query positions per N checked against the oracle in the scaling leg")
     ap.add_argument("--backward", action="store_true",
                     help="sparse-attention forward + backward over the workload's selection")
     ap.add_argument("--io", action="store_true",
@@ -594,13 +596,41 @@ def main() -> int:
     return 0
 
 
+def scaling_parity(w, data, idx, score, o, n_pos: int) -> dict:
+    """The GPU's selection and attention at n_pos sampled positions (the
+    first and last leaves included) against the oracle: non-exempt set
+    mismatches (sets must match except where the oracle's K-th and (K+1)-th
+    scores at some scored level are within 1e-3), reported-score error, and
+    attention on the GPU's own selection."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(w.N)
+    ts = np.unique(np.concatenate([[0, w.C - 1, w.C, w.N - 1], rng.integers(0, w.N, n_pos)]))
+    op = oracle.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal)
+    r_idx, r_score, r_gap, _ = oracle.select(op, data["q"], data["k"], ts=ts)
+    g_idx = idx.cpu().numpy()[:, :, ts]
+    g_score = score.cpu().numpy()[:, :, ts].astype(np.float64)
+    same = (g_idx == r_idx).all(-1)
+    exempt = r_gap < 1e-3
+    m = same[..., None] & (r_idx >= 0)
+    serr = float((np.abs(g_score[m] - r_score[m]) / np.maximum(1.0, np.abs(r_score[m]))).max()) if m.any() else 0.0
+    r_o, _ = oracle.attention(op, data["q"], data["k"], data["v"], g_idx, ts=ts)
+    aerr = float(np.abs(o.float().cpu().numpy()[:, :, ts].astype(np.float64) - r_o).max())
+    return {"positions": int(len(ts)), "non_exempt_mismatches": int((~same & ~exempt).sum()),
+            "exempt_fraction": round(float(exempt.mean()), 4), "exact_match_rate": round(float(same.mean()), 4),
+            "max_score_rel_err": serr, "max_attn_abs_err_on_gpu_selection": aerr}
+
+
 def scaling_main(args) -> int:
     """Selection time against N at fixed C = 64, K = 16 (Hq = 32, Hkv = 8,
     d = 128, bf16, causal, planted needle leaves as in the 32K/128K workloads):
     pyramid + two-stage select, the flat selector, and attention, each timed
-    with HIP events over --steps repetitions after one warm-up.  Prints one
-    JSON line with the table, log-log slopes and the interpolated N where the
-    flat selector becomes slower than PISA's."""
+    with HIP events over --steps repetitions after one warm-up, then each N's
+    selection and attention checked against the oracle on sampled positions.
+    Prints one JSON line with the table, log-log slopes and the interpolated
+    N where the flat selector becomes slower than PISA's."""
     import numpy as np
     import torch
 
@@ -613,7 +643,6 @@ def scaling_main(args) -> int:
         t0 = time.perf_counter()
         data = I.generate(w)
         q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
-        del data
         log(f"N={N}: inputs ready in {time.perf_counter() - t0:.1f}s")
         p = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True, dtype="bf16")
         pyr = pisa.alloc_pyramid(p)
@@ -649,13 +678,20 @@ def scaling_main(args) -> int:
         flat_ms = timed(flat)
         attn_ms = timed(lambda: pisa.sparse_attn(p, q, k, v, idx, o=o, lse=None, ws=aws, with_lse=False))
         rc = pisa.route_counts(p, q, k, pyr)
+        # sampled check of this N's selection and attention against the oracle
+        # (the timed calls above left their outputs in idx, score and o)
+        sel()
+        pisa.sparse_attn(p, q, k, v, idx, o=o, lse=None, ws=aws, with_lse=False)
+        torch.cuda.synchronize()
+        par = scaling_parity(w, data, idx, score, o, args.scaling_positions)
         rows.append({"N": N, "levels": pisa.levels(N, w.C), "select_ms": round(sel_ms, 4),
                      "flat_select_ms": round(flat_ms, 4), "attention_ms": round(attn_ms, 4),
                      "step_ms": round(sel_ms + attn_ms, 4),
                      "child_rows_per_query": round(rc["child_rows"] / max(1, rc["queries"]), 2),
-                     "flat_leaves_per_query": round((pisa.level_rows(N, w.C, 1) + 1) / 2, 1)})
-        log(f"N={N}: select {sel_ms:.3f} ms, flat {flat_ms:.3f} ms, attention {attn_ms:.3f} ms")
-        del q, k, v, pyr, ws, aws, idx, score, fidx, fscore, fws, o
+                     "flat_leaves_per_query": round((pisa.level_rows(N, w.C, 1) + 1) / 2, 1),
+                     "parity": par})
+        log(f"N={N}: select {sel_ms:.3f} ms, flat {flat_ms:.3f} ms, attention {attn_ms:.3f} ms; parity {par}")
+        del q, k, v, pyr, ws, aws, idx, score, fidx, fscore, fws, o, data
         torch.cuda.empty_cache()
     ln = np.log([r["N"] for r in rows])
     slope = lambda key: float(np.polyfit(ln, np.log([r[key] for r in rows]), 1)[0]) if len(rows) > 1 else None
