@@ -851,6 +851,12 @@ def io_main(args) -> int:
                          "kernels": {kk: round(vv[1] / max(1, vv[0]), 4) for kk, vv in kern.items()}}
             log(f"G_Q={G} {name}: {out[name]['ms']:.3f} ms {out[name]['kernels']}")
             del pyr, ws, idx, score
+        # (query, candidate leaf) pairs both schedules score: the two leaves of
+        # every level-2 block stage 1 keeps
+        pc = pisa.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=True, dtype="bf16")
+        pyr_c = pisa.build_pyramid(pc, k)
+        rc = pisa.route_counts(pc, q, k, pyr_c)
+        del pyr_c
         same = float((out["two_stage"]["idx"] == out["one_stage"]["idx"]).all(-1).mean())
         same_qt = bool(np.array_equal(out["two_stage"]["idx"], out["two_stage_q16"]["idx"]))
         d, C, qt, chunk = w.D, w.C, 4, 1024
@@ -859,6 +865,7 @@ def io_main(args) -> int:
             "two_stage_ms": round(out["two_stage"]["ms"], 4), "one_stage_ms": round(out["one_stage"]["ms"], 4),
             "two_stage_kernels_ms": out["two_stage"]["kernels"], "one_stage_kernels_ms": out["one_stage"]["kernels"],
             "same_selection_rate": round(same, 5),
+            "queries": rc["queries"], "candidate_leaf_pairs": 2 * rc["kept_level2"],
             "q_tile_sweep": {
                 "q_tile": [16 // G, 32 // G],
                 "leaf_score_ms": [out["two_stage_q16"]["kernels"].get("leaf_score"),
