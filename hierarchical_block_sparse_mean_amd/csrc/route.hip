@@ -123,10 +123,13 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
       // invalid row (or a tile past the last) reads row 0 of the level
       // (finite data) and gets scale 0 and bias -inf below.  Offsets within
       // a head fit 32 bits.
+      // (rows < 64: candidate reads stay inside s.cand and need no branch)
       const int rt = rt0 + q;
       const int row = 16 * rt + col;
       const int c = row >> 1;
-      const int32_t r = (c < nA) ? 2 * s.cand[c] + (row & 1) : 0x7fffffff;
+      int32_t cv = s.cand[c & (kWave - 1)];
+      asm volatile("" : "+v"(cv));  // read unconditionally (not sunk into a branch)
+      const int32_t r = (c < nA) ? 2 * cv + (row & 1) : 0x7fffffff;
       const bool vrow = r < m_child && r <= tl;  // exists and starts at or before t
       if (rows_out != nullptr && rt < nt) *rows_out += __popcll(__ballot(vrow) & 0xFFFFull);
       const uint32_t rr = (uint32_t)(lvl + (vrow ? r : 0));
@@ -139,16 +142,20 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
       if constexpr (GATHER) {
         // load st: rows (lane / 8) + 8 (st % 2) of the tile, elements
         // [64 (st / 2) + 8 (lane % 8), + 8): NS loads cover 16 rows x D
+        // the lane's two rows: slot lane / 8 (loads st even) and lane / 8 + 8
+        // (loads st odd), both of parity (lane / 8) % 2
+        const int row_a = 16 * rt + (lane >> 3), row_b = row_a + 8;
+        int32_t ca = s.cand[(row_a >> 1) & (kWave - 1)], cb = s.cand[(row_b >> 1) & (kWave - 1)];
+        asm volatile("" : "+v"(ca), "+v"(cb));
+        const int32_t ra = ((row_a >> 1) < nA) ? 2 * ca + (row_a & 1) : 0x7fffffff;
+        const int32_t rb = ((row_b >> 1) < nA) ? 2 * cb + (row_b & 1) : 0x7fffffff;
+        const uint32_t rra = (uint32_t)(lvl + ((ra < m_child && ra <= tl) ? ra : 0));
+        const uint32_t rrb = (uint32_t)(lvl + ((rb < m_child && rb <= tl) ? rb : 0));
         halfx8 gv[NS];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          const int slot = (lane >> 3) + 8 * (st & 1);
-          const int rowg = 16 * rt + slot;
-          const int cg = rowg >> 1;
-          const int32_t rg = (cg < nA) ? 2 * s.cand[cg] + (rowg & 1) : 0x7fffffff;
-          const uint32_t rrg = (uint32_t)(lvl + ((rg < m_child && rg <= tl) ? rg : 0));
-          gv[st] = *reinterpret_cast<const halfx8*>(hb + rrg * (uint32_t)D + 64 * (st >> 1) + 8 * (lane & 7));
-        }
+        for (int st = 0; st < NS; ++st)
+          gv[st] = *reinterpret_cast<const halfx8*>(hb + ((st & 1) ? rrb : rra) * (uint32_t)D + 64 * (st >> 1) +
+                                                    8 * (lane & 7));
 #pragma unroll
         for (int st = 0; st < NS; ++st)
           *reinterpret_cast<halfx8*>(tile + ((lane >> 3) + 8 * (st & 1)) * PITCH + 64 * (st >> 1) + 8 * (lane & 7)) =
