@@ -916,7 +916,7 @@ def decode_bytes_model(n: int, C: int, K: int, D: int, G: int, esz: int) -> dict
         "append": 2 * D * esz,
         "leaf_mean": (n - 1 - lo) * D * esz,
         "path": (L - 1) * D * 4 + L * (D * 4 + D * 2 + 4),
-        "summaries": summary_rows * D * 4,
+        "summaries": summary_rows * (D * 2 + 4),  # fp16 block-floating-point rows and their exponents
         "leaf_keys": max(leaf_keys, kept_keys) * D * esz,  # keys of the scored (or kept) leaves, read once
         "values": kept_keys * D * esz,
         "idx": 2 * K * 4,
