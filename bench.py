@@ -1036,9 +1036,11 @@ def decode_main(args, w) -> int:
     if dk:
         ach = per_launch / (dk["avg_ms"] * 1e-3) / 1e9
         roofline = {"kernel": "decode", "bound": "hbm", "achieved": round(ach, 2), "peak": PEAK["hbm_GBps"],
-                    "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 5), "traffic": None,
+                    "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 5), "traffic": traffic_for("decode", w.name),
                     "avg_launch_ms": round(dk["avg_ms"], 5), "work_per_launch": round(per_launch, 1),
                     "work_note": f"modelled bytes per (sequence, KV head) at n={w.N + 1}: {mid}"}
+        if roofline["traffic"]:
+            roofline["traffic_GBps"] = round(roofline["traffic"] / (dk["avg_ms"] * 1e-3) / 1e9, 1)
 
     # CPU oracle on a few sequences at the first and last timed step, with parity
     cpu = parity = None
