@@ -597,30 +597,35 @@ def main() -> int:
 
 
 def scaling_parity(w, data, idx, score, o, n_pos: int) -> dict:
-    """The GPU's selection and attention at n_pos sampled positions (the
-    first and last leaves included) against the oracle: non-exempt set
-    mismatches (sets must match except where the oracle's K-th and (K+1)-th
-    scores at some scored level are within 1e-3), reported-score error, and
-    attention on the GPU's own selection."""
+    """The GPU's selection (idx, score: tensors or host arrays of the whole
+    problem) and, unless o is None, its attention, at n_pos sampled
+    positions (the first and last leaves included) against the oracle:
+    non-exempt set mismatches (sets must match except where the oracle's
+    K-th and (K+1)-th scores at some scored level are within 1e-3),
+    reported-score error, and attention on the GPU's own selection."""
     import numpy as np
 
     import oracle
 
+    host = lambda x: x if isinstance(x, np.ndarray) else x.cpu().numpy()
     rng = np.random.default_rng(w.N)
     ts = np.unique(np.concatenate([[0, w.C - 1, w.C, w.N - 1], rng.integers(0, w.N, n_pos)]))
     op = oracle.Problem(w.B, w.N, w.Hq, w.Hkv, w.D, w.C, w.K, causal=w.causal)
     r_idx, r_score, r_gap, _ = oracle.select(op, data["q"], data["k"], ts=ts)
-    g_idx = idx.cpu().numpy()[:, :, ts]
-    g_score = score.cpu().numpy()[:, :, ts].astype(np.float64)
+    g_idx = host(idx)[:, :, ts]
+    g_score = host(score)[:, :, ts].astype(np.float64)
     same = (g_idx == r_idx).all(-1)
     exempt = r_gap < 1e-3
     m = same[..., None] & (r_idx >= 0)
     serr = float((np.abs(g_score[m] - r_score[m]) / np.maximum(1.0, np.abs(r_score[m]))).max()) if m.any() else 0.0
-    r_o, _ = oracle.attention(op, data["q"], data["k"], data["v"], g_idx, ts=ts)
-    aerr = float(np.abs(o.float().cpu().numpy()[:, :, ts].astype(np.float64) - r_o).max())
-    return {"positions": int(len(ts)), "non_exempt_mismatches": int((~same & ~exempt).sum()),
-            "exempt_fraction": round(float(exempt.mean()), 4), "exact_match_rate": round(float(same.mean()), 4),
-            "max_score_rel_err": serr, "max_attn_abs_err_on_gpu_selection": aerr}
+    out = {"positions": int(len(ts)), "non_exempt_mismatches": int((~same & ~exempt).sum()),
+           "exempt_fraction": round(float(exempt.mean()), 4), "exact_match_rate": round(float(same.mean()), 4),
+           "max_score_rel_err": serr}
+    if o is not None:
+        r_o, _ = oracle.attention(op, data["q"], data["k"], data["v"], g_idx, ts=ts)
+        out["max_attn_abs_err_on_gpu_selection"] = float(
+            np.abs(o.float().cpu().numpy()[:, :, ts].astype(np.float64) - r_o).max())
+    return out
 
 
 def scaling_main(args) -> int:
@@ -805,7 +810,8 @@ def io_main(args) -> int:
     (query, candidate leaf) of the pages' IO comparison (one-stage: C key rows;
     two-stage: G_Q query rows + C / Q_tile key rows, Q_tile = 4) next to this
     design's (G_Q query rows + 2C key rows shared by the queries of a cluster
-    chunk)."""
+    chunk).  Both schedules' selections are checked against the oracle at
+    sampled positions (--scaling-positions of them) for each G_Q."""
     import numpy as np
     import torch
 
@@ -818,7 +824,6 @@ def io_main(args) -> int:
         w = I.Workload(f"io_g{G}", 1, 131072, 32, hkv, 128, 64, 16, "bf16", True, "leaf_per_query", seed=2000)
         data = I.generate(w, with_v=False)
         q, k = dev(data["q"]), dev(data["k"])
-        del data
         out = {}
         # two-stage at both Q_tile values (queries sharing one read of a key
         # fragment from LDS: one 16-column MFMA tile = 16/G_Q, two = 32/G_Q)
@@ -848,6 +853,7 @@ def io_main(args) -> int:
             kern = pisa.timer_report()
             pisa.timer_enable(False)
             out[name] = {"ms": e0.elapsed_time(e1) / args.steps, "idx": idx.cpu().numpy(),
+                         "score": score.cpu().numpy(),
                          "kernels": {kk: round(vv[1] / max(1, vv[0]), 4) for kk, vv in kern.items()}}
             log(f"G_Q={G} {name}: {out[name]['ms']:.3f} ms {out[name]['kernels']}")
             del pyr, ws, idx, score
@@ -859,12 +865,16 @@ def io_main(args) -> int:
         del pyr_c
         same = float((out["two_stage"]["idx"] == out["one_stage"]["idx"]).all(-1).mean())
         same_qt = bool(np.array_equal(out["two_stage"]["idx"], out["two_stage_q16"]["idx"]))
+        parity = {nm: scaling_parity(w, data, out[nm]["idx"], out[nm]["score"], None, args.scaling_positions)
+                  for nm in ("two_stage", "one_stage")}
+        log(f"G_Q={G} oracle check: {parity}")
         d, C, qt, chunk = w.D, w.C, 4, 1024
         rows.append({
             "G_Q": G, "Hkv": hkv,
             "two_stage_ms": round(out["two_stage"]["ms"], 4), "one_stage_ms": round(out["one_stage"]["ms"], 4),
             "two_stage_kernels_ms": out["two_stage"]["kernels"], "one_stage_kernels_ms": out["one_stage"]["kernels"],
             "same_selection_rate": round(same, 5),
+            "parity": parity,
             "queries": rc["queries"], "candidate_leaf_pairs": 2 * rc["kept_level2"],
             "q_tile_sweep": {
                 "q_tile": [16 // G, 32 // G],
@@ -875,7 +885,7 @@ def io_main(args) -> int:
             "leaf_bytes_per_pair": {"one_stage": C * d * 2, "two_stage_pages": (G + C // qt) * d * 2,
                                     "two_stage_here": round(G * d * 2 + 2 * C * d * 2 / chunk, 1)},
         })
-        del q, k
+        del q, k, data
         torch.cuda.empty_cache()
     line = {
         "metric": "PISA one-stage vs two-stage selection ms at N=131072, G_Q in {4, 16}, 1 GPU",
