@@ -2,8 +2,9 @@
 benchmark times (default schedules, whole problem in one call), checked on
 sampled query positions the oracle computes one by one:
 
-* prefill N=32768 and N=131072 (C=64, K=16, planted needle leaves) and
-  N=262144 (C=128, K=32, shared needle spans): selection, reported scores,
+* prefill N=32768 and N=131072 (C=64, K=16, planted needle leaves, G_Q=4;
+  at N=131072 also G_Q=16, Hkv=2) and N=262144 (C=128, K=32, shared needle
+  spans): selection, reported scores,
   the GPU's own sets (scores of its leaves, top-K of the children of its
   kept level-2 blocks), attention fed by the GPU's own selection at every
   sampled position, and the flat selector;
@@ -35,10 +36,15 @@ def _positions(w: I.Workload, n_mid: int, seed: int) -> np.ndarray:
     return np.unique(np.concatenate([edge, mid]))
 
 
+# the 128K workload with sixteen query heads per KV head (Hkv = 2)
+G16 = I.Workload("prefill_128k_g16", 1, 131072, 32, 2, 128, 64, 16, "bf16", True, "leaf_per_query", seed=2000)
+
+
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name,n_mid", [("prefill_32k", 512), ("prefill_128k", 384), ("prefill_256k", 192)])
+@pytest.mark.parametrize("name,n_mid", [("prefill_32k", 512), ("prefill_128k", 384), ("prefill_128k_g16", 256),
+                                        ("prefill_256k", 192)])
 def test_prefill_fullsize_sampled(name, n_mid):
-    w = I.WORKLOADS[name]
+    w = G16 if name == G16.name else I.WORKLOADS[name]
     log(f"[fullsize {name}] generating inputs")
     data = I.generate(w)
     q, k, v = (to_dev(data[x]) for x in ("q", "k", "v"))
