@@ -45,6 +45,14 @@ CASES = {
     "bf16_d64_gathered": I.Workload("bf16_d64_gathered", 1, 20000, 4, 2, 64, 32, 8, "bf16", True, seed=19),
     "bf16_d128_gathered": I.Workload("bf16_d128_gathered", 1, 9000, 16, 4, 128, 16, 8, "bf16", True,
                                      "leaf_per_query", seed=20),
+    # degenerate shapes: one-key leaves with a top-1 at every level, two- and
+    # three-key leaves (no whole 16-key block per leaf), a single token, and
+    # K = 1 over 64-key leaves
+    "f32_c1_k1": I.Workload("f32_c1_k1", 1, 300, 4, 2, 64, 1, 1, "f32", True, seed=31),
+    "bf16_c2_k3": I.Workload("bf16_c2_k3", 1, 257, 8, 2, 128, 2, 3, "bf16", False, seed=32),
+    "bf16_c3_k5": I.Workload("bf16_c3_k5", 1, 500, 4, 1, 64, 3, 5, "bf16", True, seed=33),
+    "f32_n1": I.Workload("f32_n1", 1, 1, 4, 1, 64, 64, 4, "f32", True, seed=34),
+    "bf16_k1_c64": I.Workload("bf16_k1_c64", 1, 2000, 8, 2, 128, 64, 1, "bf16", True, seed=35),
 }
 # positions checked against the oracle (None = all)
 SAMPLED = {"bf16_c128_k32": np.unique(np.concatenate([np.arange(0, 300), np.arange(8292 - 200, 8292),
@@ -227,6 +235,11 @@ DECODE = {
     "bf16_grow": (I.Workload("dec_bf16", 3, 1021, 8, 2, 128, 64, 4, "bf16", True, seed=21, steps=8)),
     "f32_dense": (I.Workload("dec_f32", 2, 500, 4, 1, 64, 64, 16, "f32", True, seed=22, steps=6)),
     "bf16_g4_c128": (I.Workload("dec_c128", 2, 2000, 16, 4, 128, 128, 8, "bf16", True, seed=23, steps=5)),
+    # two-key leaves (nine levels), K = 1 with G_Q = 8 (four waves), and a
+    # one-token prefix (a single-level pyramid that gains its second leaf)
+    "f32_c2_k3": (I.Workload("dec_c2_k3", 2, 301, 4, 1, 64, 2, 3, "f32", True, seed=26, steps=4)),
+    "bf16_k1_g8": (I.Workload("dec_k1_g8", 2, 700, 16, 2, 128, 32, 1, "bf16", True, seed=27, steps=3)),
+    "f32_n1": (I.Workload("dec_n1", 1, 1, 4, 1, 64, 64, 4, "f32", True, seed=28, steps=3)),
 }
 
 
