@@ -10,8 +10,8 @@ query head's dq row, one key's dk or dv row): max |GPU - oracle| over the row
 fp32 and 5e-2 for bf16 (the bf16 rounding of p and dS gives rows up to about
 3e-2 of their own magnitude, dq most), so that an error confined to rows of
 small gradient is not hidden by the largest ones.  Cases cover
-ragged N, N <= C, C = 48 / 32 / 128, every GQA width, D = 64, B = 2, causal
-and not, and leaves whose queries span several workgroup chunks."""
+ragged N, N <= C, C = 1 / 3 / 48 / 32 / 128, every GQA width, D = 64, B = 2,
+causal and not, and leaves whose queries span several workgroup chunks."""
 from __future__ import annotations
 
 import numpy as np
@@ -37,6 +37,9 @@ CASES = {
     "bf16_c128": I.Workload("bwd_bf16_c128", 1, 3000, 8, 2, 128, 128, 8, "bf16", True, seed=86),
     "bf16_d64_b2_g2": I.Workload("bwd_bf16_d64", 2, 1500, 4, 2, 64, 64, 8, "bf16", False, seed=87),
     "bf16_g1_g8": I.Workload("bwd_bf16_g8", 1, 2100, 16, 2, 128, 64, 8, "bf16", True, seed=88),
+    # one- and three-key leaves
+    "f32_c1_k2": I.Workload("bwd_f32_c1", 1, 200, 4, 2, 64, 1, 2, "f32", True, seed=90),
+    "bf16_c3_k5": I.Workload("bwd_bf16_c3", 1, 500, 4, 1, 64, 3, 5, "bf16", True, seed=91),
 }
 
 
