@@ -287,6 +287,17 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
     }
   }
   __syncthreads();
+  // this lane's slice of the G query rows (dims sub*DL .. +DL), held in
+  // registers through the descent where they fit
+  constexpr int DLq = D / 8;
+  constexpr bool QREG = G * DLq <= 64;
+  float qr[QREG ? G : 1][QREG ? DLq : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < DLq; ++e) qr[g][e] = s_q[g * D + (lane & 7) * DLq + e];
+  }
   for (;;) {
     const int l = s_state[0], nA = s_state[1];
     if (l < 2) break;
@@ -300,15 +311,17 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
       for (int base = 0; base < 2 * nA; base += NW * 8) {
         const int rr = base + w * 8 + (lane >> 3);
         const int i = rr >> 1;
-        const int64_t r = (i < nA) ? 2 * (int64_t)s_cand[i] + (rr & 1) : -1;
+        int32_t ci = s_cand[i & (kDecMaxCand - 1)];
+        asm volatile("" : "+v"(ci));
+        const int64_t r = (i < nA) ? 2 * (int64_t)ci + (rr & 1) : -1;
         const bool valid = i < nA && r < m_child;
+        const int64_t rl = valid ? r : 0;  // rows past the list load row 0 (results dropped below)
         float dot[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) dot[g] = 0.f;
-        int32_t er = 0;
-        if (valid) {
-          const _Float16* row = child_level + r * D + sub * DL;
-          er = child_ex[r];
+        int32_t er = child_ex[rl];
+        {
+          const _Float16* row = child_level + rl * D + sub * DL;
           float rv[DL];
 #pragma unroll
           for (int e = 0; e < DL; e += 8) {
@@ -320,7 +333,9 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
           for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < DL; e += 4) {
-              const float4 qv = *reinterpret_cast<const float4*>(s_q + g * D + sub * DL + e);
+              float4 qv;
+              if constexpr (QREG) qv = float4{qr[g][e], qr[g][e + 1], qr[g][e + 2], qr[g][e + 3]};
+              else qv = *reinterpret_cast<const float4*>(s_q + g * D + sub * DL + e);
               dot[g] = fmaf(rv[e], qv.x, dot[g]);
               dot[g] = fmaf(rv[e + 1], qv.y, dot[g]);
               dot[g] = fmaf(rv[e + 2], qv.z, dot[g]);
