@@ -115,8 +115,25 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
   const int lane = lane_id(), g = lane >> 4, col = lane & 15;
   const int qp = col / GP, hc = col % GP;  // packed: tile qp of the set, head hc
   const int nt = (2 * nA + 15) >> 4;      // row tiles of this level
+  // gathers of row tile rtg into gv: rows (lane / 8) + 8 (st % 2) of the
+  // tile, elements [64 (st / 2) + 8 (lane % 8), + 8)
+  auto gather = [&](int rtg, halfx8* gv) {
+    const int row_a = 16 * rtg + (lane >> 3), row_b = row_a + 8;
+    int32_t ca = s.cand[(row_a >> 1) & (kWave - 1)], cb = s.cand[(row_b >> 1) & (kWave - 1)];
+    asm volatile("" : "+v"(ca), "+v"(cb));
+    const int32_t ra = ((row_a >> 1) < nA) ? 2 * ca + (row_a & 1) : 0x7fffffff;
+    const int32_t rb = ((row_b >> 1) < nA) ? 2 * cb + (row_b & 1) : 0x7fffffff;
+    const uint32_t rra = (uint32_t)(lvl + ((ra < m_child && ra <= tl) ? ra : 0));
+    const uint32_t rrb = (uint32_t)(lvl + ((rb < m_child && rb <= tl) ? rb : 0));
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      gv[st] = *reinterpret_cast<const halfx8*>(hb + ((st & 1) ? rrb : rra) * (uint32_t)D + 64 * (st >> 1) +
+                                                8 * (lane & 7));
+  };
   for (int rt0 = 0; rt0 < nt; rt0 += P) {
     floatx4 acc[P];
+    halfx8 gv_next[NS];
+    if constexpr (GATHER) gather(rt0, gv_next);
 #pragma unroll
     for (int q = 0; q < P; ++q) {
       // A row `col` of tile rt: child (row & 1) of candidate row >> 1; an
@@ -140,22 +157,12 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
       // scheduler from sinking each load next to its use).
       halfx8 fa[NS];
       if constexpr (GATHER) {
-        // load st: rows (lane / 8) + 8 (st % 2) of the tile, elements
-        // [64 (st / 2) + 8 (lane % 8), + 8): NS loads cover 16 rows x D
-        // the lane's two rows: slot lane / 8 (loads st even) and lane / 8 + 8
-        // (loads st odd), both of parity (lane / 8) % 2
-        const int row_a = 16 * rt + (lane >> 3), row_b = row_a + 8;
-        int32_t ca = s.cand[(row_a >> 1) & (kWave - 1)], cb = s.cand[(row_b >> 1) & (kWave - 1)];
-        asm volatile("" : "+v"(ca), "+v"(cb));
-        const int32_t ra = ((row_a >> 1) < nA) ? 2 * ca + (row_a & 1) : 0x7fffffff;
-        const int32_t rb = ((row_b >> 1) < nA) ? 2 * cb + (row_b & 1) : 0x7fffffff;
-        const uint32_t rra = (uint32_t)(lvl + ((ra < m_child && ra <= tl) ? ra : 0));
-        const uint32_t rrb = (uint32_t)(lvl + ((rb < m_child && rb <= tl) ? rb : 0));
+        // this tile's rows arrived in gv_next; the next tile's loads are
+        // issued before they are stored, so two tiles are in flight
         halfx8 gv[NS];
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
-          gv[st] = *reinterpret_cast<const halfx8*>(hb + ((st & 1) ? rrb : rra) * (uint32_t)D + 64 * (st >> 1) +
-                                                    8 * (lane & 7));
+        for (int st = 0; st < NS; ++st) gv[st] = gv_next[st];
+        if (q + 1 < P) gather(rt + 1, gv_next);
 #pragma unroll
         for (int st = 0; st < NS; ++st)
           *reinterpret_cast<halfx8*>(tile + ((lane >> 3) + 8 * (st & 1)) * PITCH + 64 * (st >> 1) + 8 * (lane & 7)) =
