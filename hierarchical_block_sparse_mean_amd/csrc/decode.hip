@@ -53,6 +53,9 @@ constexpr int kDecMaxCand = 64;  // 2K, K <= 32
 // (2K candidates x C keys x G_Q heads; 32 KB: K = 16, C = 64, G_Q = 4);
 // larger problems recompute the kept leaves' logits from their keys
 constexpr int kDecLogitFloats = 8192;
+// value rows per lane whose loads are in flight together in the attention
+// phase (8 would spill at d = 128, G_Q = 4)
+constexpr int kVRows = 4;
 
 // N consecutive elements (N = 4 or 8) as fp32
 template <typename T, int N>
@@ -508,16 +511,35 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < DPV; ++e) acc_o[g][e] = 0.f;
-#pragma unroll 4
-    for (int kk = rg; kk < nk; kk += RPI) {
-      const int64_t r = lo + kk;
-      float vv[DPV];
-      load_vec<T, DPV>((r == n ? vnew : vbase + r * D) + dl, vv);
+    // kVRows value rows per lane in flight: every load of a batch is issued
+    // before the first is used (rows past the leaf re-read row rg, which
+    // exists whenever the loop runs); each lane's DPV elements of a row are
+    // read as 16- or 8-byte pieces
+    using Piece = std::conditional_t<(DPV * sizeof(T)) % 16 == 0, uint4, uint2>;
+    constexpr int NPC = (int)(DPV * sizeof(T) / sizeof(Piece));
+    for (int kk0 = rg; kk0 < nk; kk0 += kVRows * RPI) {
+      Piece raw[kVRows][NPC];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pg = s_p[w][kk][g];
+      for (int u = 0; u < kVRows; ++u) {
+        const int kk = kk0 + u * RPI < nk ? kk0 + u * RPI : rg;
+        const int64_t r = lo + kk;
+        const Piece* src = reinterpret_cast<const Piece*>((r == n ? vnew : vbase + r * D) + dl);
 #pragma unroll
-        for (int e = 0; e < DPV; ++e) acc_o[g][e] = fmaf(pg, vv[e], acc_o[g][e]);
+        for (int x = 0; x < NPC; ++x) raw[u][x] = src[x];
+      }
+#pragma unroll
+      for (int u = 0; u < kVRows; ++u) {
+        const int kk = kk0 + u * RPI;
+        if (kk < nk) {
+          float vv[DPV];
+          load_vec<T, DPV>(reinterpret_cast<const T*>(raw[u]), vv);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pg = s_p[w][kk][g];
+#pragma unroll
+            for (int e = 0; e < DPV; ++e) acc_o[g][e] = fmaf(pg, vv[e], acc_o[g][e]);
+          }
+        }
       }
     }
 #pragma unroll
