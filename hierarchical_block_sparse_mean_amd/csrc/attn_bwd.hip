@@ -384,12 +384,14 @@ __global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void 
         if (pc >= 0) {
           const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (col % G);
           T* dst = static_cast<T*>(a.dq_part) + rec * D + db * 16 + 4 * g;
-          if constexpr (B16)
-            *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(dqt[0] * a.scale, dqt[1] * a.scale),
-                                                   pack_bf16x2(dqt[2] * a.scale, dqt[3] * a.scale)};
-          else
-            *reinterpret_cast<float4*>(dst) = float4{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale,
-                                                     dqt[3] * a.scale};
+          // (streaming stores: each partial row is read once, by the merge)
+          if constexpr (B16) {
+            store8_nt(dst, uint2{pack_bf16x2(dqt[0] * a.scale, dqt[1] * a.scale),
+                                 pack_bf16x2(dqt[2] * a.scale, dqt[3] * a.scale)});
+          } else {
+            const float4 x{dqt[0] * a.scale, dqt[1] * a.scale, dqt[2] * a.scale, dqt[3] * a.scale};
+            store16_nt(dst, &x);
+          }
         }
       }
     }
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdMergeArgs a) {
 #pragma unroll
       for (int u = 0; u < SG; ++u) {
         const int s = s0 + u;
-        if (s < a.K && ((okm >> s) & 1ull)) rows[u].load(part + (rec0 + s * G + hh) * D + d);
+        if (s < a.K && ((okm >> s) & 1ull)) rows[u].load_nt(part + (rec0 + s * G + hh) * D + d);
         else rows[u] = Row8<T>{};
       }
 #pragma unroll

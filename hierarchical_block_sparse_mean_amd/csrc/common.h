@@ -67,6 +67,22 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* out) {
   }
 }
 
+// Streaming (nontemporal) 16-byte store and load: data written once and read
+// once much later (partial records, outputs) marked so that it does not
+// displace the cached working set of the kernel that writes or reads it.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void* p, const void* src) {
+  __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(p));
+}
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8_nt(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{x.x, x.y, x.z, x.w};
+}
+
 // 8 consecutive elements of a row, as loaded (16 or 32 bytes), unpacked later
 template <typename T>
 struct Row8 {
@@ -75,6 +91,11 @@ struct Row8 {
     const uint4* q = reinterpret_cast<const uint4*>(p);
     v[0] = q[0];
     if constexpr (sizeof(T) == 4) v[1] = q[1];
+  }
+  // a streaming load (data read once)
+  __device__ __forceinline__ void load_nt(const T* p) {
+    v[0] = load16_nt(p);
+    if constexpr (sizeof(T) == 4) v[1] = load16_nt(p + 4);
   }
   __device__ __forceinline__ void get(float* out) const {
     if constexpr (sizeof(T) == 2) {

@@ -56,7 +56,55 @@ __global__ __launch_bounds__(kProbeWaves* kWave) void probe_gather_kernel(const 
   sink[((int64_t)blockIdx.x * kProbeWaves + w) * kWave + lane] = acc;
 }
 
+// Streaming probe (not part of the method): the HBM rate of plain 16-byte
+// streams, the ceiling the memory-bound kernels are compared with.  mode 0
+// reads `bytes` of src with streaming (nontemporal) loads, each thread
+// folding its 16-byte pieces into one word of sink; mode 1 copies src to dst;
+// unrolled by 4 so every lane keeps four 16-byte loads in flight, grid-stride
+// over the buffer.
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+
+__global__ __launch_bounds__(kStreamThreads) void probe_stream_kernel(const uint4* __restrict__ src,
+                                                                      uint4* __restrict__ dst, int64_t n16,
+                                                                      int32_t mode, uint32_t* __restrict__ sink) {
+  const int64_t tid = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  const int64_t nthreads = (int64_t)gridDim.x * kStreamThreads;
+  uint32_t acc = 0u;
+  int64_t i = tid;
+  for (; i + (kStreamUnroll - 1) * nthreads < n16; i += kStreamUnroll * nthreads) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = mode == 1 ? src[i + u * nthreads] : load16_nt(src + i + u * nthreads);
+    if (mode == 1) {
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) dst[i + u * nthreads] = v[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  }
+  for (; i < n16; i += nthreads) {
+    const uint4 v = src[i];
+    if (mode == 1) dst[i] = v;
+    else acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (mode == 0) sink[tid] = acc;
+}
+
 }  // namespace pisa
+
+extern "C" pisa_status pisa_probe_stream(const void* src, void* dst, int64_t bytes, int32_t mode,
+                                         int32_t workgroups, uint32_t* sink, hipStream_t stream) {
+  if (src == nullptr || bytes < 16 || bytes % 16 != 0 || workgroups < 1 || (mode != 0 && mode != 1) ||
+      (mode == 1 && dst == nullptr) || (mode == 0 && sink == nullptr) ||
+      (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+    return PISA_ERR_INVALID_ARG;
+  PISA_LAUNCH("probe_stream", stream, pisa::probe_stream_kernel, dim3((unsigned)workgroups),
+              dim3(pisa::kStreamThreads), 0, static_cast<const uint4*>(src), static_cast<uint4*>(dst), bytes / 16,
+              mode, sink);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
 
 extern "C" pisa_status pisa_probe_gather(const void* table, int64_t rows_per_head, int32_t heads, int32_t D,
                                          int32_t workgroups, int64_t tiles_per_wave, uint32_t* sink,

@@ -269,8 +269,8 @@ __global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_ker
       const float u1 = lane_group_sum<G>(u[tt][1]);
       if (g == 0 && hh == 0 && pr[tt] >= 0) {
         const int64_t e = (int64_t)(pr[tt] >> 5) * a.K + (pr[tt] & 31);  // (t, slot) entry
-        out_base[e * 2] = u0;
-        out_base[e * 2 + 1] = u1;
+        // (a streaming store: read once, by the final top-K)
+        __builtin_nontemporal_store(floatx2_t{u0, u1}, reinterpret_cast<floatx2_t*>(out_base + e * 2));
       }
     }
   };

@@ -32,7 +32,7 @@ EXPORTS = [
     "pisa_pyramid_bytes", "pisa_levels", "pisa_level_rows", "pisa_level_offset", "pisa_build_pyramid",
     "pisa_select_workspace_bytes", "pisa_select", "pisa_attn_workspace_bytes", "pisa_sparse_attn",
     "pisa_attn_backward_workspace_bytes", "pisa_sparse_attn_backward", "pisa_flat_workspace_bytes", "pisa_flat_select", "pisa_decode_step", "pisa_timer_enable", "pisa_timer_report",
-    "pisa_route_counts", "pisa_select_noalloc", "pisa_probe_gather",
+    "pisa_route_counts", "pisa_select_noalloc", "pisa_probe_gather", "pisa_probe_stream",
     "pisa_last_error", "pisa_version",
 ]
 
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH):
         "pisa_select": ([P, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_select_noalloc": ([P, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "pisa_probe_gather": ([vp, i64, i32, i32, i32, i64, vp, vp], ctypes.c_int),
+        "pisa_probe_stream": ([vp, vp, i64, i32, i32, vp, vp], ctypes.c_int),
         "pisa_attn_workspace_bytes": ([P], sz),
         "pisa_sparse_attn": ([P, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "pisa_attn_backward_workspace_bytes": ([P], sz),
@@ -424,3 +425,10 @@ def probe_gather(table: torch.Tensor, rows_per_head: int, heads: int, D: int, wo
     """Measurement probe: pisa_probe_gather over an fp16 table [heads][rows][D]."""
     _check(load().pisa_probe_gather(table.data_ptr(), rows_per_head, heads, D, workgroups, tiles_per_wave,
                                     sink.data_ptr(), _stream(stream)))
+
+
+def probe_stream(src: torch.Tensor, dst: torch.Tensor | None, nbytes: int, mode: int, workgroups: int,
+                 sink: torch.Tensor | None, stream=None) -> None:
+    """Measurement probe: pisa_probe_stream (mode 0 reads src, mode 1 copies src to dst)."""
+    _check(load().pisa_probe_stream(src.data_ptr(), _ptr(dst), nbytes, mode, workgroups, _ptr(sink),
+                                    _stream(stream)))

@@ -271,6 +271,17 @@ pisa_status pisa_route_counts(const pisa_problem* p, const void* q, const void* 
 pisa_status pisa_probe_gather(const void* table, int64_t rows_per_head, int32_t heads, int32_t D,
                               int32_t workgroups, int64_t tiles_per_wave, uint32_t* sink, hipStream_t stream);
 
+/* Measurement probe, not part of the method: plain 16-byte streams over a
+ * device buffer, so that a benchmark can time the HBM rate the memory-bound
+ * kernels are compared with.  mode 0 reads `bytes` of src and writes one
+ * checksum word per thread to sink (device uint32 [workgroups * 256]);
+ * mode 1 copies `bytes` of src to dst (sink unused).  bytes is a positive
+ * multiple of 16 and src / dst are 16-byte aligned device pointers; the
+ * grid is `workgroups` workgroups of 256 threads striding over the buffer.
+ * Returns PISA_ERR_INVALID_ARG for a bad argument (nothing launched).       */
+pisa_status pisa_probe_stream(const void* src, void* dst, int64_t bytes, int32_t mode, int32_t workgroups,
+                              uint32_t* sink, hipStream_t stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* pisa_last_error(void);
 /* Library version string (static storage). */
