@@ -390,6 +390,11 @@ template <>
 struct Frag<uint16_t> {
   bf16x8 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  // a streaming load (rows read once)
+  __device__ __forceinline__ void load_nt(const uint16_t* p) {
+    const uint4 u = load16_nt(p);
+    v = *reinterpret_cast<const bf16x8*>(&u);
+  }
   // elements 0..3 from p0, 4..7 from p1 (each 8-byte aligned)
   __device__ __forceinline__ void load4x2(const uint16_t* p0, const uint16_t* p1) {
     const uint2 a = *reinterpret_cast<const uint2*>(p0);
@@ -412,6 +417,12 @@ template <>
 struct Frag<float> {
   float v[8];
   __device__ __forceinline__ void load(const float* p) { load8<float>(p, v); }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    const uint4 a = load16_nt(p), b = load16_nt(p + 4);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
   __device__ __forceinline__ void load4x2(const float* p0, const float* p1) {
     const float4 a = *reinterpret_cast<const float4*>(p0);
     const float4 b = *reinterpret_cast<const float4*>(p1);

@@ -95,7 +95,7 @@ __device__ __forceinline__ void leaf_dots(const Frag<T>* fq, const T* kbase, con
     Frag<T> fk[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (r < nk) fk[s].load(row + 32 * s + 8 * g);  // contiguous 64-byte spans per row
+      if (r < nk) fk[s].load_nt(row + 32 * s + 8 * g);  // contiguous 64-byte spans per row (streamed)
       else fk[s].zero();
     }
     acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -525,7 +525,10 @@ __global__ __launch_bounds__(NW* kWave, (sizeof(T) == 2 && NKB <= 4) ? NW / 2 : 
         const int64_t r = lo + kk;
         const Piece* src = reinterpret_cast<const Piece*>((r == n ? vnew : vbase + r * D) + dl);
 #pragma unroll
-        for (int x = 0; x < NPC; ++x) raw[u][x] = src[x];
+        for (int x = 0; x < NPC; ++x) {
+          if constexpr (sizeof(Piece) == 16) raw[u][x] = load16_nt(src + x);  // streamed: read once per step
+          else raw[u][x] = src[x];
+        }
       }
 #pragma unroll
       for (int u = 0; u < kVRows; ++u) {
