@@ -84,7 +84,7 @@ static bool attn_pairs(const Problem& p) {
 struct AttnLayout {
   int64_t heads;  // (b, h) heads per chunk
   int64_t M1, Mk, Mb, ncl, slots, max_chunks;  // Mk: key blocks (leaves, then level-2 blocks); Mb: bins per head
-  size_t off_counts, off_cursor, off_offsets, off_chunks, off_map, off_pairs, off_m, off_l, off_o, off_hist, total;
+  size_t off_counts, off_cursor, off_offsets, off_chunks, off_map, off_pairs, off_ml, off_o, off_hist, total;
 };
 
 static AttnLayout attn_layout(const Problem& p) {
@@ -117,10 +117,8 @@ static AttnLayout attn_layout(const Problem& p) {
   off = a256(off + 4 * (size_t)L.max_chunks);
   L.off_pairs = off;
   off = a256(off + 4 * (size_t)L.slots);
-  L.off_m = off;
-  off = a256(off + 4 * (size_t)L.slots * p.G);
-  L.off_l = off;
-  off = a256(off + 4 * (size_t)L.slots * p.G);
+  L.off_ml = off;
+  off = a256(off + 8 * (size_t)L.slots * p.G);
   L.off_o = off;
   off = a256(off + osz * (size_t)L.slots * p.G * p.D);
   L.off_hist = off;
@@ -140,8 +138,7 @@ struct AttnLeafArgs {
   const int32_t* chunk_off;
   const int32_t* chunk_map;  // work chunk -> cluster
   const int32_t* pairs;
-  float* pm;   // [heads][N][K][G]
-  float* pl;
+  floatx2_t* pml;  // (m, l) [heads][N][K][G]
   void* po;    // [heads][N][K][G][D] (input dtype)
   int64_t ncl, M1, Mk, Mb, head0;
   int32_t N, Hq, Hkv, C, K;
@@ -298,8 +295,7 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
     }
     if (live && g == 0) {
       const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
-      __builtin_nontemporal_store(m, &a.pm[rec]);
-      __builtin_nontemporal_store(l, &a.pl[rec]);
+      __builtin_nontemporal_store(floatx2_t{m, l}, a.pml + rec);  // one 8-byte store per (query, slot, head)
     }
     wave_sync();
     {
@@ -356,8 +352,7 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
 // ---- merge the K partials of every (query, KV head) ---------------------------
 struct MergeArgs {
   const int32_t* idx;
-  const float* pm;
-  const float* pl;
+  const floatx2_t* pml;
   const void* po;
   void* o;
   float* lse;
@@ -397,8 +392,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int r = 0; r < MLP; ++r) {
     const int i = lane + r * kWave;
-    mv[r] = i < a.K * G ? __builtin_nontemporal_load(&a.pm[rec0 + i]) : 0.f;
-    lv[r] = i < a.K * G ? __builtin_nontemporal_load(&a.pl[rec0 + i]) : 0.f;
+    const floatx2_t ml = i < a.K * G ? __builtin_nontemporal_load(a.pml + rec0 + i) : floatx2_t{0.f, 0.f};
+    mv[r] = ml[0];
+    lv[r] = ml[1];
   }
   wave_sync();  // s_ok
   const T* po = static_cast<const T*>(a.po);
@@ -488,8 +484,7 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
   int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
-  float* pm = reinterpret_cast<float*>(base + L.off_m);
-  float* pl = reinterpret_cast<float*>(base + L.off_l);
+  floatx2_t* pml = reinterpret_cast<floatx2_t*>(base + L.off_ml);
   void* po = base + L.off_o;
   const int64_t BH = (int64_t)p.B * p.Hkv;
   for (int64_t head0 = 0; head0 < BH; head0 += L.heads) {
@@ -502,9 +497,9 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     if (err != hipSuccess) return err;
     err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
     if (err != hipSuccess) return err;
-    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, chunk_map, pairs, pm, pl, po, ncl, L.M1, L.Mk, L.Mb, head0,
+    AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, chunk_map, pairs, pml, po, ncl, L.M1, L.Mk, L.Mb, head0,
                     p.N, p.Hq, p.Hkv, p.C, p.K, attn_chunk(p), p.causal ? 1 : 0, p.cap, p.scale};
-    MergeArgs ma{idx, pm, pl, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K, pairs_on ? 1 : 0};
+    MergeArgs ma{idx, pml, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K, pairs_on ? 1 : 0};
     const int64_t max_chunks = (entries + attn_chunk(p) - 1) / attn_chunk(p) + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
       using T = std::remove_pointer_t<decltype(tp)>;
