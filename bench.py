@@ -110,7 +110,8 @@ def traffic_for(kernel: str, workload: str):
 def measured_ceilings() -> dict:
     """Ceilings measured on this GPU, next to the vendor peaks: a 1 GiB
     device-to-device copy by the platform (2 GiB of HBM traffic per copy), the
-    library's 16-byte streaming probe reading 2 GiB and copying 1 GiB, and a
+    library's 16-byte streaming probe reading 2 GiB and copying 1 GiB (best of
+    a few grid sizes), and a
     bf16 GEMM (8192^3, the platform BLAS), each timed with HIP events.  The
     HBM ceiling the memory-bound kernels are compared with (`hbm_GBps`) is the
     best of the three streams: mostly-read kernels exceed a copy's rate."""
@@ -139,8 +140,8 @@ def measured_ceilings() -> dict:
         return e0.elapsed_time(e1) / reps / 1000.0
 
     copy_s = timed(lambda: dst.copy_(half), 10)
-    read_s = min(timed(lambda: pisa.probe_stream(src, None, 2 << 30, 0, n, sink), 10) for n in (1024, wgs))
-    pcopy_s = timed(lambda: pisa.probe_stream(half, dst, 1 << 30, 1, wgs, None), 10)
+    read_s = min(timed(lambda: pisa.probe_stream(src, None, 2 << 30, 0, n, sink), 10) for n in (256, 512, 1024, wgs))
+    pcopy_s = min(timed(lambda: pisa.probe_stream(half, dst, 1 << 30, 1, n, None), 10) for n in (256, 1024, wgs))
     gemm_s = timed(lambda: torch.matmul(a, b), 10)
     del src, dst, a, b, sink, half
     torch.cuda.empty_cache()

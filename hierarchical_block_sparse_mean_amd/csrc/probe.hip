@@ -60,10 +60,11 @@ __global__ __launch_bounds__(kProbeWaves* kWave) void probe_gather_kernel(const 
 // streams, the ceiling the memory-bound kernels are compared with.  mode 0
 // reads `bytes` of src with streaming (nontemporal) loads, each thread
 // folding its 16-byte pieces into one word of sink; mode 1 copies src to dst;
-// unrolled by 4 so every lane keeps four 16-byte loads in flight, grid-stride
-// over the buffer.
+// unrolled by 8 so every lane keeps eight 16-byte loads in flight, grid-stride
+// over the buffer (the highest read rate here came from one workgroup per
+// compute unit: about 7.1 TB/s, against about 6 TB/s with sixteen).
 constexpr int kStreamThreads = 256;
-constexpr int kStreamUnroll = 4;
+constexpr int kStreamUnroll = 8;
 
 __global__ __launch_bounds__(kStreamThreads) void probe_stream_kernel(const uint4* __restrict__ src,
                                                                       uint4* __restrict__ dst, int64_t n16,
