@@ -133,7 +133,14 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
   for (int rt0 = 0; rt0 < nt; rt0 += P) {
     floatx4 acc[P];
     halfx8 gv_next[NS];
-    if constexpr (GATHER) gather(rt0, gv_next);
+    // the gathers are issued at a raised wave priority, so that the SIMD's
+    // other waves (sorting, scoring) do not delay the level's critical loads
+    // (stage 1 at 128K: 5.13 -> 5.05 ms)
+    if constexpr (GATHER) {
+      __builtin_amdgcn_s_setprio(2);
+      gather(rt0, gv_next);
+      __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int q = 0; q < P; ++q) {
       // A row `col` of tile rt: child (row & 1) of candidate row >> 1; an
@@ -162,7 +169,11 @@ __device__ __forceinline__ void score_level_mfma(RouteLds& s, int nA, const half
         halfx8 gv[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) gv[st] = gv_next[st];
-        if (q + 1 < P) gather(rt + 1, gv_next);
+        if (q + 1 < P) {
+          __builtin_amdgcn_s_setprio(2);
+          gather(rt + 1, gv_next);
+          __builtin_amdgcn_s_setprio(0);
+        }
 #pragma unroll
         for (int st = 0; st < NS; ++st)
           *reinterpret_cast<halfx8*>(tile + ((lane >> 3) + 8 * (st & 1)) * PITCH + 64 * (st >> 1) + 8 * (lane & 7)) =

@@ -207,3 +207,22 @@ def test_product_has_no_oracle_dependency():
                     text = f.read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "pisa_oracle" not in text and "libpisa_oracle" not in text, fn
+
+
+def test_probe_stream_host_checks(lib):
+    """The streaming probe rejects, before any launch, a missing source, a size
+    that is not a positive multiple of 16, an unknown mode, a missing
+    destination (copy) or sink (read), a bad grid and misaligned pointers."""
+    ok_ptr = ctypes.c_void_p(1 << 20)
+    bad = [
+        (None, ok_ptr, 1 << 20, 0, 4, ok_ptr),
+        (ok_ptr, ok_ptr, 0, 0, 4, ok_ptr),
+        (ok_ptr, ok_ptr, 1000, 0, 4, ok_ptr),
+        (ok_ptr, ok_ptr, 1 << 20, 2, 4, ok_ptr),
+        (ok_ptr, None, 1 << 20, 1, 4, None),
+        (ok_ptr, None, 1 << 20, 0, 4, None),
+        (ok_ptr, ok_ptr, 1 << 20, 0, 0, ok_ptr),
+        (ctypes.c_void_p((1 << 20) + 8), ok_ptr, 1 << 20, 1, 4, None),
+    ]
+    for src, dst, nbytes, mode, wgs, sink in bad:
+        assert lib.pisa_probe_stream(src, dst, nbytes, mode, wgs, sink, None) == pisa.PISA_ERR_INVALID_ARG
