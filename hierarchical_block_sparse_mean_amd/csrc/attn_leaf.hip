@@ -38,6 +38,13 @@ namespace pisa {
 constexpr int kAttnChunk = 1024;
 static int attn_chunk(const Problem& p) { return p.C > 64 ? 1024 : 512; }
 constexpr size_t kLdsPerCu = 160 * 1024;
+// Tiles of this many 16-key blocks or more (the 256-key sibling-pair tiles
+// of 16-bit inputs at C = 128) store their partial rows straight from the
+// accumulators: the LDS the output staging would take is what limited them
+// to five waves per CU; without it eight fit (256K attention 32.2 -> 27.7 ms).
+// Smaller tiles stage through LDS and store whole rows, which measured
+// faster for them (128K: 5.5 vs 7.2 ms with register stores everywhere).
+constexpr int kAttnRegStoreNKB = 16;
 
 // V^T row pad (elements): rows 4 elements apart in bank offset, so the 8-byte
 // reads of 16 consecutive dims (rows) at one key offset fall in distinct
@@ -49,16 +56,17 @@ constexpr int kVtPad = 4;
 template <typename T, int D, int NKB>
 constexpr size_t attn_lds_bytes(int nw) {
   constexpr size_t e = 16 / sizeof(T);
-  return ((size_t)NKB * 16 * (D + e) + (size_t)D * (NKB * 16 + kVtPad) + (size_t)nw * 16 * (D + e)) * sizeof(T) +
-         4 * (size_t)kAttnChunk;
+  const size_t staging = (size_t)(NKB >= kAttnRegStoreNKB ? 1 : nw) * 16 * (D + e);
+  return ((size_t)NKB * 16 * (D + e) + (size_t)D * (NKB * 16 + kVtPad) + staging) * sizeof(T) + 4 * (size_t)kAttnChunk;
 }
 // waves per workgroup: 12 for tiles of 8 key blocks (their K, V^T and the
 // waves' output staging leave room for one workgroup per CU, so it brings
-// the waves), 8 otherwise (two workgroups per CU); fewer where that would
-// not fit the LDS (fp32 rows of d = 128 in 8-block tiles)
+// the waves), 8 for 16-block tiles (no output staging; their registers allow
+// two waves per SIMD) and for smaller tiles (two workgroups per CU); fewer
+// where that would not fit the LDS (fp32 rows of d = 128 in 8-block tiles)
 template <typename T, int D, int NKB>
 constexpr int attn_waves() {
-  int nw = NKB >= 8 ? 12 : 8;
+  int nw = NKB >= 16 ? 8 : (NKB >= 8 ? 12 : 8);
   while (nw > 1 && attn_lds_bytes<T, D, NKB>(nw) > kLdsPerCu) --nw;
   return nw;
 }
@@ -163,7 +171,8 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [CP][KP]
   T* s_vt = s_k + CP * KP;                   // [D][VP]
   // a tile's 16 output columns x D, staged so each lane stores 16-byte pieces
-  __shared__ __align__(16) T s_o[NW][16][D + 16 / sizeof(T)];
+  // (tiles that store from registers keep a one-wave placeholder)
+  __shared__ __align__(16) T s_o[NKB >= kAttnRegStoreNKB ? 1 : NW][16][D + 16 / sizeof(T)];
   __shared__ int32_t s_pr[kAttnChunk];  // the chunk's pair codes
 
   const int64_t chunk = blockIdx.x;
@@ -282,37 +291,70 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
         oacc[db] = mma(fv, fp, oacc[db]);
       }
     }
-    // partial record of (query, slot, head): column col holds rows 4g+i of
-    // each d-block; stage the 16 x D tile in LDS, then store whole rows
-    // (the lane's 4 dims of a d-block are consecutive: one 8- or 16-byte store)
+    if constexpr (NKB >= kAttnRegStoreNKB) {
+      // lane (col, g) holds dims 16 db + 4g + [0, 4) of column col; a row
+      // swap between lane groups g and g ^ 1 (v_permlane16_swap) turns each
+      // pair of d-blocks (2p, 2p + 1) into 8 consecutive dims per lane
+      // (group 0: [32p, +8), 1: [32p + 16, +8), 2: [32p + 8, +8),
+      // 3: [32p + 24, +8)), so a column's four lanes store 64 contiguous
+      // bytes per instruction; fp32 rows already hold 16 contiguous bytes
+      if (live) {
+        const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
+        T* dst = static_cast<T*>(a.po) + rec * D;
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      T* dst = &s_o[w][col][db * 16 + 4 * g];
-      if constexpr (sizeof(T) == 2)
-        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(oacc[db][0], oacc[db][1]), pack_bf16x2(oacc[db][2], oacc[db][3])};
-      else
-        *reinterpret_cast<float4*>(dst) = float4{oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]};
-    }
-    if (live && g == 0) {
-      const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
-      __builtin_nontemporal_store(floatx2_t{m, l}, a.pml + rec);  // one 8-byte store per (query, slot, head)
-    }
-    wave_sync();
-    {
-      constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte piece
-      constexpr int PER_COL = D / CH;
+          for (int pp = 0; pp < D / 32; ++pp) {
+            const uint32_t a0 = pack_bf16x2(oacc[2 * pp][0], oacc[2 * pp][1]);
+            const uint32_t a1 = pack_bf16x2(oacc[2 * pp][2], oacc[2 * pp][3]);
+            const uint32_t b0 = pack_bf16x2(oacc[2 * pp + 1][0], oacc[2 * pp + 1][1]);
+            const uint32_t b1 = pack_bf16x2(oacc[2 * pp + 1][2], oacc[2 * pp + 1][3]);
+            const auto r0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+            const auto r1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+            const uint4 x{r0[0], r1[0], r0[1], r1[1]};
+            store16_nt(dst + 32 * pp + (g & 1) * 16 + (g >> 1) * 8, &x);
+          }
+        } else {
 #pragma unroll
-      for (int it = 0; it < 16 * PER_COL / kWave; ++it) {
-        const int i = it * kWave + lane;
-        const int cc = i / PER_COL, piece = i % PER_COL;
-        const int32_t pc = __shfl(pr, cc);  // pair of column cc (lane cc of group 0)
-        if (pc >= 0) {
-          const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (cc % G);
-          store16_nt(static_cast<T*>(a.po) + rec * D + piece * CH, &s_o[w][cc][piece * CH]);
+          for (int db = 0; db < D / 16; ++db) {
+            const float4 x{oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]};
+            store16_nt(dst + db * 16 + 4 * g, &x);
+          }
+        }
+        if (g == 0) __builtin_nontemporal_store(floatx2_t{m, l}, a.pml + rec);  // one 8-byte store per record
+      }
+    } else {
+      // partial record of (query, slot, head): column col holds rows 4g+i of
+      // each d-block; stage the 16 x D tile in LDS, then store whole rows
+      // (the lane's 4 dims of a d-block are consecutive: one 8- or 16-byte store)
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        T* dst = &s_o[w][col][db * 16 + 4 * g];
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(oacc[db][0], oacc[db][1]), pack_bf16x2(oacc[db][2], oacc[db][3])};
+        else
+          *reinterpret_cast<float4*>(dst) = float4{oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]};
+      }
+      if (live && g == 0) {
+        const int64_t rec = ((hl * a.N + t) * a.K + (pr & 31)) * G + hh;
+        __builtin_nontemporal_store(floatx2_t{m, l}, a.pml + rec);  // one 8-byte store per (query, slot, head)
+      }
+      wave_sync();
+      {
+        constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte piece
+        constexpr int PER_COL = D / CH;
+#pragma unroll
+        for (int it = 0; it < 16 * PER_COL / kWave; ++it) {
+          const int i = it * kWave + lane;
+          const int cc = i / PER_COL, piece = i % PER_COL;
+          const int32_t pc = __shfl(pr, cc);  // pair of column cc (lane cc of group 0)
+          if (pc >= 0) {
+            const int64_t rec = ((hl * a.N + (pc >> 5)) * a.K + (pc & 31)) * G + (cc % G);
+            store16_nt(static_cast<T*>(a.po) + rec * D + piece * CH, &s_o[w][cc][piece * CH]);
+          }
         }
       }
+      wave_sync();
     }
-    wave_sync();
   };
   // tiles w, w + W, ... of the chunk (W = waves), two query-row buffers: the
   // next tile's rows load while the current tile is attended
