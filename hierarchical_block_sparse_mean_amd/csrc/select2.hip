@@ -347,14 +347,16 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void final_topk_kernel(TopkArgs 
   const int64_t wid = wid0 + half;
   const bool live = wid < total;
   const int slot = lane >> 1, l = lane & 1;
-  uint64_t key = 0ull;
+  // the block and its score are loaded together (the score of an empty
+  // slot is read but not used), so the row costs one memory round trip
+  int32_t j2 = -1;
+  float sc = -INFINITY;
   if (live && slot < a.K) {
-    const int32_t j2 = a.blk2[wid * a.K + slot];
-    if (j2 >= 0) {
-      const float sc = a.scores[(wid * a.K + slot) * 2 + l];
-      if (sc != -INFINITY) key = score_key(sc, 2 * j2 + l);
-    }
+    j2 = a.blk2[wid * a.K + slot];
+    sc = a.scores[(wid * a.K + slot) * 2 + l];
   }
+  const uint64_t key0 = (j2 >= 0 && sc != -INFINITY) ? score_key(sc, 2 * j2 + l) : 0ull;
+  uint64_t key = key0;
   if (KP) key = top_half<(KP ? KP : 16)>(key);
   else key = wave_sort_desc(key);
   const bool kept = lane < a.K && key != 0ull;
