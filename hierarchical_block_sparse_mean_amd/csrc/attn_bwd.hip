@@ -73,7 +73,7 @@ static BwdLayout bwd_layout(const Problem& p) {
   L.off_chunks = off;
   off = b256(off + 4 * (size_t)(L.ncl + 1));
   L.off_map = off;
-  off = b256(off + 4 * (size_t)L.max_chunks);
+  off = b256(off + sizeof(ChunkEntry) * (size_t)L.max_chunks);
   L.off_pairs = off;
   off = b256(off + 4 * (size_t)L.slots);
   L.off_dq = off;
@@ -141,7 +141,7 @@ struct BwdArgs {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
-  const int32_t* chunk_map;  // work chunk -> cluster
+  const ChunkEntry* chunk_map;  // work chunk -> (cluster, first pair, pairs)
   const int32_t* pairs;
   void* dq_part;  // [heads][N][K][G][D], input dtype
   float* dk_acc;   // [B][Hkv][N][D]
@@ -187,16 +187,15 @@ __global__ __launch_bounds__((bwd_waves<D, NKB>() * kWave)) PISA_MFMA_REGS void 
   __shared__ int32_t s_pr[NC];
   __shared__ int32_t s_cpr[bwd_chunk_max<NKB>()];  // the chunk's pair codes
 
-  const int64_t chunk = blockIdx.x;
-  if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
-  const int64_t c = a.chunk_map[chunk];
+  const ChunkEntry ce = a.chunk_map[blockIdx.x];
+  if (ce.cluster < 0) return;  // past the last work chunk (uniform over the workgroup)
+  const int64_t c = ce.cluster;
   const int64_t hl = c / a.Mb;
   const int64_t j = c % a.M1;
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
-  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)a.chunk;
-  const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
-  const int64_t p_end = p_begin + a.chunk < p_end_c ? p_begin + a.chunk : p_end_c;
+  const int64_t p_begin = ce.begin;
+  const int64_t p_end = p_begin + ce.count;
 
   const int64_t key0 = j * (int64_t)a.C;
   const int nkeys = (int)((a.N - key0) < a.C ? (a.N - key0) : a.C);
@@ -494,7 +493,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
-  int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
+  ChunkEntry* chunk_map = reinterpret_cast<ChunkEntry*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
   void* dq_part = base + L.off_dq;
   float* rowdot = reinterpret_cast<float*>(base + L.off_rowdot);
@@ -522,12 +521,12 @@ hipError_t launch_attn_bwd(const Problem& p, const void* q, const void* k, const
     const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
     err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.M1, kAttnBins, bwd_chunk(p), cb, stream);
     if (err != hipSuccess) return err;
-    err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
+    const int64_t max_chunks = (entries + bwd_chunk(p) - 1) / bwd_chunk(p) + ncl;
+    err = launch_chunk_map(chunk_off, offsets, counts, ncl, bwd_chunk(p), max_chunks, chunk_map, stream);
     if (err != hipSuccess) return err;
     BwdArgs ba{q, k, v, dout, lse, rowdot, counts, offsets, chunk_off, chunk_map, pairs, dq_part, dk_acc, dv_acc, ncl, L.M1, L.Mb,
                head0, p.N, p.Hq, p.Hkv, p.C, p.K, bwd_chunk(p), p.causal ? 1 : 0, p.cap, p.scale};
     BwdMergeArgs ma{idx, dq_part, dq, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K};
-    const int64_t max_chunks = (entries + bwd_chunk(p) - 1) / bwd_chunk(p) + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value;

@@ -122,7 +122,7 @@ static AttnLayout attn_layout(const Problem& p) {
   L.off_chunks = off;
   off = a256(off + 4 * (size_t)(L.ncl + 1));
   L.off_map = off;
-  off = a256(off + 4 * (size_t)L.max_chunks);
+  off = a256(off + sizeof(ChunkEntry) * (size_t)L.max_chunks);
   L.off_pairs = off;
   off = a256(off + 4 * (size_t)L.slots);
   L.off_ml = off;
@@ -144,7 +144,7 @@ struct AttnLeafArgs {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
-  const int32_t* chunk_map;  // work chunk -> cluster
+  const ChunkEntry* chunk_map;  // work chunk -> (cluster, first pair, pairs)
   const int32_t* pairs;
   floatx2_t* pml;  // (m, l) [heads][N][K][G]
   void* po;    // [heads][N][K][G][D] (input dtype)
@@ -175,17 +175,16 @@ __global__ __launch_bounds__((attn_waves<T, D, NKB>() * kWave)) PISA_MFMA_REGS v
   __shared__ __align__(16) T s_o[NKB >= kAttnRegStoreNKB ? 1 : NW][16][D + 16 / sizeof(T)];
   __shared__ int32_t s_pr[kAttnChunk];  // the chunk's pair codes
 
-  const int64_t chunk = blockIdx.x;
-  if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
-  const int64_t c = a.chunk_map[chunk];
+  const ChunkEntry ce = a.chunk_map[blockIdx.x];
+  if (ce.cluster < 0) return;  // past the last work chunk (uniform over the workgroup)
+  const int64_t c = ce.cluster;
   const int64_t hl = c / a.Mb;  // head within the chunk
   const int64_t jk = c % a.Mk;  // key block: leaf, or M_1 + level-2 block
   if ((jk >= a.M1) != PAIRED) return;  // the other launch's cluster
   const int64_t bh = a.head0 + hl;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
-  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)a.chunk;
-  const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
-  const int64_t p_end = p_begin + a.chunk < p_end_c ? p_begin + a.chunk : p_end_c;
+  const int64_t p_begin = ce.begin;
+  const int64_t p_end = p_begin + ce.count;
 
   const int C = PAIRED ? 2 * a.C : a.C;  // keys of the tile
   const int64_t key0 = (PAIRED ? jk - a.M1 : jk) * (int64_t)C;
@@ -524,7 +523,7 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
-  int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
+  ChunkEntry* chunk_map = reinterpret_cast<ChunkEntry*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
   floatx2_t* pml = reinterpret_cast<floatx2_t*>(base + L.off_ml);
   void* po = base + L.off_o;
@@ -537,12 +536,12 @@ hipError_t launch_attn_leaf(const Problem& p, const void* q, const void* k, cons
     hipError_t err = launch_clusters(idx + head0 * p.N * p.K, heads, (int64_t)p.N * p.K, p.K, L.Mk, kAttnBins,
                                      attn_chunk(p), cb, stream, pairs_on ? L.M1 : 0);
     if (err != hipSuccess) return err;
-    err = launch_chunk_map(chunk_off, ncl, chunk_map, stream);
+    const int64_t max_chunks = (entries + attn_chunk(p) - 1) / attn_chunk(p) + ncl;
+    err = launch_chunk_map(chunk_off, offsets, counts, ncl, attn_chunk(p), max_chunks, chunk_map, stream);
     if (err != hipSuccess) return err;
     AttnLeafArgs aa{q, k, v, counts, offsets, chunk_off, chunk_map, pairs, pml, po, ncl, L.M1, L.Mk, L.Mb, head0,
                     p.N, p.Hq, p.Hkv, p.C, p.K, attn_chunk(p), p.causal ? 1 : 0, p.cap, p.scale};
     MergeArgs ma{idx, pml, po, o, lse, head0, heads, L.M1, p.N, p.Hq, p.Hkv, p.K, pairs_on ? 1 : 0};
-    const int64_t max_chunks = (entries + attn_chunk(p) - 1) / attn_chunk(p) + ncl;
     err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
       using T = std::remove_pointer_t<decltype(tp)>;
       constexpr int D = decltype(dc)::value;

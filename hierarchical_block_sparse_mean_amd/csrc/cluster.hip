@@ -295,17 +295,33 @@ static hipError_t launch_chunk_scan(const ClusterBufs& b, int64_t heads, int64_t
   return hipGetLastError();
 }
 
-// map[ch] = c for every work chunk ch of cluster c
-__global__ void chunk_map_kernel(const int32_t* __restrict__ chunk_off, int64_t ncl, int32_t* __restrict__ map) {
-  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < ncl; c += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t hi = chunk_off[c + 1];
-    for (int32_t ch = chunk_off[c]; ch < hi; ++ch) map[ch] = (int32_t)c;
+// map[ch] = (c, first pair, pairs) for every work chunk ch of cluster c, and
+// cluster -1 for ch from chunk_off[ncl] to max_chunks: the consumers' first
+// and only lookup (they used to read the chunk total, the cluster, and then
+// its offset and count, three dependent loads before any work)
+__global__ void chunk_map_kernel(const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ offsets,
+                                 const int32_t* __restrict__ counts, int64_t ncl, int32_t chunk, int64_t max_chunks,
+                                 ChunkEntry* __restrict__ map) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  for (int64_t c = tid; c < ncl; c += stride) {
+    const int32_t lo = chunk_off[c], hi = chunk_off[c + 1];
+    const int32_t off = offsets[c], cnt = counts[c];
+    for (int32_t ch = lo; ch < hi; ++ch) {
+      const int32_t first = (ch - lo) * chunk;
+      const int32_t rest = cnt - first;
+      map[ch] = ChunkEntry{(int32_t)c, off + first, rest < chunk ? rest : chunk, 0};
+    }
   }
+  for (int64_t ch = chunk_off[ncl] + tid; ch < max_chunks; ch += stride) map[ch] = ChunkEntry{-1, 0, 0, 0};
 }
 
-hipError_t launch_chunk_map(const int32_t* chunk_off, int64_t ncl, int32_t* map, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((ncl + 255) / 256 < 65536 ? (ncl + 255) / 256 : 65536);
-  PISA_LAUNCH("cluster_chunks", stream, chunk_map_kernel, dim3(blocks), dim3(256), 0, chunk_off, ncl, map);
+hipError_t launch_chunk_map(const int32_t* chunk_off, const int32_t* offsets, const int32_t* counts, int64_t ncl,
+                            int32_t chunk, int64_t max_chunks, ChunkEntry* map, hipStream_t stream) {
+  const int64_t work = ncl > max_chunks ? ncl : max_chunks;
+  const unsigned blocks = (unsigned)((work + 255) / 256 < 65536 ? (work + 255) / 256 : 65536);
+  PISA_LAUNCH("cluster_chunks", stream, chunk_map_kernel, dim3(blocks), dim3(256), 0, chunk_off, offsets, counts, ncl,
+              chunk, max_chunks, map);
   return hipGetLastError();
 }
 

@@ -105,8 +105,16 @@ size_t cluster_scratch_bytes(int64_t heads, int64_t NK, int64_t Mb);
 // slot of j, and the entry of j + 1 is dropped.
 hipError_t launch_clusters(const int32_t* keys, int64_t heads, int64_t NK, int32_t K, int64_t M, int64_t max_bins,
                            int32_t chunk, const ClusterBufs& b, hipStream_t stream, int64_t pair_m1 = 0);
-// map[ch] = the cluster of work chunk ch, for ch < chunk_off[ncl]
-hipError_t launch_chunk_map(const int32_t* chunk_off, int64_t ncl, int32_t* map, hipStream_t stream);
+// One entry per work chunk: its cluster, first pair and pair count, so a
+// workgroup finds its work with one load.  Entries past the last chunk
+// (up to max_chunks, the launch grid) hold cluster -1.
+struct ChunkEntry {
+  int32_t cluster, begin, count, pad;
+};
+// map[ch] for ch < max_chunks, from the clusters' chunk_off, offsets, counts
+// and the pairs per work chunk
+hipError_t launch_chunk_map(const int32_t* chunk_off, const int32_t* offsets, const int32_t* counts, int64_t ncl,
+                            int32_t chunk, int64_t max_chunks, ChunkEntry* map, hipStream_t stream);
 
 // Attention clusters (forward and backward): (query block, key block) bins
 // per head (key blocks: the leaves, and in the forward also the level-2

@@ -51,7 +51,7 @@ static S2Layout s2_layout(const Problem& p) {
   s.off_chunks = off;
   off = align256(off + sizeof(int32_t) * (s.ncl + 1));
   s.off_map = off;
-  off = align256(off + sizeof(int32_t) * s.max_chunks);
+  off = align256(off + sizeof(ChunkEntry) * s.max_chunks);
   s.off_pairs = off;
   off = align256(off + sizeof(int32_t) * s.max_pairs);
   s.off_scores = off;
@@ -70,7 +70,7 @@ struct S2Args {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* chunk_off;
-  const int32_t* chunk_map;  // work chunk -> cluster
+  const ChunkEntry* chunk_map;  // work chunk -> (cluster, first pair, pairs)
   const int32_t* pairs;
   float* scores;  // [B][Hkv][N][K][2]
   int64_t ncl, M1, M2, Mb;  // Mb: cluster bins per head
@@ -101,15 +101,14 @@ __global__ __launch_bounds__(kS2Waves* kWave) PISA_MFMA_REGS void leaf_score_ker
   T* s_k = reinterpret_cast<T*>(smem_raw);  // [NCB*16][PITCH]
   __shared__ int32_t s_pr[kS2Chunk];        // the chunk's pair codes
 
-  const int64_t chunk = blockIdx.x;
-  if (chunk >= a.chunk_off[a.ncl]) return;  // uniform over the workgroup
-  const int64_t c = a.chunk_map[chunk];  // chunk_off[c] <= chunk < chunk_off[c + 1]
+  const ChunkEntry ce = a.chunk_map[blockIdx.x];
+  if (ce.cluster < 0) return;  // past the last work chunk (uniform over the workgroup)
+  const int64_t c = ce.cluster;
   const int64_t bh = c / a.Mb;
   const int64_t j2 = c % a.M2;
   const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
-  const int64_t p_begin = a.offsets[c] + (chunk - a.chunk_off[c]) * (int64_t)kS2Chunk;
-  const int64_t p_end_c = (int64_t)a.offsets[c] + a.counts[c];
-  const int64_t p_end = p_begin + kS2Chunk < p_end_c ? p_begin + kS2Chunk : p_end_c;
+  const int64_t p_begin = ce.begin;
+  const int64_t p_end = p_begin + ce.count;
 
   // key tile: leaves 2*j2 and 2*j2+1 are the contiguous keys [key0, key0 + 2C)
   const int C = a.C;
@@ -378,7 +377,7 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.off_cursor);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.off_offsets);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + L.off_chunks);
-  int32_t* chunk_map = reinterpret_cast<int32_t*>(base + L.off_map);
+  ChunkEntry* chunk_map = reinterpret_cast<ChunkEntry*>(base + L.off_map);
   int32_t* pairs = reinterpret_cast<int32_t*>(base + L.off_pairs);
   float* scores = reinterpret_cast<float*>(base + L.off_scores);
   const int64_t M1 = level_rows(p.N, p.C, 1), M2 = level_rows(p.N, p.C, 2);
@@ -386,12 +385,12 @@ hipError_t launch_stage2(const Problem& p, const void* q, const void* k, const i
   const ClusterBufs cb{counts, cursor, offsets, chunk_off, pairs, reinterpret_cast<int32_t*>(base + L.off_hist)};
   hipError_t err = launch_clusters(blk2, (int64_t)p.B * p.Hkv, (int64_t)p.N * p.K, p.K, M2, M2, kS2Chunk, cb, stream);
   if (err != hipSuccess) return err;
-  err = launch_chunk_map(chunk_off, L.ncl, chunk_map, stream);
+  const int64_t max_chunks = (entries + kS2Chunk - 1) / kS2Chunk + L.ncl;
+  err = launch_chunk_map(chunk_off, offsets, counts, L.ncl, kS2Chunk, max_chunks, chunk_map, stream);
   if (err != hipSuccess) return err;
   S2Args a{q, k, counts, offsets, chunk_off, chunk_map, pairs, scores, L.ncl, M1, M2, cluster_bins(p.N, M2, M2), p.B, p.N, p.Hq, p.Hkv,
            p.C, p.K,
            p.causal ? 1 : 0, p.cap, p.scale};
-  const int64_t max_chunks = (entries + kS2Chunk - 1) / kS2Chunk + L.ncl;
   err = dispatch_tdg(p.dtype, p.D, p.G, [&](auto tp, auto dc, auto gc) -> hipError_t {
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr int D = decltype(dc)::value;
