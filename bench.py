@@ -111,10 +111,10 @@ def measured_ceilings() -> dict:
     """Ceilings measured on this GPU, next to the vendor peaks: a 1 GiB
     device-to-device copy by the platform (2 GiB of HBM traffic per copy), the
     library's 16-byte streaming probe reading 2 GiB and copying 1 GiB (best of
-    a few grid sizes), and a
-    bf16 GEMM (8192^3, the platform BLAS), each timed with HIP events.  The
-    HBM ceiling the memory-bound kernels are compared with (`hbm_GBps`) is the
-    best of the three streams: mostly-read kernels exceed a copy's rate."""
+    a few grid sizes), and a bf16 GEMM (8192^3, the platform BLAS), each timed
+    with HIP events.  The HBM ceiling the memory-bound kernels are compared
+    with (`hbm_GBps`) is the best of the three streams: mostly-read kernels
+    exceed a copy's rate."""
     import torch
 
     from hierarchical_block_sparse_mean_amd import pisa
