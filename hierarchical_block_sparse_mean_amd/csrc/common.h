@@ -83,6 +83,25 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
   return uint4{x.x, x.y, x.z, x.w};
 }
 
+// load8 with streaming loads (rows read once)
+template <typename T>
+__device__ __forceinline__ void load8_nt(const T* p, float* out) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 u = load16_nt(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const uint4 a = load16_nt(p), b = load16_nt(p + 4);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(w[i]);
+  }
+}
+
 // 8 consecutive elements of a row, as loaded (16 or 32 bytes), unpacked later
 template <typename T>
 struct Row8 {

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void pyr_leaf_kernel(PyrArgs a) {
 #pragma unroll 4
     for (int64_t r = rsub; r < cnt; r += RPP) {
       float v[8];
-      load8<T>(kh + (lo + r) * D + d0, v);
+      load8_nt<T>(kh + (lo + r) * D + d0, v);  // keys read once here (0.065 -> 0.058 ms at 128K)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
