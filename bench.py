@@ -16,7 +16,9 @@ query positions (with a parity summary of the GPU outputs at those
 positions).  The default 128K run then runs the metric's other sequence
 length, N=262144 (C=128, K=32, shared needle spans), in the same process and
 adds it to the line as "prefill_256k" (step, select and flat-select times,
-its dominant kernel's roofline, a sampled parity summary).
+its dominant kernel's roofline, a sampled parity summary), then the fused
+decode step over 64 sequences of 131072 cached tokens (all 256 of its decode
+steps timed) as "decode_128k".
 """
 from __future__ import annotations
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-256k", action="store_true",
                     help="skip the 256K sub-leg that the default 128K run adds to its JSON line")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the fused decode leg the default 128K run adds to the line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (reference for HBM counter scaling)")
     ap.add_argument("--scaling", action="store_true",
@@ -580,6 +584,16 @@ def main() -> int:
             "stage_ms": {kk: round(vv, 4) for kk, vv in r2["stage_ms"].items()}, "kernels": r2["kernels"],
             "roofline": r2["roofline"], "kernel_rooflines": r2["kernel_rooflines"], "route_work": r2["route_work"],
             "parity": r2["parity"]}
+    dec = None
+    if w.name == "prefill_128k" and not args.no_decode:
+        # the fused decode step on its own workload, in the same process: all
+        # of its decode steps timed (a step is about a tenth of a millisecond),
+        # its oracle parity sample kept small
+        torch.cuda.empty_cache()
+        wd = I.workload("decode_128k")
+        d = decode_leg(wd, wd.steps, 8, cpu_leg=not args.no_cpu_baseline)
+        dec = {kk: d[kk] for kk in ("metric", "config", "steps", "warmup", "value", "unit", "ms_per_step",
+                                     "step_latency_ms", "kernels", "roofline", "cpu_baseline", "parity")}
     line = {
         "metric": METRIC,
         "value": round(r["value"], 1),
@@ -607,6 +621,7 @@ def main() -> int:
         "cpu_baseline": r["cpu_baseline"],
         "parity": r["parity"],
         "prefill_256k": second,
+        "decode_128k": dec,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -953,7 +968,7 @@ def decode_bytes_model(n: int, C: int, K: int, D: int, G: int, esz: int) -> dict
     return b
 
 
-def decode_main(args, w) -> int:
+def decode_leg(w, steps: int, warmup: int, cpu_leg: bool) -> dict:
     """Fused decode: S sequences with an N-token cached prefix; one step
     appends one token per sequence (k, v, leaf mean, ancestor path) and runs
     selection + sparse attention for it in one kernel.  The timed region is
@@ -964,8 +979,8 @@ def decode_main(args, w) -> int:
     from hierarchical_block_sparse_mean_amd import inputs as I
     from hierarchical_block_sparse_mean_amd import pisa
 
-    if args.steps > w.steps or args.warmup > w.steps:
-        raise SystemExit(f"{w.name} has {w.steps} decode steps; asked for --steps {args.steps} --warmup {args.warmup}")
+    if steps > w.steps or warmup > w.steps:
+        raise SystemExit(f"{w.name} has {w.steps} decode steps; asked for --steps {steps} --warmup {warmup}")
     S, cap, G = w.B, w.N + w.steps, w.Hq // w.Hkv
     log(f"workload {w.name}: S={S} sequences x N={w.N} cached tokens (+{w.steps} steps), Hq={w.Hq} Hkv={w.Hkv} "
         f"D={w.D} C={w.C} K={w.K} {w.dtype}")
@@ -1010,12 +1025,12 @@ def decode_main(args, w) -> int:
     torch.cuda.synchronize()
     pyr_ms = e0.elapsed_time(e1)
     log(f"prefix pyramid built in {pyr_ms:.3f} ms")
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     reset()
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done; cache length and pyramid reset to the prefix")
+    log(f"warmup {warmup} steps done; cache length and pyramid reset to the prefix")
 
     # timed region: the K steps alone.  At this step length, HIP events around
     # every launch and step would cost about a sixth of the step, so the
@@ -1024,19 +1039,19 @@ def decode_main(args, w) -> int:
     # events on the launch stream.
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     if int(err.item()) != 0:
         raise SystemExit("decode reported a full cache")
-    ms_per_step = wall * 1000.0 / args.steps
-    value = S * args.steps / wall
+    ms_per_step = wall * 1000.0 / steps
+    value = S * steps / wall
     reset()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     pisa.timer_enable(True)
-    for i in range(args.steps):
+    for i in range(steps):
         evs[i][0].record()
         step(i)
         evs[i][1].record()
@@ -1046,16 +1061,16 @@ def decode_main(args, w) -> int:
     if int(err.item()) != 0:
         raise SystemExit("decode reported a full cache")
     lat = np.array([a.elapsed_time(b) for a, b in evs])
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; instrumented pass: median step {np.median(lat):.4f} ms, "
+    log(f"timed {steps} steps: {ms_per_step:.4f} ms/step; instrumented pass: median step {np.median(lat):.4f} ms, "
         f"p99 {np.percentile(lat, 99):.4f} ms")
     per_kernel = {kk: {"launches": vv[0], "avg_ms": vv[1] / max(1, vv[0])} for kk, vv in kernels.items()}
 
     # roofline of the fused decode kernel, on the modelled bytes of each step
     esz = 2 if w.dtype == "bf16" else 4
     per_launch = 0
-    for i in range(args.steps):
+    for i in range(steps):
         per_launch += decode_bytes_model(w.N + i + 1, w.C, w.K, w.D, G, esz)["total"] * S * w.Hkv
-    per_launch /= args.steps
+    per_launch /= steps
     mid = decode_bytes_model(w.N + 1, w.C, w.K, w.D, G, esz)
     dk = per_kernel.get("decode")
     roofline = None
@@ -1070,11 +1085,11 @@ def decode_main(args, w) -> int:
 
     # CPU oracle on a few sequences at the first and last timed step, with parity
     cpu = parity = None
-    if not args.no_cpu_baseline:
+    if cpu_leg:
         import oracle
 
         seqs = [0, S // 3, (2 * S) // 3, S - 1][: max(1, min(4, S))]
-        checks = sorted({0, args.steps - 1})
+        checks = sorted({0, steps - 1})
         g_idx = idx_all.cpu().numpy()
         g_score = score_all.cpu().numpy().astype(np.float64)
         g_o = o_all.float().cpu().numpy().astype(np.float64)
@@ -1122,8 +1137,8 @@ def decode_main(args, w) -> int:
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -1137,13 +1152,17 @@ def decode_main(args, w) -> int:
         "prefix_pyramid_ms": round(pyr_ms, 4),
         "timing_note": "value and ms_per_step: the K steps with nothing else on the stream; kernels, roofline and "
                        "step_latency_ms: the same K steps re-run from the prefix with HIP events per launch and step",
-        "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 5), "launches_per_step": vv["launches"] / args.steps}
+        "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 5), "launches_per_step": vv["launches"] / steps}
                     for kk, vv in per_kernel.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
     }
-    print(json.dumps(line), flush=True)
+    return line
+
+
+def decode_main(args, w) -> int:
+    print(json.dumps(decode_leg(w, args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
     return 0
 
 
